@@ -1,0 +1,196 @@
+"""Gated delta-rule (Kimi Delta Attention) forward pass on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libkda.so`` (C ABI in ``include/kda.h``).  Every
+step of the computation runs in the library's HIP kernels; this module only
+checks tensor properties, allocates outputs with torch and passes raw device
+pointers plus torch's current HIP stream.  There is no fallback: if the library
+is missing or the tensors are not on a GPU, the call raises.
+
+Recurrence per head (worldcybernews page "Kimi K3 Open Model Surpasses Closed
+GPT and Anthropic Systems on Independent Benchmarks", second paragraph, read as
+the gated delta rule):  S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+o_t = S_t^T q_t, a_t = exp(clamp(g_t, -5, 0)).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
+           "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "DTYPE"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+DTYPE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+STATUS = {0: "OK", 1: "NULL_ARG", 2: "BAD_SHAPE", 3: "BAD_DTYPE", 4: "MISALIGNED", 5: "HIP_ERROR"}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kda status {status} ({STATUS.get(status, '?')}): {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def load_library():
+    """Open libkda.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                          f"g.build()'` or `python gated_delta_rule_65_amd/_build.py`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, vp]
+    L.kda_chunk_fwd.restype = ci
+    L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    L.kda_varlen_fwd.restype = ci
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, vp]
+    L.kda_decode_step.restype = ci
+    L.kda_last_error.restype = ctypes.c_char_p
+    L.kda_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise KDAError(status, load_library().kda_last_error().decode())
+
+
+# ----------------------------------------------------------------- raw calls (ints in, status out)
+
+def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, stream) -> int:
+    return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, stream)
+
+
+def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, stream) -> int:
+    return load_library().kda_varlen_fwd(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype,
+                                         stream)
+
+
+def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream) -> int:
+    return load_library().kda_decode_step(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream)
+
+
+# ----------------------------------------------------------------- torch front end
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              s0: Optional[torch.Tensor] = None, chunk: int = 64, output_final_state: bool = True
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill over equal-length sequences.
+
+    q, k: [B, T, H, Dk]; v: [B, T, H, Dv] (bf16 or fp32, all the same);
+    g (log forget gate, fp32): [B, T, H, Dk]; beta (fp32): [B, T, H]; s0 (fp32): [B, H, Dk, Dv] or None.
+    Returns o (fp32) [B, T, H, Dv] and the final state [B, H, Dk, Dv] (or None).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(g, "g", torch.float32, (B, T, H, Dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
+    o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    sf = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    with torch.cuda.device(q.device):
+        _check(chunk_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
+                             B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], _stream(q.device)))
+    return o, sf
+
+
+def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+               cu_seqlens: torch.Tensor, s0: Optional[torch.Tensor] = None, chunk: int = 64,
+               output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed variable-length prefill.
+
+    q, k, g: [total, H, Dk]; v: [total, H, Dv]; beta: [total, H]; cu_seqlens: int32 [N+1] on the GPU;
+    s0: [N, H, Dk, Dv] or None.  Returns o [total, H, Dv] (fp32) and the final states [N, H, Dk, Dv].
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, Dk]")
+    total, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (total, H, Dk))
+    _need(v, "v", q.dtype, (total, H, Dv))
+    _need(g, "g", torch.float32, (total, H, Dk))
+    _need(beta, "beta", torch.float32, (total, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (N, H, Dk, Dv))
+    o = torch.empty((total, H, Dv), dtype=torch.float32, device=q.device)
+    sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    with torch.cuda.device(q.device):
+        _check(varlen_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
+                              _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], _stream(q.device)))
+    return o, sf
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                state: torch.Tensor, inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One token per sequence.  q, k, g: [B, H, Dk]; v: [B, H, Dv]; beta: [B, H];
+    state (fp32): [B, H, Dk, Dv].  Returns o [B, H, Dv] (fp32) and the new state
+    (``state`` itself when ``inplace``)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, Dk]")
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, H, Dk))
+    _need(v, "v", q.dtype, (B, H, Dv))
+    _need(g, "g", torch.float32, (B, H, Dk))
+    _need(beta, "beta", torch.float32, (B, H))
+    _need(state, "state", torch.float32, (B, H, Dk, Dv))
+    o = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    out_state = state if inplace else torch.empty_like(state)
+    with torch.cuda.device(q.device):
+        _check(decode_step_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out_state),
+                               _ptr(o), B, H, Dk, Dv, DTYPE[q.dtype], _stream(q.device)))
+    return o, out_state

@@ -1,0 +1,143 @@
+// C ABI of the library (declared in include/kda.h): host-side validation,
+// error reporting and dispatch to the gfx950 kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kda_status ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_head_dims(int H, int Dk, int Dv) {
+    if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
+    if (Dk != 64 && Dk != 128) return fail(KDA_ERR_BAD_SHAPE, "Dk must be 64 or 128 (got %d)", Dk);
+    if (Dv != 64 && Dv != 128) return fail(KDA_ERR_BAD_SHAPE, "Dv must be 64 or 128 (got %d)", Dv);
+    return KDA_OK;
+}
+
+kda_status check_dtype(kda_dtype dt) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_BAD_DTYPE, "dtype must be KDA_F32 or KDA_BF16");
+    return KDA_OK;
+}
+
+struct Ptr {
+    const void* p;
+    const char* name;
+    bool required;
+};
+
+kda_status check_ptrs(std::initializer_list<Ptr> ptrs) {
+    for (const Ptr& x : ptrs) {
+        if (x.required && !x.p) return fail(KDA_ERR_NULL_ARG, "%s is NULL", x.name);
+        if (x.p && !aligned16(x.p)) return fail(KDA_ERR_MISALIGNED, "%s is not 16-byte aligned", x.name);
+    }
+    return KDA_OK;
+}
+
+kda_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+kda_status run_chunked(const kda::ChunkArgs& a, hipStream_t st, const char* what) {
+    const int64_t grid = kda::chunk_grid_size(a.N, a.H, a.Dv);
+    if (grid > 0x7fffffff) return fail(KDA_ERR_BAD_SHAPE, "%s: %lld sequence-heads exceed the grid limit", what,
+                                       (long long)(a.N * a.H));
+    if (grid == 0) return ok();
+    return launched(kda::launch_chunk_fwd(a, st), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk, int Dv,
+                         int chunk, kda_dtype dtype, void* stream) {
+    kda_status st;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
+    if (B < 0 || T < 0) return fail(KDA_ERR_BAD_SHAPE, "B and T must be >= 0");
+    if (T > 0 && B > INT64_MAX / T) return fail(KDA_ERR_BAD_SHAPE, "B*T overflows");
+    const bool tokens = B > 0 && T > 0;
+    if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
+                          {beta, "beta", tokens}, {o, "o", tokens}, {s0, "s0", false},
+                          {s_final, "s_final", false}})) != KDA_OK)
+        return st;
+    if (B == 0 || (!tokens && !s_final)) return ok();
+    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, nullptr, T, B * T, B, H, Dk, Dv, dtype == KDA_F32};
+    return run_chunked(a, static_cast<hipStream_t>(stream), "kda_chunk_fwd");
+}
+
+kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* stream) {
+    kda_status st;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
+    if (N < 0 || total < 0) return fail(KDA_ERR_BAD_SHAPE, "N and total must be >= 0");
+    if (total > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "total exceeds the int32 range of cu_seqlens");
+    const bool tokens = total > 0;
+    if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_ARG, "cu_seqlens is NULL");
+    if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
+                          {beta, "beta", tokens}, {o, "o", tokens}, {s0, "s0", false},
+                          {s_final, "s_final", false}})) != KDA_OK)
+        return st;
+    if (N == 0 || (!tokens && !s_final)) return ok();
+    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, cu_seqlens, 0, total, N, H, Dk, Dv, dtype == KDA_F32};
+    return run_chunked(a, static_cast<hipStream_t>(stream), "kda_varlen_fwd");
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const float* s_in, float* s_out, float* o, int64_t B, int H, int Dk, int Dv,
+                           kda_dtype dtype, void* stream) {
+    kda_status st;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (B < 0) return fail(KDA_ERR_BAD_SHAPE, "B must be >= 0");
+    if (B * H > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "B*H exceeds the grid limit");
+    const bool any = B > 0;
+    if ((st = check_ptrs({{q, "q", any}, {k, "k", any}, {v, "v", any}, {g, "g", any}, {beta, "beta", any},
+                          {s_in, "s_in", any}, {s_out, "s_out", any}, {o, "o", any}})) != KDA_OK)
+        return st;
+    if (s_in != s_out && s_in && s_out) {
+        const char* a0 = reinterpret_cast<const char*>(s_in);
+        const char* b0 = reinterpret_cast<const char*>(s_out);
+        const int64_t bytes = B * H * (int64_t)Dk * Dv * 4;
+        if (a0 < b0 + bytes && b0 < a0 + bytes)
+            return fail(KDA_ERR_BAD_SHAPE, "s_in and s_out overlap without being the same buffer");
+    }
+    if (!any) return ok();
+    kda::DecodeArgs a{q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype == KDA_F32};
+    return launched(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda_decode_step");
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_version(void) { return "kda-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// One decoding step of the gated delta rule for gfx950: a single token per
+// (sequence, head) against a state S that lives in HBM.
+//
+// Per head ("Kimi K3 Open Model Surpasses Closed GPT and Anthropic Systems on
+// Independent Benchmarks", worldcybernews, second paragraph: the state replaces
+// the key/value cache and is updated with the delta rule; read as
+// S' = (I - b k k^T) Diag(a) S + b k v^T, o = S'^T q with a = exp(clamp(g,-5,0))):
+//     w_j  = sum_i a_i k_i S_ij          (prediction of v from the decayed state)
+//     u_j  = b (v_j - w_j)
+//     S'_ij = a_i S_ij + k_i u_j
+//     o_j  = sum_i q_i S'_ij
+// The step is a single streaming pass over S: each element is read once and
+// written once with 128-bit accesses, and both column reductions over i stay on
+// chip.  A workgroup of 256 threads owns one (sequence, head): thread t covers
+// four adjacent columns (one float4) of every (256/(Dv/4))-th row.
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <int DK, int DV, bool F32>
+__global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
+                                                     const void* __restrict__ vv, const float* __restrict__ g,
+                                                     const float* __restrict__ beta, const float* s_in,
+                                                     float* s_out, float* __restrict__ o) {
+    using In = typename std::conditional<F32, float, uint16_t>::type;
+    constexpr int C4 = DV / 4;     // threads across the columns
+    constexpr int RG = 256 / C4;   // row groups
+    constexpr int RPT = DK / RG;   // rows per thread
+    static_assert(RPT * RG == DK, "row split");
+
+    __shared__ float sk[DK], sa[DK], sq[DK], su[DV];
+    __shared__ float4 sred[RG][C4];
+
+    const In* __restrict__ q = static_cast<const In*>(qv);
+    const In* __restrict__ k = static_cast<const In*>(kv);
+    const In* __restrict__ v = static_cast<const In*>(vv);
+    const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4;
+    const int64_t bh = blockIdx.x;
+
+    auto ld = [](const In* p, int64_t i) -> float {
+        if constexpr (F32) return p[i];
+        else return bf16_bits_to_float(p[i]);
+    };
+    if (tid < DK) {
+        sk[tid] = ld(k, bh * DK + tid);
+        sq[tid] = ld(q, bh * DK + tid);
+        sa[tid] = __expf(fminf(fmaxf(g[bh * DK + tid], -5.f), 0.f));
+    }
+    __syncthreads();
+
+    const f32x4_t* S = reinterpret_cast<const f32x4_t*>(s_in + bh * (int64_t)DK * DV);
+    f32x4_t* So = reinterpret_cast<f32x4_t*>(s_out + bh * (int64_t)DK * DV);
+    f32x4_t st[RPT];
+    float4 wp = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int mm = 0; mm < RPT; ++mm) st[mm] = __builtin_nontemporal_load(&S[(rg + RG * mm) * C4 + c4]);
+#pragma unroll
+    for (int mm = 0; mm < RPT; ++mm) {
+        const int i = rg + RG * mm;
+        const float ak = sa[i] * sk[i];
+        wp.x = fmaf(ak, st[mm][0], wp.x);
+        wp.y = fmaf(ak, st[mm][1], wp.y);
+        wp.z = fmaf(ak, st[mm][2], wp.z);
+        wp.w = fmaf(ak, st[mm][3], wp.w);
+    }
+    sred[rg][c4] = wp;
+    __syncthreads();
+    if (tid < C4) {
+        float4 acc = sred[0][tid];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            const float4 x = sred[r][tid];
+            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+        }
+        const float b = beta[bh];
+        const int64_t vb = bh * DV + 4 * tid;
+        su[4 * tid + 0] = b * (ld(v, vb + 0) - acc.x);
+        su[4 * tid + 1] = b * (ld(v, vb + 1) - acc.y);
+        su[4 * tid + 2] = b * (ld(v, vb + 2) - acc.z);
+        su[4 * tid + 3] = b * (ld(v, vb + 3) - acc.w);
+    }
+    __syncthreads();
+    const float4 u = make_float4(su[4 * c4], su[4 * c4 + 1], su[4 * c4 + 2], su[4 * c4 + 3]);
+    float4 op = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int mm = 0; mm < RPT; ++mm) {
+        const int i = rg + RG * mm;
+        const float a = sa[i], kk = sk[i], qq = sq[i];
+        f32x4_t x;
+        x[0] = fmaf(a, st[mm][0], kk * u.x);
+        x[1] = fmaf(a, st[mm][1], kk * u.y);
+        x[2] = fmaf(a, st[mm][2], kk * u.z);
+        x[3] = fmaf(a, st[mm][3], kk * u.w);
+        __builtin_nontemporal_store(x, &So[i * C4 + c4]);
+        op.x = fmaf(qq, x[0], op.x);
+        op.y = fmaf(qq, x[1], op.y);
+        op.z = fmaf(qq, x[2], op.z);
+        op.w = fmaf(qq, x[3], op.w);
+    }
+    sred[rg][c4] = op;
+    __syncthreads();
+    if (tid < C4) {
+        float4 acc = sred[0][tid];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            const float4 x = sred[r][tid];
+            acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+        }
+        reinterpret_cast<float4*>(o + bh * DV)[tid] = acc;
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_dv(const DecodeArgs& a, hipStream_t st) {
+    const dim3 grid((unsigned)(a.B * a.H));
+    if (a.f32)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta, a.s_in,
+                           a.s_out, a.o);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.s_in, a.s_out, a.o);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+    if (a.Dk == 128) return a.Dv == 128 ? launch_dv<128, 128>(a, st) : launch_dv<128, 64>(a, st);
+    return a.Dv == 128 ? launch_dv<64, 128>(a, st) : launch_dv<64, 64>(a, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,116 @@
+// Device-side helpers for the gfx950 kernels: bf16 conversion, MFMA operand
+// fragments with a split-bf16 or fp32 precision policy, and a 16-lane DPP scan.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Eight consecutive input elements (bf16 or fp32) as floats; p must be 16-byte aligned.
+__device__ __forceinline__ void load8_as_float(const uint16_t* p, float x[8]) {
+    uint4 w = *reinterpret_cast<const uint4*>(p);
+    uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(u[i] << 16);
+        x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8_as_float(const float* p, float x[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand fragments.  For v_mfma_f32_16x16x32_bf16 a lane holds eight
+// consecutive reduction-index values of one row (A) or one column (B):
+// lane l -> row/column l%16, reduction indices 8*(l/16) .. 8*(l/16)+7 of the
+// 32-wide step; the 16x16 result gives lane l column l%16, rows 4*(l/16)..+3.
+//
+// Precision policies:
+//   SPLIT (bf16 inputs): each operand is x = hi + lo with hi = bf16(x) and
+//     lo = bf16(x - hi); a 3-pass product hi*hi + hi*lo + lo*hi keeps about
+//     16 significant bits, a 1-pass product uses hi*hi only.
+//   F32 (fp32 inputs): products go through v_mfma_f32_16x16x4_f32; MFMA number
+//     j consumes value j of every lane, so the same eight-values-per-lane
+//     fragment covers the 32-wide step in 8 instructions.
+// ---------------------------------------------------------------------------
+template <bool F32>
+struct Frag;
+
+template <>
+struct Frag<false> {
+    bf16x8_t hi, lo;
+    __device__ __forceinline__ void set(const float x[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __bf16 h = (__bf16)x[j];
+            hi[j] = h;
+            lo[j] = (__bf16)(x[j] - (float)h);
+        }
+    }
+    __device__ __forceinline__ void set_hi_only(const float x[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hi[j] = (__bf16)x[j];
+    }
+};
+
+template <>
+struct Frag<true> {
+    float v[8];
+    __device__ __forceinline__ void set(const float x[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = x[j];
+    }
+    __device__ __forceinline__ void set_hi_only(const float x[8]) { set(x); }
+};
+
+// acc += A * B with the full precision of the policy.
+__device__ __forceinline__ f32x4_t mma_full(f32x4_t acc, const Frag<false>& a, const Frag<false>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4_t mma_full(f32x4_t acc, const Frag<true>& a, const Frag<true>& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+    return acc;
+}
+// acc += A * B with one bf16 pass (SPLIT) or full fp32 (F32).
+__device__ __forceinline__ f32x4_t mma_fast(f32x4_t acc, const Frag<false>& a, const Frag<false>& b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma_fast(f32x4_t acc, const Frag<true>& a, const Frag<true>& b) {
+    return mma_full(acc, a, b);
+}
+
+// Eight consecutive floats from LDS (16-byte aligned).
+__device__ __forceinline__ void lds_read8(const float* p, float x[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15),
+// Hillis-Steele with row_shr 1, 2, 4, 8; lanes shifted in from outside the row
+// contribute 0.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_inclusive_scan(float x) {
+    x += dpp_row_shr<1>(x);
+    x += dpp_row_shr<2>(x);
+    x += dpp_row_shr<4>(x);
+    x += dpp_row_shr<8>(x);
+    return x;
+}

@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI (kda_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *s0;
+    float *o, *s_final;
+    const int32_t* cu_seqlens;  // device offsets, or nullptr for equal-length sequences
+    int64_t T_fixed;            // tokens per sequence when cu_seqlens == nullptr
+    int64_t total;              // tokens in all sequences
+    int64_t N;                  // sequences
+    int H, Dk, Dv;
+    bool f32;                   // q/k/v are float32 (else bf16)
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *s_in;
+    float *s_out, *o;
+    int64_t B;
+    int H, Dk, Dv;
+    bool f32;
+};
+
+int64_t chunk_grid_size(int64_t N, int H, int Dv);
+hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,113 @@
+/*
+ * kda.h — C ABI of the gated delta-rule (Kimi Delta Attention) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Kimi K3 Open Model Surpasses Closed GPT and Anthropic
+ * Systems on Independent Benchmarks", worldcybernews, second paragraph): each
+ * head keeps a fixed-size state matrix S (Dk x Dv) in place of a key/value
+ * cache; every token updates it with the delta rule, beta being the write
+ * strength and alpha the forget gate, and alpha is kept inside [e^-5, 1].
+ * Read here as, per token t and head h,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,      alpha_t = exp(clamp(g_t, -5, 0))  (per key channel)
+ *
+ * The third paragraph of the same page describes a kernel that processes the
+ * tokens of each chunk in parallel while the state is carried sequentially from
+ * chunk to chunk; kda_chunk_fwd and kda_varlen_fwd compute the recurrence that
+ * way, 64 tokens at a time, and their results do not depend on the chunk size
+ * beyond rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
+ *    layouts given below, 16-byte aligned.  The caller owns every buffer; the
+ *    library allocates nothing and keeps no pointer after a call returns.
+ *  - q, k, v use `dtype` (KDA_BF16 or KDA_F32).  g (log alpha, clamped to
+ *    [-5, 0] by the library), beta, the states and the output o are float32.
+ *    o is float32 for both input types: rounding it to bf16 would by itself
+ *    cost up to about 3% of the output RMS on realistic gate statistics.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous and stream-ordered; nothing here synchronises the device.
+ *  - Arguments are validated on the host before any launch.  A non-zero
+ *    status means nothing was launched, except KDA_ERR_HIP, which reports a
+ *    launch failure.  kda_last_error() returns a message for the last failing
+ *    call on the calling thread.  No call aborts or throws.
+ *  - Supported head sizes: Dk, Dv in {64, 128}.  chunk must be 64.
+ *  - Calls are reentrant; concurrent calls on different streams must not
+ *    write the same buffers.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,  /* unsupported or inconsistent size */
+    KDA_ERR_BAD_DTYPE = 3,  /* dtype not KDA_F32 / KDA_BF16 */
+    KDA_ERR_MISALIGNED = 4, /* a pointer is not 16-byte aligned */
+    KDA_ERR_HIP = 5         /* the HIP runtime reported an error at launch */
+} kda_status;
+
+/*
+ * Chunked prefill over B sequences of equal length T.
+ *   q, k : [B, T, H, Dk]  dtype          v : [B, T, H, Dv]  dtype
+ *   g    : [B, T, H, Dk]  float32 (log alpha; clamped to [-5, 0] inside)
+ *   beta : [B, T, H]      float32 (used as given, not clamped)
+ *   s0   : [B, H, Dk, Dv] float32 initial state, or NULL for zeros
+ *   o    : [B, T, H, Dv]  float32 output (written)
+ *   s_final : [B, H, Dk, Dv] float32 final state (written), or NULL
+ * T = 0 is allowed: o is untouched and s_final receives s0 (or zeros).
+ * s_final may alias s0 (each state is read before it is written).
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
+                         int Dv, int chunk, kda_dtype dtype, void* stream);
+
+/*
+ * Packed variable-length prefill: N independent sequences stored back to back.
+ *   q, k, g : [total, H, Dk]; v, o : [total, H, Dv]; beta : [total, H]
+ *   cu_seqlens : DEVICE int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
+ *                cu_seqlens[N] = total; sequence n is tokens
+ *                cu_seqlens[n] .. cu_seqlens[n+1]-1 and starts its own chunks.
+ *   s0, s_final : [N, H, Dk, Dv] float32, each may be NULL (zeros / not written).
+ * The offsets are read on the device (no host synchronisation); offsets that
+ * break the stated invariants give unspecified results for the affected
+ * sequences but never access memory outside [0, total) tokens.
+ */
+kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* stream);
+
+/*
+ * One decoding step (one new token per sequence) on B sequences.
+ *   q, k : [B, H, Dk] dtype;  v : [B, H, Dv] dtype
+ *   g    : [B, H, Dk] float32 (log alpha);  beta : [B, H] float32
+ *   s_in : [B, H, Dk, Dv] float32 state before the token
+ *   s_out: [B, H, Dk, Dv] float32 state after the token; s_out == s_in is
+ *          allowed (in-place update); partial overlap is not.
+ *   o    : [B, H, Dv] float32 output of the token
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const float* s_in, float* s_out, float* o, int64_t B, int H, int Dk, int Dv,
+                           kda_dtype dtype, void* stream);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

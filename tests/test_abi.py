@@ -1,0 +1,125 @@
+"""The C ABI: symbols, host-side validation (no GPU needed: every case below is
+rejected before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_65_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+FAKE = 1 << 20  # 16-byte aligned stand-in address; never dereferenced because validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_last_error", "kda_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kda.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version():
+    assert kda.load_library().kda_version().decode().startswith("kda-gfx950")
+
+
+def last_error():
+    return kda.load_library().kda_last_error().decode()
+
+
+def chunk(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, s_final=None, B=1, T=64, H=1, Dk=128,
+             Dv=128, chunk=64, dtype=1, stream=None)
+    a.update(kw)
+    return kda.chunk_fwd_raw(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Dk=96), 2, "Dk"), (dict(Dv=32), 2, "Dv"), (dict(H=0), 2, "H"), (dict(chunk=32), 2, "chunk"),
+    (dict(T=-1), 2, "T"), (dict(B=-2), 2, "B"), (dict(dtype=7), 3, "dtype"),
+    (dict(q=None), 1, "q"), (dict(k=None), 1, "k"), (dict(v=None), 1, "v"), (dict(g=None), 1, "g"),
+    (dict(beta=None), 1, "beta"), (dict(o=None), 1, "o"),
+    (dict(q=FAKE + 2), 4, "q"), (dict(v=FAKE + 8), 4, "v"), (dict(s0=FAKE + 4), 4, "s0"),
+    (dict(s_final=FAKE + 12), 4, "s_final"),
+])
+def test_chunk_validation(kw, status, msg):
+    assert chunk(**kw) == status
+    assert msg in last_error()
+
+
+def test_chunk_nothing_to_do_returns_ok():
+    # no tokens and no final state requested: nothing is launched
+    assert chunk(q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
+    assert chunk(B=0) == 0
+    assert last_error() == ""
+
+
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, N=2, total=100, s0=None, o=FAKE, s_final=None, H=2,
+             Dk=128, Dv=128, chunk=64, dtype=1, stream=None)
+    a.update(kw)
+    return kda.varlen_fwd_raw(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(cu=None), 1, "cu_seqlens"), (dict(N=-1), 2, "N"), (dict(total=-5), 2, "total"),
+    (dict(total=1 << 31), 2, "int32"), (dict(Dk=48), 2, "Dk"), (dict(chunk=128), 2, "chunk"),
+    (dict(o=FAKE + 4), 4, "o"), (dict(dtype=-1), 3, "dtype"), (dict(g=None), 1, "g"),
+])
+def test_varlen_validation(kw, status, msg):
+    assert varlen(**kw) == status
+    assert msg in last_error()
+
+
+def test_varlen_nothing_to_do():
+    assert varlen(N=0, cu=None) == 0
+
+
+def decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s_in=FAKE, s_out=FAKE, o=FAKE, B=4, H=2, Dk=128, Dv=128,
+             dtype=1, stream=None)
+    a.update(kw)
+    return kda.decode_step_raw(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(s_in=None), 1, "s_in"), (dict(o=None), 1, "o"), (dict(Dv=100), 2, "Dv"), (dict(B=-1), 2, "B"),
+    (dict(s_out=FAKE + 64), 2, "overlap"), (dict(k=FAKE + 2), 4, "k"), (dict(dtype=5), 3, "dtype"),
+])
+def test_decode_validation(kw, status, msg):
+    assert decode(**kw) == status
+    assert msg in last_error()
+
+
+def test_decode_empty_batch_ok():
+    assert decode(B=0, q=None, k=None, v=None, g=None, beta=None, s_in=None, s_out=None, o=None) == 0
+
+
+def test_torch_front_end_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.chunk_fwd(q, q, q, q.float(), torch.zeros(1, 64, 1))
+
+
+def test_error_is_thread_local():
+    import threading
+    assert chunk(Dk=96) == 2
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(last_error()))
+    t.start()
+    t.join()
+    assert seen == [""] and "Dk" in last_error()

@@ -1,0 +1,77 @@
+"""GPU parity of the single-token decode step against the fp64 oracle (one-token sequences)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_65_amd as kda
+import kda_inputs
+import oracle
+from tests.gpu_util import TOL, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp, inplace=False):
+    sp = inp.spec
+    B, H = sp.n_seq, sp.H
+    q = to_dev(inp.q, (B, H, sp.Dk))
+    k = to_dev(inp.k, (B, H, sp.Dk))
+    v = to_dev(inp.v, (B, H, sp.Dv))
+    g = to_dev(inp.g, (B, H, sp.Dk))
+    beta = to_dev(inp.beta, (B, H))
+    st = to_dev(inp.s0)
+    o, s1 = kda.decode_step(q, k, v, g, beta, st, inplace=inplace)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), s1.cpu().numpy(), st
+
+
+def test_workload_decode_b256_h32_d128_bf16():
+    inp = kda_inputs.generate(kda_inputs.workload("decode_b256_h32_d128_bf16"))
+    o, s, _ = run_decode(inp)
+    o_ref, s_ref = oracle.forward_inputs(inp)
+    eo, es = rel_err(o, o_ref.reshape(o.shape)), rel_err(s, s_ref)
+    print(f"decode o err {eo:.3e} S err {es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_shapes(Dk, Dv, dtype):
+    spec = kda_inputs.Spec([1] * 5, 3, Dk, Dv, dtype, "softplus_bounds", 0.1, s0_std=0.3, seed=31)
+    inp = kda_inputs.generate(spec)
+    o, s, _ = run_decode(inp)
+    o_ref, s_ref = oracle.forward_inputs(inp)
+    assert rel_err(o, o_ref.reshape(o.shape)) <= TOL[dtype] and rel_err(s, s_ref) <= TOL[dtype]
+
+
+def test_decode_inplace():
+    spec = kda_inputs.Spec([1] * 7, 4, 128, 128, "bf16", "softplus", s0_std=0.02, seed=32)
+    inp = kda_inputs.generate(spec)
+    o1, s1, _ = run_decode(inp, inplace=False)
+    o2, s2, st = run_decode(inp, inplace=True)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    assert np.array_equal(st.cpu().numpy(), s2)
+
+
+def test_decode_steps_equal_chunked_prefill():
+    """T successive decode steps reproduce the chunked forward pass over the same T tokens."""
+    T, B, H, D = 70, 2, 2, 128
+    spec = kda_inputs.Spec([T] * B, H, D, D, "bf16", "softplus_bounds", 0.05, s0_std=0.02, seed=33)
+    inp = kda_inputs.generate(spec)
+    q = to_dev(inp.q, (B, T, H, D))
+    k = to_dev(inp.k, (B, T, H, D))
+    v = to_dev(inp.v, (B, T, H, D))
+    g = to_dev(inp.g, (B, T, H, D))
+    beta = to_dev(inp.beta, (B, T, H))
+    s0 = to_dev(inp.s0)
+    o_c, s_c = kda.chunk_fwd(q, k, v, g, beta, s0)
+    st = s0.clone()
+    outs = []
+    for t in range(T):
+        o_t, st = kda.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                  g[:, t].contiguous(), beta[:, t].contiguous(), st)
+        outs.append(o_t)
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, 1)
+    assert rel_err(o_d.cpu().numpy(), o_c.double().cpu().numpy()) < 5e-3
+    assert rel_err(st.cpu().numpy(), s_c.double().cpu().numpy()) < 5e-3
