@@ -1,0 +1,206 @@
+"""Throughput benchmark of the gated delta-rule (KDA) forward pass on one MI355X.
+
+Timed step: one kda_chunk_fwd call over the chunked-prefill batch B=4, H=16,
+T=8192, d_k=d_v=128 (bf16 q/k/v, fp32 gates, fp32 state and output), inputs
+resident in HBM.  value = B*T tokens per step / seconds per step.
+
+Also reported on the same JSON line:
+  roofline      chunk kernel against HBM bandwidth (algorithmic bytes / kernel time)
+  mfma          the same kernel's algorithmic FLOPs against the dense bf16 MFMA peak
+  decode        single-token decode step, B=256, H=32, d=128: GB/s against HBM peak
+  varlen        packed varlen prefill, 32 sequences, H=16, d=128: tokens/s
+  cpu_baseline  the fp64 CPU oracle on the same chunked batch (rank 0 only)
+  parity        max|err|/RMS of the timed output against that oracle run
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def chunk_alg_bytes(n_head_tokens, n_heads, Dk, Dv, in_bytes, with_s0):
+    # q, k, v in the input type; g fp32 (Dk); beta fp32; o fp32 (Dv); final state fp32 (+ initial state if given)
+    per_tok = (2 * Dk + Dv) * in_bytes + 4 * Dk + 4 + 4 * Dv
+    return n_head_tokens * per_tok + n_heads * Dk * Dv * 4 * (2 if with_s0 else 1)
+
+
+def chunk_alg_flops(n_head_tokens, Dk, Dv, C=64):
+    # three state products, two triangular Gram matrices, triangular P.U, triangular solve on [K|V]
+    return n_head_tokens * (6 * Dk * Dv + 2 * C * Dk + C * Dv + C * (Dk + Dv))
+
+
+def decode_alg_bytes(B, H, Dk, Dv, in_bytes):
+    return B * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * in_bytes + 4 * Dk + 4 + 4 * Dv)
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn warmup times, then `steps` times bracketed by synchronize; per-launch
+    durations from events on the current stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in evs]
+    return wall, float(np.mean(per)), float(np.min(per))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single device.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_65_amd as kda
+    import kda_inputs
+    from tests.gpu_util import device_inputs, rel_err, to_dev
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.load_library()
+
+    # ------------------------------------------------ chunked prefill, B=4 H=16 T=8192 d=128 bf16
+    name = "chunk_b4_h16_t8192_d128_bf16"
+    spec = kda_inputs.workload(name)
+    inp = kda_inputs.generate(spec)
+    d = device_inputs(inp, batched=True)
+    B, T, H, Dk, Dv = spec.n_seq, spec.lengths[0], spec.H, spec.Dk, spec.Dv
+    out = {}
+
+    def step():
+        out["o"], out["s"] = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+
+    wall, k_ms, k_min = time_launches(step, args.steps, args.warmup, torch)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = B * T
+    value = tokens * args.steps / wall
+    n_ht = tokens * H
+    alg_bytes = chunk_alg_bytes(n_ht, B * H, Dk, Dv, 2, with_s0=False)
+    alg_flops = chunk_alg_flops(n_ht, Dk, Dv)
+    gbs = alg_bytes / (k_ms * 1e-3) / 1e9
+    tflops = alg_flops / (k_ms * 1e-3) / 1e12
+    traffic = None
+    tr_path = os.path.join(ROOT, "profiles", "chunk_fwd_traffic.json")
+    if os.path.exists(tr_path):
+        try:
+            traffic = json.load(open(tr_path)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    line = {
+        "metric": "KDA fwd tokens/s (H=16,d=128,T=8192) + % MFMA peak; decode % HBM BW",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "T": T, "H": H, "d_k": Dk, "d_v": Dv, "chunk": 64,
+                   "qkv": "bf16", "gates": "fp32", "state": "fp32", "output": "fp32", "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel<128,false>", "kernel_ms": k_ms, "kernel_ms_min": k_min,
+                     "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
+    }
+
+    if not args.no_extras:
+        # ------------------------------------------------ decode step, B=256 H=32 d=128
+        dspec = kda_inputs.workload("decode_b256_h32_d128_bf16")
+        dinp = kda_inputs.generate(dspec)
+        Bd, Hd = dspec.n_seq, dspec.H
+        dq = to_dev(dinp.q, (Bd, Hd, 128))
+        dk = to_dev(dinp.k, (Bd, Hd, 128))
+        dv = to_dev(dinp.v, (Bd, Hd, 128))
+        dg = to_dev(dinp.g, (Bd, Hd, 128))
+        db = to_dev(dinp.beta, (Bd, Hd))
+        st = [to_dev(dinp.s0), torch.empty_like(to_dev(dinp.s0))]
+        flip = [0]
+        o = torch.empty((Bd, Hd, 128), dtype=torch.float32, device=dq.device)
+
+        def dstep():
+            # ping-pong between two state buffers: every launch reads and writes a full state
+            a = flip[0]
+            rc = kda.decode_step_raw(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
+                                     st[a].data_ptr(), st[1 - a].data_ptr(), o.data_ptr(), Bd, Hd, 128, 128,
+                                     kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
+            assert rc == 0
+            flip[0] = 1 - a
+
+        dsteps = max(20, args.steps)
+        _, dk_ms, dk_min = time_launches(dstep, dsteps, args.warmup, torch)
+        dbytes = decode_alg_bytes(Bd, Hd, 128, 128, 2)
+        dgbs = dbytes / (dk_ms * 1e-3) / 1e9
+        line["decode"] = {"workload": "decode_b256_h32_d128_bf16", "kernel_ms": dk_ms, "kernel_ms_min": dk_min,
+                          "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                          "alg_bytes_per_launch": dbytes, "tokens_per_s": Bd / (dk_ms * 1e-3)}
+        del st, dinp
+
+        # ------------------------------------------------ varlen prefill, 32 sequences
+        vspec = kda_inputs.workload("varlen_n32_h16_d128_bf16")
+        vinp = kda_inputs.generate(vspec)
+        vd = device_inputs(vinp, batched=False)
+
+        def vstep():
+            kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"])
+
+        _, vk_ms, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
+        vbytes = chunk_alg_bytes(vspec.total * vspec.H, vspec.n_seq * vspec.H, 128, 128, 2, with_s0=True)
+        line["varlen"] = {"workload": "varlen_n32_h16_d128_bf16", "tokens": vspec.total,
+                          "longest": max(vspec.lengths), "kernel_ms": vk_ms,
+                          "tokens_per_s": vspec.total / (vk_ms * 1e-3),
+                          "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s"}
+        del vd, vinp
+
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        o_ref, s_ref = oracle.forward_inputs(inp)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                                "kind": "oracle", "seconds": dt,
+                                "sample": f"the whole timed batch ({B}x{T} tokens, {H} heads, all {Dv} columns), "
+                                          "fp64 token-by-token recurrence"}
+        o_gpu = out["o"].reshape(tokens, H, Dv).cpu().numpy()
+        line["parity"] = {"o_err": rel_err(o_gpu, o_ref), "s_err": rel_err(out["s"].cpu().numpy(), s_ref),
+                          "tol": 2e-2, "metric": "max|err|/RMS vs fp64 oracle"}
+
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

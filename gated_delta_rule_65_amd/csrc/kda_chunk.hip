@@ -24,6 +24,12 @@
 // channel the decays between boundaries; no exponent ever exceeds 80 in size,
 // and a factor that underflows multiplies a quantity that is itself below
 // e^-87.
+//
+// Work split inside a workgroup (4 waves, one per SIMD): wave w owns tokens
+// 16w..16w+15 of the chunk for the per-element work and the Gram rows, column
+// block w of M^{-1}, and channel rows 32w..32w+31 (16w..16w+15 for Dk=64) of the
+// state.  The next chunk's inputs are loaded into registers while the current
+// chunk is computed.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -33,35 +39,135 @@ namespace kda {
 
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int kSlice = 32;  // state columns per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DK>
+template <int DK, bool F32>
 struct ChunkLds {
-    static constexpr int PK = DK + 4;  // padded row of DK floats
-    static constexpr int P64 = 68;     // padded row of 64 floats
-    static constexpr int PV = 36;      // padded row of the value slice
-    static constexpr int S = 0;                          // S^T       [32][PK]
-    static constexpr int KBT = S + kSlice * PK;          // Kbar^T    [DK][P64]
-    static constexpr int COL = KBT + DK * P64;           // k*F rows of sub-blocks 0..2 [48][PK]
-    static constexpr int A = COL + 48 * PK;              // b_r * A   [64][P64]
-    static constexpr int T = A + 64 * P64;               // M^{-1}    [64][P64]
-    static constexpr int P = T + 64 * P64;               // P         [64][P64]
-    static constexpr int X = P + 64 * P64;               // (b(V-KS))^T [32][P64]
-    static constexpr int U = X + kSlice * P64;           // U^T       [32][P64]
-    static constexpr int V = U + kSlice * P64;           // V slice   [64][PV]
-    static constexpr int GT = V + kChunk * PV;           // sub-block sums of g [4][DK]
-    static constexpr int GC = GT + 4 * DK;               // gamma_C   [DK]
-    static constexpr int BETA = GC + DK;                 // b         [64]
-    static constexpr int TOTAL = BETA + kChunk;
-    // decay tables, overlaid on X/U (free until the chain step)
-    static constexpr int TPW = X;           // e^{sum_{J<w} Gt_J}  [4][DK]
-    static constexpr int TAF = TPW + 4 * DK;  // e^{sum_{J>w} Gt_J}  [4][DK]
-    static constexpr int TBT = TAF + 4 * DK;  // e^{Gt_w}            [4][DK]
-    static constexpr int TD = TBT + 4 * DK;   // e^{sum_{I<J<R} Gt_J} for (I,R) = (0,2),(1,3),(0,3)  [3][DK]
-    static_assert(TD + 3 * DK <= V, "decay tables overflow");
-    static constexpr int Z = COL;             // solve temporaries [3][16][17], overlaid on COL
-    static_assert(3 * 16 * 17 <= 48 * PK, "solve scratch overflow");
-    static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
+    using MS = LMat<F32, kSlice, DK>;   // S^T          [n][c]
+    using MKB = LMat<F32, DK, kChunk>;  // Kbar^T       [c][t]
+    using MCOL = LMat<true, 48, DK>;    // fp32 k * e^{G_end(blk) - G}, sub-blocks 0..2  [t][c]
+    using MN = LMat<F32, 64, 64>;       // M^{-1}       [t][t]
+    using MP = LMat<F32, 64, 64>;       // P            [t][t]
+    using MX = LMat<F32, kSlice, 64>;   // (b (V - Kt S))^T  [n][t]
+    using MU = LMat<F32, kSlice, 64>;   // U^T          [n][t]
+    static constexpr int S = 0;
+    static constexpr int KB = S + MS::BYTES;
+    static constexpr int COL = KB + MKB::BYTES;
+    static constexpr int N = COL + MCOL::BYTES;
+    static constexpr int P = N + MN::BYTES;
+    static constexpr int X = P + MP::BYTES;
+    static constexpr int U = X + MX::BYTES;
+    static constexpr int A = U;                       // fp32 b_r A_ri [64][68], shares space with U
+    static constexpr int UA_BYTES = (MU::BYTES > 64 * 68 * 4) ? MU::BYTES : 64 * 68 * 4;
+    static constexpr int D = U + UA_BYTES;            // fp32 diagonal inverses [4][16][17]
+    static constexpr int TAB = D + 4 * 16 * 17 * 4;   // fp32 decay tables [15][DK]
+    static constexpr int GT = TAB + 15 * DK * 4;      // fp32 sub-block sums of g (log2 units) [4][DK]
+    static constexpr int GC = GT + 4 * DK * 4;        // fp32 gamma_C [DK]
+    static constexpr int BETA = GC + DK * 4;          // fp32 b [64]
+    static constexpr int TOTAL = BETA + 64 * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
+
+// Row block W of a chunk (rows 16W..16W+15), one pass over the key channels:
+//   Gram blocks I <= W:  A_ri = b_r sum_c kE_rc col_ic (one pass, strictly lower in block W),
+//                        P_ri = sum_c qE_rc col_ic (full precision, lower in block W),
+//     with kE = k e^{Gloc}, qE = q e^{Gloc}; col = k e^{-Gloc} for I = W, and for I < W the
+//     LDS rows k_i e^{G_end(I) - G_i} times e^{G_start(W) - G_end(I)} (both factors <= 1);
+//   chain 1:  X = b (V - Kt S) (one pass), O1 = Qt S (full), with Qt = q e^{G}, Kt = k e^{G}.
+// X goes to LDS (transposed, for U = M^{-1} X), A and P to LDS, O1 stays in accO.
+template <int W, int DK, bool F32>
+__device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>* pk, const float (*E)[8],
+                                            const float (*Ei)[8], const float* tPw, const char* pCol,
+                                            const float* tD, const char* pS, const float* sBeta,
+                                            const float (*vD)[4], float* sA, char* pP, char* pX, f32x4_t* accO,
+                                            int m, int cg) {
+    using Fr = Frag<F32>;
+    constexpr int KS = DK / 32;
+    f32x4_t accA[W + 1], accP[W + 1], accX[2];
+#pragma unroll
+    for (int I = 0; I <= W; ++I) accA[I] = accP[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) accX[nb] = accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c0 = 32 * s + 8 * cg;
+        float qf[8], kf[8], pw[8], x1[8], x2[8], x3[8];
+        raw8_to_float<F32>(pq[s], qf);
+        raw8_to_float<F32>(pk[s], kf);
+        lds_read8(&tPw[W * DK + c0], pw);
+        Fr fqE, fkE, fkd, fQt, fKt;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x1[j] = qf[j] * E[s][j];
+            x2[j] = kf[j] * E[s][j];
+            x3[j] = kf[j] * Ei[s][j];
+        }
+        fqE.set(x1);
+        fkE.set_hi_only(x2);
+        fkd.set(x3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x1[j] *= pw[j];  // q e^{G}
+            x2[j] *= pw[j];  // k e^{G}
+        }
+        fQt.set(x1);
+        fKt.set_hi_only(x2);
+        // chain 1
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const Fr sf = lds_frag<F32, kSlice, DK>(pS, 16 * nb + m, c0);
+            accX[nb] = mma_fast(accX[nb], fKt, sf);
+            accO[nb] = mma_full(accO[nb], fQt, sf);
+        }
+        // Gram blocks below the diagonal
+#pragma unroll
+        for (int I = 0; I < W; ++I) {
+            float cx[8];
+            lds_read8(reinterpret_cast<const float*>(pCol) + (16 * I + m) * (DK + 4) + c0, cx);
+            if constexpr (W >= 2) {
+                if (W - I >= 2) {
+                    const int dsel = (W - I == 3) ? 2 : I;  // (0,2)->0, (1,3)->1, (0,3)->2
+                    float d[8];
+                    lds_read8(&tD[dsel * DK + c0], d);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) cx[j] *= d[j];
+                }
+            }
+            Fr colf;
+            colf.set(cx);
+            accA[I] = mma_fast(accA[I], fkE, colf);
+            accP[I] = mma_full(accP[I], fqE, colf);
+        }
+        // diagonal block
+        accA[W] = mma_fast(accA[W], fkE, fkd);
+        accP[W] = mma_full(accP[W], fqE, fkd);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        f32x4_t xv;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int rr = 16 * W + 4 * cg + jj;
+            xv[jj] = sBeta[rr] * (vD[nb][jj] - accX[nb][jj]);
+        }
+        lds_store4<F32, kSlice, 64>(pX, 16 * nb + m, 16 * W + 4 * cg, xv);
+    }
+#pragma unroll
+    for (int I = 0; I <= W; ++I) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int rr = 4 * cg + jj;  // row inside the sub-block
+            const int gr = 16 * W + rr, gi = 16 * I + m;
+            float a = accA[I][jj], pv = accP[I][jj];
+            if (I == W) {
+                if (m >= rr) a = 0.f;
+                if (m > rr) pv = 0.f;
+            }
+            sA[gr * 68 + gi] = a * sBeta[gr];
+            lds_store1<F32, 64, 64>(pP, gr, gi, pv);
+        }
+    }
+}
 
 template <int DK, bool F32>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
@@ -71,33 +177,31 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
     int Dv) {
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
-    using L = ChunkLds<DK>;
+    using L = ChunkLds<DK, F32>;
     constexpr int KS = DK / 32;   // 32-wide reduction steps over the key dimension
     constexpr int CBW = DK / 64;  // 16-row channel blocks of S owned by each wave
-    constexpr int PK = L::PK, P64 = L::P64, PV = L::PV;
 
     const In* __restrict__ q = static_cast<const In*>(qv);
     const In* __restrict__ k = static_cast<const In*>(kv);
     const In* __restrict__ v = static_cast<const In*>(vv);
 
-    __shared__ __align__(16) float smem[L::TOTAL];
-    float* sS = smem + L::S;
-    float* sKbT = smem + L::KBT;
-    float* sCol = smem + L::COL;
-    float* sA = smem + L::A;
-    float* sT = smem + L::T;
-    float* sP = smem + L::P;
-    float* sX = smem + L::X;
-    float* sU = smem + L::U;
-    float* sV = smem + L::V;
-    float* sGt = smem + L::GT;
-    float* sGC = smem + L::GC;
-    float* sBeta = smem + L::BETA;
-    float* tPw = smem + L::TPW;
-    float* tAf = smem + L::TAF;
-    float* tBt = smem + L::TBT;
-    float* tD = smem + L::TD;
-    float* sZ = smem + L::Z;
+    __shared__ __align__(16) char smem[L::TOTAL];
+    char* pS = smem + L::S;
+    char* pKB = smem + L::KB;
+    char* pCol = smem + L::COL;
+    char* pN = smem + L::N;
+    char* pP = smem + L::P;
+    char* pX = smem + L::X;
+    char* pU = smem + L::U;
+    float* sA = reinterpret_cast<float*>(smem + L::A);
+    float* sD = reinterpret_cast<float*>(smem + L::D);
+    float* tPw = reinterpret_cast<float*>(smem + L::TAB);  // e^{sum_{J<w} Gt_J}      [4][DK]
+    float* tAf = tPw + 4 * DK;                              // e^{sum_{J>w} Gt_J}      [4][DK]
+    float* tBt = tAf + 4 * DK;                              // e^{Gt_w}                [4][DK]
+    float* tD = tBt + 4 * DK;                               // e^{sum_{I<J<R} Gt_J}, (I,R) = (0,2),(1,3),(0,3)
+    float* sGt = reinterpret_cast<float*>(smem + L::GT);
+    float* sGC = reinterpret_cast<float*>(smem + L::GC);
+    float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
 
@@ -123,11 +227,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
     }
     const int col0 = sl * kSlice;
 
-    // Zero T and P once: their blocks above the diagonal are never written.
-    for (int e = tid; e < 64 * P64; e += 256) {
-        sT[e] = 0.f;
-        sP[e] = 0.f;
-    }
+    // M^{-1} and P are lower triangular: zero their planes once, the blocks above
+    // the diagonal are never written.
+    lds_zero<F32, 64, 64>(pN, tid, 256);
+    lds_zero<F32, 64, 64>(pP, tid, 256);
 
     // ---- initial state: wave w owns channel blocks cb = w*CBW + i, both 16-column halves
     f32x4_t accS[CBW][2];
@@ -141,39 +244,100 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
                 const int c = 16 * cb + 4 * cg + jj;
                 accS[ci][nb][jj] = s0 ? s0[((n * H + h) * DK + c) * (int64_t)Dv + col0 + 16 * nb + m] : 0.f;
             }
-            *reinterpret_cast<float4*>(&sS[(16 * nb + m) * PK + 16 * cb + 4 * cg]) =
-                make_float4(accS[ci][nb][0], accS[ci][nb][1], accS[ci][nb][2], accS[ci][nb][3]);
+            lds_store4<F32, kSlice, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
         }
     }
-    __syncthreads();
 
-    const int r = 16 * w + m;  // this lane's token row inside the chunk (phase A layout)
+    const int r = 16 * w + m;  // this lane's token row inside the chunk (per-element layout)
+
+    // ---- prefetch registers: this lane's q/k/g row pieces, its 8 entries of the value
+    // slice in MFMA result layout (rows 16w+4cg+jj, column 16nb+m), one beta.  Rows past
+    // the end of the sequence are loaded from its last row (always valid memory) and
+    // zeroed when consumed, so no load has to be waited for before it is used.
+    Raw8<F32> pq[KS], pk[KS];
+    Raw8<true> pg[KS];
+    In pv[2][4];
+    float pb = 0.f;
+    // The next chunk's loads are issued in four parts spread over the current chunk,
+    // so that the waves of all workgroups do not hit the memory system in one burst.
+    auto prefetch_part = [&](int part, int64_t t0, int nt) {
+        const int64_t base = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK;
+        if (part == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load_raw8(g + base + 32 * s + 8 * cg, pg[s]);
+        } else if (part == 1) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load_raw8(k + base + 32 * s + 8 * cg, pk[s]);
+        } else if (part == 2) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load_raw8(q + base + 32 * s + 8 * cg, pq[s]);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int vr = min(16 * w + 4 * cg + jj, nt - 1);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    pv[nb][jj] = v[((t0 + vr) * H + h) * (int64_t)Dv + col0 + 16 * nb + m];
+            }
+            pb = beta[(t0 + min(tid & 63, nt - 1)) * H + h];
+        }
+    };
+    auto prefetch = [&](int64_t t0, int nt) {
+        for (int part = 0; part < 4; ++part) prefetch_part(part, t0, nt);
+    };
+    if (start < end) prefetch(start, (int)min<int64_t>(kChunk, end - start));
+    lds_barrier();
+
+    f32x4_t oPrev[2];  // output rows of the last chunk computed (rows 16w+4cg+jj, column 16nb+m)
+    auto store_o = [&](int64_t tc, int ntc) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rr = 16 * w + 4 * cg + jj;
+                if (rr < ntc) o[((tc + rr) * H + h) * (int64_t)Dv + col0 + 16 * nb + m] = oPrev[nb][jj];
+            }
+    };
 
     for (int64_t t0 = start; t0 < end; t0 += kChunk) {
         const int nt = (int)min<int64_t>(kChunk, end - t0);
-        const bool rv = r < nt;
 
-        // ---------------- phase A: loads, clamp, sub-block prefix sums of g
-        float qf[KS][8], kf[KS][8], gl[KS][8];
-        {
-            const int64_t base = ((t0 + r) * H + h) * (int64_t)DK;
+        // ---------------- phase A: take the prefetched chunk (rows >= nt contribute nothing:
+        // q = k = v = 0, g = 0, beta = 0)
+        const bool rv = r < nt;
+        // next chunk to prefetch; on the last chunk the current one is read again, so the
+        // loads need no branch (which would cost exact wait counts on the loads in flight)
+        const bool more = t0 + kChunk < end;
+        const int64_t t0_next = more ? t0 + kChunk : t0;
+        const int nt_next = more ? (int)min<int64_t>(kChunk, end - t0 - kChunk) : nt;
+        float gl[KS][8];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (rv) {
-                    load8_as_float(q + base + 32 * s + 8 * cg, qf[s]);
-                    load8_as_float(k + base + 32 * s + 8 * cg, kf[s]);
-                    load8_as_float(g + base + 32 * s + 8 * cg, gl[s]);
-                } else {
+        for (int s = 0; s < KS; ++s) {
+            raw8_to_float<true>(pg[s], gl[s]);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) qf[s][j] = kf[s][j] = gl[s][j] = 0.f;
-                }
-            }
+            for (int j = 0; j < 8; ++j) gl[s][j] = rv ? gl[s][j] : 0.f;
         }
+        prefetch_part(0, t0_next, nt_next);  // g of the next chunk
+        float vD[2][4];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                float x;
+                if constexpr (F32) x = pv[nb][jj];
+                else x = bf16_bits_to_float(pv[nb][jj]);
+                vD[nb][jj] = (16 * w + 4 * cg + jj < nt) ? x : 0.f;
+            }
+        const float bval = (tid < nt) ? pb : 0.f;
+        if (tid < kChunk) sBeta[tid] = bval;
+        prefetch_part(3, t0_next, nt_next);  // v and beta of the next chunk
+
+        // clamp to [-5, 0], convert to log2 units, inclusive sums over each 16-token sub-block
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                gl[s][j] = row16_inclusive_scan(fminf(fmaxf(gl[s][j], -5.f), 0.f));
+                gl[s][j] = row16_inclusive_scan(__builtin_amdgcn_fmed3f(gl[s][j], -5.f, 0.f) * kLog2e);
         if (m == 15) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -182,276 +346,199 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
                 *reinterpret_cast<float4*>(dst + 4) = make_float4(gl[s][4], gl[s][5], gl[s][6], gl[s][7]);
             }
         }
-        {   // value slice [64 tokens][32 columns] and beta
-            const int vr = tid >> 2, vc = (tid & 3) * 8;
-            float vx[8];
-            if (vr < nt) {
-                load8_as_float(v + ((t0 + vr) * H + h) * (int64_t)Dv + col0 + vc, vx);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) vx[j] = 0.f;
-            }
-            *reinterpret_cast<float4*>(&sV[vr * PV + vc]) = make_float4(vx[0], vx[1], vx[2], vx[3]);
-            *reinterpret_cast<float4*>(&sV[vr * PV + vc + 4]) = make_float4(vx[4], vx[5], vx[6], vx[7]);
-            if (tid < kChunk) sBeta[tid] = tid < nt ? beta[(t0 + tid) * H + h] : 0.f;
-        }
-        __syncthreads();
+        lds_barrier();  // (1)
 
         // ---------------- decay tables per (sub-block, channel)
         if (tid < DK) {
             const int c = tid;
             const float G0 = sGt[c], G1 = sGt[DK + c], G2 = sGt[2 * DK + c], G3 = sGt[3 * DK + c];
             tPw[c] = 1.f;
-            tPw[DK + c] = __expf(G0);
-            tPw[2 * DK + c] = __expf(G0 + G1);
-            tPw[3 * DK + c] = __expf(G0 + G1 + G2);
-            tAf[c] = __expf(G1 + G2 + G3);
-            tAf[DK + c] = __expf(G2 + G3);
-            tAf[2 * DK + c] = __expf(G3);
+            tPw[DK + c] = __builtin_amdgcn_exp2f(G0);
+            tPw[2 * DK + c] = __builtin_amdgcn_exp2f(G0 + G1);
+            tPw[3 * DK + c] = __builtin_amdgcn_exp2f(G0 + G1 + G2);
+            tAf[c] = __builtin_amdgcn_exp2f(G1 + G2 + G3);
+            tAf[DK + c] = __builtin_amdgcn_exp2f(G2 + G3);
+            tAf[2 * DK + c] = __builtin_amdgcn_exp2f(G3);
             tAf[3 * DK + c] = 1.f;
-            tBt[c] = __expf(G0);
-            tBt[DK + c] = __expf(G1);
-            tBt[2 * DK + c] = __expf(G2);
-            tBt[3 * DK + c] = __expf(G3);
-            tD[c] = __expf(G1);            // (I=0, R=2)
-            tD[DK + c] = __expf(G2);       // (I=1, R=3)
-            tD[2 * DK + c] = __expf(G1 + G2);  // (I=0, R=3)
-            sGC[c] = __expf(G0 + G1 + G2 + G3);
+            tBt[c] = __builtin_amdgcn_exp2f(G0);
+            tBt[DK + c] = __builtin_amdgcn_exp2f(G1);
+            tBt[2 * DK + c] = __builtin_amdgcn_exp2f(G2);
+            tBt[3 * DK + c] = __builtin_amdgcn_exp2f(G3);
+            tD[c] = __builtin_amdgcn_exp2f(G1);                 // (I=0, R=2)
+            tD[DK + c] = __builtin_amdgcn_exp2f(G2);            // (I=1, R=3)
+            tD[2 * DK + c] = __builtin_amdgcn_exp2f(G1 + G2);   // (I=0, R=3)
+            sGC[c] = __builtin_amdgcn_exp2f(G0 + G1 + G2 + G3);
         }
-        __syncthreads();
+        lds_barrier();  // (2)
 
-        // ---------------- per-element factors and operands (rows of sub-block w)
-        Fr fQt[KS], fKt[KS], fqE[KS], fkE[KS], fkd[KS];
-        float qE[KS][8], kE[KS][8];
+        // ---------------- per-element decay factors; column operands of the Gram blocks below
+        // the diagonal and Kbar^T go to LDS.  Rows past the end of the sequence need no
+        // masking beyond g = 0 and b = 0: their rows of A are zero, so their rows of
+        // M^{-1} are unit rows and their pseudo-values U = b(V - Kt S) = 0.
+        float Ei[KS][8];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int c0 = 32 * s + 8 * cg;
-            float pw[8], af[8], bt[8];
-            lds_read8(&tPw[w * DK + c0], pw);
+            float af[8], bt[8], kf[8], xkf[8], xkb[8];
             lds_read8(&tAf[w * DK + c0], af);
             lds_read8(&tBt[w * DK + c0], bt);
-            float xq[8], xk[8], xkd[8], xkf[8], xkb[8];
+            raw8_to_float<F32>(pk[s], kf);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float E = __expf(gl[s][j]);    // e^{G_r - G_start(w)} in [e^-80, 1]
-                const float Ei = __expf(-gl[s][j]);  // its inverse, <= e^80
-                const float gam = pw[j] * E;         // e^{G_r}
-                const float F = bt[j] * Ei;          // e^{G_end(w) - G_r} in [e^-80, 1]
-                xq[j] = qf[s][j] * gam;
-                xk[j] = kf[s][j] * gam;
-                qE[s][j] = qf[s][j] * E;
-                kE[s][j] = kf[s][j] * E;
-                xkd[j] = kf[s][j] * Ei;
-                xkf[j] = kf[s][j] * F;
-                xkb[j] = kf[s][j] * (af[j] * F);     // e^{G_C - G_r} k_r
+                const float E = __builtin_amdgcn_exp2f(gl[s][j]);   // e^{G_r - G_start(w)} in [e^-80, 1]
+                Ei[s][j] = __builtin_amdgcn_exp2f(-gl[s][j]);       // its inverse, <= e^80
+                gl[s][j] = E;
+                xkf[j] = kf[j] * (bt[j] * Ei[s][j]);                // k e^{G_end(w) - G_r}, factor in [e^-80, 1]
+                xkb[j] = xkf[j] * af[j];                            // k e^{G_C - G_r}
             }
-            fQt[s].set(xq);
-            fKt[s].set_hi_only(xk);
-            fqE[s].set(qE[s]);
-            fkE[s].set_hi_only(kE[s]);
-            fkd[s].set(xkd);
-            if (w < 3) {
-                float* dst = &sCol[r * PK + c0];
-                *reinterpret_cast<float4*>(dst) = make_float4(xkf[0], xkf[1], xkf[2], xkf[3]);
-                *reinterpret_cast<float4*>(dst + 4) = make_float4(xkf[4], xkf[5], xkf[6], xkf[7]);
-            }
+            if (w < 3) lds_store8<true, 48, DK>(pCol, r, c0, xkf);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sKbT[(c0 + j) * P64 + r] = xkb[j];
+            for (int j = 0; j < 8; ++j) lds_store1<F32, DK, kChunk>(pKB, c0 + j, r, xkb[j]);
         }
-        __syncthreads();
+        // output rows of the previous chunk, kept in registers until this chunk's inputs
+        // have been consumed, so that later waits on loads never have to count these stores
+        if (t0 > start) store_o(t0 - kChunk, kChunk);
+        lds_barrier();  // (3)
 
-        // ---------------- decay-folded Gram blocks (w, I), I <= w
-        for (int I = 0; I <= w; ++I) {
-            f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            if (I == w) {
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    accA = mma_fast(accA, fkE[s], fkd[s]);
-                    accP = mma_full(accP, fqE[s], fkd[s]);
-                }
-            } else {
-                const int dsel = (w - I == 2) ? (I == 0 ? 0 : 1) : 2;  // only read when w - I >= 2
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const int c0 = 32 * s + 8 * cg;
-                    float cx[8];
-                    lds_read8(&sCol[(16 * I + m) * PK + c0], cx);
-                    Fr colf;
-                    colf.set(cx);
-                    if (w - I >= 2) {
-                        float d[8], rk[8], rq[8];
-                        lds_read8(&tD[dsel * DK + c0], d);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            rk[j] = kE[s][j] * d[j];
-                            rq[j] = qE[s][j] * d[j];
-                        }
-                        Fr rkf, rqf;
-                        rkf.set_hi_only(rk);
-                        rqf.set(rq);
-                        accA = mma_fast(accA, rkf, colf);
-                        accP = mma_full(accP, rqf, colf);
-                    } else {
-                        accA = mma_fast(accA, fkE[s], colf);
-                        accP = mma_full(accP, fqE[s], colf);
-                    }
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rr = 4 * cg + jj;  // row inside the sub-block
-                const int gr = 16 * w + rr, gi = 16 * I + m;
-                float a = accA[jj], pv = accP[jj];
-                if (I == w) {
-                    if (m >= rr) a = 0.f;
-                    if (m > rr) pv = 0.f;
-                }
-                sA[gr * P64 + gi] = a * sBeta[gr];
-                sP[gr * P64 + gi] = pv;
-            }
+        // ---------------- Gram row block w and chain 1, sharing one pass over the key channels:
+        //   A = b (kE . col^T) strictly lower (one pass), P = qE . col^T lower (full),
+        //   X = b (V - Kt S) (one pass), O1 = Qt S (full).
+        // Each wave runs a copy specialised for its sub-block so that its independent
+        // accumulations interleave.
+        f32x4_t accO[2];
+        switch (w) {
+            case 0: gram_chain1<0, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 1: gram_chain1<1, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 2: gram_chain1<2, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            default: gram_chain1<3, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
         }
-        __syncthreads();
 
-        // ---------------- M^{-1} = (I + A)^{-1}: diagonal sub-blocks by forward substitution
+        lds_barrier();  // (4)
+        prefetch_part(1, t0_next, nt_next);  // k of the next chunk
+
+
+        // ---------------- diagonal blocks of M^{-1} = (I + A)^{-1}: forward substitution,
+        // one column per lane (lanes 0..15 of wave w, block w)
         if (lane < 16) {
             const int cidx = lane;
-            const float* Ab = &sA[(16 * w) * P64 + 16 * w];
+            const float* Ab = &sA[(16 * w) * 68 + 16 * w];
             float x[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                float acc = 0.f;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < rr; ++j) acc = fmaf(Ab[rr * P64 + j], x[j], acc);
-                x[rr] = (rr == cidx) ? 1.f : (rr < cidx ? 0.f : -acc);
+                for (int j = 0; j < rr; ++j) acc[j & 3] = fmaf(Ab[rr * 68 + j], x[j], acc[j & 3]);
+                const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                x[rr] = (rr == cidx) ? 1.f : (rr < cidx ? 0.f : -sum);
             }
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) sT[(16 * w + rr) * P64 + 16 * w + cidx] = x[rr];
+            for (int rr = 0; rr < 16; ++rr) sD[(w * 16 + rr) * 17 + cidx] = x[rr];
         }
-        __syncthreads();
-        // off-diagonal sub-blocks, by distance d = R - I:
-        //   N_RI = -N_RR * sum_{J=I}^{R-1} A_RJ N_JI
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            const int nblk = 4 - d;
-            for (int e = tid; e < nblk * 256; e += 256) {
-                const int b = e >> 8, i = (e >> 4) & 15, j = e & 15;
-                const int R = d + b, I = R - d;
-                float acc = 0.f;
-                for (int J = I; J < R; ++J)
-#pragma unroll
-                    for (int kk = 0; kk < 16; ++kk)
-                        acc = fmaf(sA[(16 * R + i) * P64 + 16 * J + kk], sT[(16 * J + kk) * P64 + 16 * I + j], acc);
-                sZ[(b * 16 + i) * 17 + j] = acc;
-            }
-            __syncthreads();
-            for (int e = tid; e < nblk * 256; e += 256) {
-                const int b = e >> 8, i = (e >> 4) & 15, j = e & 15;
-                const int R = d + b, I = R - d;
-                float acc = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    acc = fmaf(sT[(16 * R + i) * P64 + 16 * R + kk], sZ[(b * 16 + kk) * 17 + j], acc);
-                sT[(16 * R + i) * P64 + 16 * I + j] = -acc;
-            }
-            __syncthreads();
-        }
+        lds_barrier();  // (5)
+        prefetch_part(2, t0_next, nt_next);  // q of the next chunk
 
-        // ---------------- chain 1: X = b (V - Kt S), O1 = Qt S
-        f32x4_t accO[2];
+        // ---------------- column block I = w of M^{-1}:  N_II = D_I,
+        //   N_RI = -D_R sum_{J=I}^{R-1} A_RJ N_JI,  R = I+1..3  (fp32 MFMA, 16x16x4).
+        // A 16x16 result in registers (lane: column m, rows 4cg..4cg+3) is used
+        // directly as the B operand of the next product, reduction index 4cg+j
+        // in MFMA number j.
+        {
+            const int I = w;
+            f32x4_t Nr[4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x4_t accX = {0.f, 0.f, 0.f, 0.f};
-            accO[nb] = accX;
+            for (int R = 0; R < 4; ++R) Nr[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                float sx[8];
-                lds_read8(&sS[(16 * nb + m) * PK + 32 * s + 8 * cg], sx);
-                Fr sf;
-                sf.set(sx);
-                accX = mma_fast(accX, fKt[s], sf);
-                accO[nb] = mma_full(accO[nb], fQt[s], sf);
+            for (int R = 0; R < 4; ++R) {
+                if (R < I) continue;
+                f32x4_t nv;
+                if (R == I) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) nv[jj] = sD[(I * 16 + 4 * cg + jj) * 17 + m];
+                } else {
+                    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int J = 0; J < 3; ++J) {
+                        if (J < I || J >= R) continue;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + m) * 68 + 16 * J + 4 * cg + j],
+                                                                     Nr[J][j], z, 0, 0, 0);
+                    }
+                    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sD[(R * 16 + m) * 17 + 4 * cg + j], z[j], y, 0, 0,
+                                                                 0);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) nv[jj] = -y[jj];
+                }
+                Nr[R] = nv;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) lds_store1<F32, 64, 64>(pN, 16 * R + 4 * cg + jj, 16 * I + m, nv[jj]);
             }
-            float xv[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rr = 16 * w + 4 * cg + jj;
-                xv[jj] = sBeta[rr] * (sV[rr * PV + 16 * nb + m] - accX[jj]);
-            }
-            *reinterpret_cast<float4*>(&sX[(16 * nb + m) * P64 + 16 * w + 4 * cg]) =
-                make_float4(xv[0], xv[1], xv[2], xv[3]);
         }
-        __syncthreads();
+        lds_barrier();  // (6)
 
         // ---------------- chain 2: U = M^{-1} X   (rows of sub-block w)
         const int nk = (w >= 2) ? 2 : 1;  // 32-token steps that reach the diagonal
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x4_t accU = {0.f, 0.f, 0.f, 0.f};
-            for (int kb = 0; kb < nk; ++kb) {
-                float tx[8], xx[8];
-                lds_read8(&sT[(16 * w + m) * P64 + 32 * kb + 8 * cg], tx);
-                lds_read8(&sX[(16 * nb + m) * P64 + 32 * kb + 8 * cg], xx);
-                Fr tf, xf;
-                tf.set(tx);
-                xf.set(xx);
-                accU = mma_full(accU, tf, xf);
-            }
-            *reinterpret_cast<float4*>(&sU[(16 * nb + m) * P64 + 16 * w + 4 * cg]) =
-                make_float4(accU[0], accU[1], accU[2], accU[3]);
-        }
-        __syncthreads();
-
-        // ---------------- chain 3: O = O1 + P U (store), S = gamma_C S + Kbar^T U
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x4_t acc = accO[nb];
-            for (int kb = 0; kb < nk; ++kb) {
-                float px[8], ux[8];
-                lds_read8(&sP[(16 * w + m) * P64 + 32 * kb + 8 * cg], px);
-                lds_read8(&sU[(16 * nb + m) * P64 + 32 * kb + 8 * cg], ux);
-                Fr pf, uf;
-                pf.set(px);
-                uf.set(ux);
-                acc = mma_full(acc, pf, uf);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rr = 16 * w + 4 * cg + jj;
-                if (rr < nt) o[((t0 + rr) * H + h) * (int64_t)Dv + col0 + 16 * nb + m] = acc[jj];
-            }
-        }
-#pragma unroll
-        for (int ci = 0; ci < CBW; ++ci) {
-            const int cb = w * CBW + ci;
-            float gc[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) gc[jj] = sGC[16 * cb + 4 * cg + jj];
-            Fr af[2];
+        {
+            f32x4_t accU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                float kx[8];
-                lds_read8(&sKbT[(16 * cb + m) * P64 + 32 * kb + 8 * cg], kx);
-                af[kb].set(kx);
+                if (kb >= nk) continue;
+                const Fr tf = lds_frag<F32, 64, 64>(pN, 16 * w + m, 32 * kb + 8 * cg);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const Fr xf = lds_frag<F32, kSlice, 64>(pX, 16 * nb + m, 32 * kb + 8 * cg);
+                    accU[nb] = mma_full(accU[nb], tf, xf);
+                }
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                f32x4_t acc;
+            for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kSlice, 64>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
+        }
+        lds_barrier();  // (8)
+
+        // ---------------- chain 3: O = O1 + P U (store), S = gamma_C S + Kbar^T U
+        {
+            Fr uf[2][2];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) acc[jj] = accS[ci][nb][jj] * gc[jj];
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) uf[nb][kb] = lds_frag<F32, kSlice, 64>(pU, 16 * nb + m, 32 * kb + 8 * cg);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb >= nk) continue;
+                const Fr pf = lds_frag<F32, 64, 64>(pP, 16 * w + m, 32 * kb + 8 * cg);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], pf, uf[nb][kb]);
+            }
+#pragma unroll
+            for (int ci = 0; ci < CBW; ++ci) {
+                const int cb = w * CBW + ci;
+                float gc[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) gc[jj] = sGC[16 * cb + 4 * cg + jj];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) accS[ci][nb][jj] *= gc[jj];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    float ux[8];
-                    lds_read8(&sU[(16 * nb + m) * P64 + 32 * kb + 8 * cg], ux);
-                    Fr uf;
-                    uf.set(ux);
-                    acc = mma_full(acc, af[kb], uf);
+                    const Fr af = lds_frag<F32, DK, kChunk>(pKB, 16 * cb + m, 32 * kb + 8 * cg);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], af, uf[nb][kb]);
                 }
-                accS[ci][nb] = acc;
-                *reinterpret_cast<float4*>(&sS[(16 * nb + m) * PK + 16 * cb + 4 * cg]) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kSlice, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
             }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
         }
-        __syncthreads();
+        lds_barrier();  // (9)
+    }
+    if (start < end) {
+        const int64_t t_last = start + ((end - start - 1) / kChunk) * kChunk;
+        store_o(t_last, (int)(end - t_last));
     }
 
     if (s_final) {

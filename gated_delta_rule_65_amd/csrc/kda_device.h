@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -46,6 +47,15 @@ struct Frag;
 template <>
 struct Frag<false> {
     bf16x8_t hi, lo;
+    // value as float: hi + lo (about 16 significant bits)
+    __device__ __forceinline__ void get(float x[8]) const {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)hi[j] + (float)lo[j];
+    }
+    __device__ __forceinline__ void get_hi(float x[8]) const {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)hi[j];
+    }
     __device__ __forceinline__ void set(const float x[8]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -63,6 +73,11 @@ struct Frag<false> {
 template <>
 struct Frag<true> {
     float v[8];
+    __device__ __forceinline__ void get(float x[8]) const {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = v[j];
+    }
+    __device__ __forceinline__ void get_hi(float x[8]) const { get(x); }
     __device__ __forceinline__ void set(const float x[8]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = x[j];
@@ -98,6 +113,10 @@ __device__ __forceinline__ void lds_read8(const float* p, float x[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// not for its outstanding global loads (which may be prefetches still in flight).
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15),
 // Hillis-Steele with row_shr 1, 2, 4, 8; lanes shifted in from outside the row
@@ -113,4 +132,133 @@ __device__ __forceinline__ float row16_inclusive_scan(float x) {
     x += dpp_row_shr<4>(x);
     x += dpp_row_shr<8>(x);
     return x;
+}
+
+// ---------------------------------------------------------------------------
+// Matrices in LDS that feed MFMA operands.  SPLIT policy: two planes, bf16 hi
+// then bf16 lo, each ROWS x STRIDE; an element is split once, when written.
+// F32 policy: one fp32 plane.  Both take 4 bytes per element.  Rows are padded
+// so that sixteen lanes reading 16 bytes from sixteen consecutive rows hit
+// distinct LDS banks.
+// ---------------------------------------------------------------------------
+template <bool F32, int ROWS, int COLS>
+struct LMat {
+    static constexpr int STRIDE = F32 ? COLS + 4 : COLS + 8;
+    static constexpr int PLANE = ROWS * STRIDE;
+    static constexpr int BYTES = PLANE * 4;
+};
+
+template <bool F32, int ROWS, int COLS>
+__device__ __forceinline__ Frag<F32> lds_frag(const char* base, int row, int col) {
+    using M = LMat<F32, ROWS, COLS>;
+    Frag<F32> f;
+    if constexpr (F32) {
+        const float* p = reinterpret_cast<const float*>(base) + row * M::STRIDE + col;
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    } else {
+        const __bf16* p = reinterpret_cast<const __bf16*>(base) + row * M::STRIDE + col;
+        f.hi = *reinterpret_cast<const bf16x8_t*>(p);
+        f.lo = *reinterpret_cast<const bf16x8_t*>(p + M::PLANE);
+    }
+    return f;
+}
+
+template <bool F32, int ROWS, int COLS>
+__device__ __forceinline__ void lds_store8(char* base, int row, int col, const float x[8]) {
+    using M = LMat<F32, ROWS, COLS>;
+    if constexpr (F32) {
+        float* p = reinterpret_cast<float*>(base) + row * M::STRIDE + col;
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        bf16x8_t hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            __bf16 h = (__bf16)x[j];
+            hi[j] = h;
+            lo[j] = (__bf16)(x[j] - (float)h);
+        }
+        __bf16* p = reinterpret_cast<__bf16*>(base) + row * M::STRIDE + col;
+        *reinterpret_cast<bf16x8_t*>(p) = hi;
+        *reinterpret_cast<bf16x8_t*>(p + M::PLANE) = lo;
+    }
+}
+
+template <bool F32, int ROWS, int COLS>
+__device__ __forceinline__ void lds_store4(char* base, int row, int col, f32x4_t x) {
+    using M = LMat<F32, ROWS, COLS>;
+    if constexpr (F32) {
+        float* p = reinterpret_cast<float*>(base) + row * M::STRIDE + col;
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+        bf16x4_t hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __bf16 h = (__bf16)x[j];
+            hi[j] = h;
+            lo[j] = (__bf16)(x[j] - (float)h);
+        }
+        __bf16* p = reinterpret_cast<__bf16*>(base) + row * M::STRIDE + col;
+        *reinterpret_cast<bf16x4_t*>(p) = hi;
+        *reinterpret_cast<bf16x4_t*>(p + M::PLANE) = lo;
+    }
+}
+
+template <bool F32, int ROWS, int COLS>
+__device__ __forceinline__ void lds_store1(char* base, int row, int col, float x) {
+    using M = LMat<F32, ROWS, COLS>;
+    if constexpr (F32) {
+        reinterpret_cast<float*>(base)[row * M::STRIDE + col] = x;
+    } else {
+        __bf16 h = (__bf16)x;
+        __bf16* p = reinterpret_cast<__bf16*>(base) + row * M::STRIDE + col;
+        p[0] = h;
+        p[M::PLANE] = (__bf16)(x - (float)h);
+    }
+}
+
+template <bool F32, int ROWS, int COLS>
+__device__ __forceinline__ void lds_zero(char* base, int tid, int nthreads) {
+    using M = LMat<F32, ROWS, COLS>;
+    float4* p = reinterpret_cast<float4*>(base);
+    for (int i = tid; i < M::BYTES / 16; i += nthreads) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Eight input elements held raw in registers between their global load and use
+// (one 16-byte load for bf16, two for fp32).
+template <bool F32>
+struct Raw8 {
+    uint4 a, b;
+};
+template <>
+struct Raw8<false> {
+    uint4 a;
+};
+__device__ __forceinline__ void load_raw8(const uint16_t* p, Raw8<false>& r) {
+    r.a = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void load_raw8(const float* p, Raw8<true>& r) {
+    r.a = *reinterpret_cast<const uint4*>(p);
+    r.b = *reinterpret_cast<const uint4*>(p + 4);
+}
+__device__ __forceinline__ void zero_raw8(Raw8<false>& r) { r.a = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero_raw8(Raw8<true>& r) { r.a = r.b = make_uint4(0, 0, 0, 0); }
+template <bool F32>
+__device__ __forceinline__ void raw8_to_float(const Raw8<F32>& r, float x[8]) {
+    if constexpr (F32) {
+        x[0] = __uint_as_float(r.a.x); x[1] = __uint_as_float(r.a.y);
+        x[2] = __uint_as_float(r.a.z); x[3] = __uint_as_float(r.a.w);
+        x[4] = __uint_as_float(r.b.x); x[5] = __uint_as_float(r.b.y);
+        x[6] = __uint_as_float(r.b.z); x[7] = __uint_as_float(r.b.w);
+    } else {
+        uint32_t u[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(u[i] << 16);
+            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
 }
