@@ -44,6 +44,30 @@ def decode_alg_bytes(B, H, Dk, Dv, in_bytes):
     return B * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * in_bytes + 4 * Dk + 4 + 4 * Dv)
 
 
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_65_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/traffic.json, scaled by the same counters on a plain copy of known size.
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
+
 def time_launches(fn, steps, warmup, torch):
     """Run fn warmup times, then `steps` times bracketed by synchronize; per-launch
     durations from events on the current stream (the stream the library launches on)."""
@@ -70,6 +94,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
+    ap.add_argument("--only", choices=["chunk", "decode", "varlen"], default=None,
+                    help="time one workload only (for profiler runs); prints its own JSON line")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single device.",
@@ -86,6 +114,23 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     kda.load_library()
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
+        return
+
+    if args.only == "decode":
+        print(json.dumps({"decode": measure_decode(args, torch, kda, kda_inputs, to_dev)}))
+        return
+    if args.only == "varlen":
+        print(json.dumps({"varlen": measure_varlen(args, torch, kda, kda_inputs, device_inputs)}))
+        return
 
     # ------------------------------------------------ chunked prefill, B=4 H=16 T=8192 d=128 bf16
     name = "chunk_b4_h16_t8192_d128_bf16"
@@ -107,13 +152,7 @@ def main():
     alg_flops = chunk_alg_flops(n_ht, Dk, Dv)
     gbs = alg_bytes / (k_ms * 1e-3) / 1e9
     tflops = alg_flops / (k_ms * 1e-3) / 1e12
-    traffic = None
-    tr_path = os.path.join(ROOT, "profiles", "chunk_fwd_traffic.json")
-    if os.path.exists(tr_path):
-        try:
-            traffic = json.load(open(tr_path)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(name)
 
     line = {
         "metric": "KDA fwd tokens/s (H=16,d=128,T=8192) + % MFMA peak; decode % HBM BW",
@@ -138,55 +177,11 @@ def main():
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
     }
 
-    if not args.no_extras:
-        # ------------------------------------------------ decode step, B=256 H=32 d=128
-        dspec = kda_inputs.workload("decode_b256_h32_d128_bf16")
-        dinp = kda_inputs.generate(dspec)
-        Bd, Hd = dspec.n_seq, dspec.H
-        dq = to_dev(dinp.q, (Bd, Hd, 128))
-        dk = to_dev(dinp.k, (Bd, Hd, 128))
-        dv = to_dev(dinp.v, (Bd, Hd, 128))
-        dg = to_dev(dinp.g, (Bd, Hd, 128))
-        db = to_dev(dinp.beta, (Bd, Hd))
-        st = [to_dev(dinp.s0), torch.empty_like(to_dev(dinp.s0))]
-        flip = [0]
-        o = torch.empty((Bd, Hd, 128), dtype=torch.float32, device=dq.device)
+    if args.only is None and not args.no_extras:
+        line["decode"] = measure_decode(args, torch, kda, kda_inputs, to_dev)
+        line["varlen"] = measure_varlen(args, torch, kda, kda_inputs, device_inputs)
 
-        def dstep():
-            # ping-pong between two state buffers: every launch reads and writes a full state
-            a = flip[0]
-            rc = kda.decode_step_raw(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
-                                     st[a].data_ptr(), st[1 - a].data_ptr(), o.data_ptr(), Bd, Hd, 128, 128,
-                                     kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
-            assert rc == 0
-            flip[0] = 1 - a
-
-        dsteps = max(20, args.steps)
-        _, dk_ms, dk_min = time_launches(dstep, dsteps, args.warmup, torch)
-        dbytes = decode_alg_bytes(Bd, Hd, 128, 128, 2)
-        dgbs = dbytes / (dk_ms * 1e-3) / 1e9
-        line["decode"] = {"workload": "decode_b256_h32_d128_bf16", "kernel_ms": dk_ms, "kernel_ms_min": dk_min,
-                          "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                          "alg_bytes_per_launch": dbytes, "tokens_per_s": Bd / (dk_ms * 1e-3)}
-        del st, dinp
-
-        # ------------------------------------------------ varlen prefill, 32 sequences
-        vspec = kda_inputs.workload("varlen_n32_h16_d128_bf16")
-        vinp = kda_inputs.generate(vspec)
-        vd = device_inputs(vinp, batched=False)
-
-        def vstep():
-            kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"])
-
-        _, vk_ms, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
-        vbytes = chunk_alg_bytes(vspec.total * vspec.H, vspec.n_seq * vspec.H, 128, 128, 2, with_s0=True)
-        line["varlen"] = {"workload": "varlen_n32_h16_d128_bf16", "tokens": vspec.total,
-                          "longest": max(vspec.lengths), "kernel_ms": vk_ms,
-                          "tokens_per_s": vspec.total / (vk_ms * 1e-3),
-                          "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s"}
-        del vd, vinp
-
-    if not args.no_cpu_baseline:
+    if args.only is None and not args.no_cpu_baseline:
         import oracle
         t0 = time.perf_counter()
         o_ref, s_ref = oracle.forward_inputs(inp)
@@ -200,6 +195,56 @@ def main():
                           "tol": 2e-2, "metric": "max|err|/RMS vs fp64 oracle"}
 
     print(json.dumps(line))
+
+
+def measure_decode(args, torch, kda, kda_inputs, to_dev):
+    """Single-token decode step, B=256 H=32 d=128: GB/s of algorithmic bytes per launch."""
+    name = "decode_b256_h32_d128_bf16"
+    dspec = kda_inputs.workload(name)
+    dinp = kda_inputs.generate(dspec)
+    Bd, Hd = dspec.n_seq, dspec.H
+    dq = to_dev(dinp.q, (Bd, Hd, 128))
+    dk = to_dev(dinp.k, (Bd, Hd, 128))
+    dv = to_dev(dinp.v, (Bd, Hd, 128))
+    dg = to_dev(dinp.g, (Bd, Hd, 128))
+    db = to_dev(dinp.beta, (Bd, Hd))
+    s0 = to_dev(dinp.s0)
+    st = [s0, torch.empty_like(s0)]
+    flip = [0]
+    o = torch.empty((Bd, Hd, 128), dtype=torch.float32, device=dq.device)
+
+    def dstep():
+        # ping-pong between two state buffers: every launch reads and writes a full state
+        a = flip[0]
+        rc = kda.decode_step_raw(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
+                                 st[a].data_ptr(), st[1 - a].data_ptr(), o.data_ptr(), Bd, Hd, 128, 128,
+                                 kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        flip[0] = 1 - a
+
+    _, dk_ms, dk_min = time_launches(dstep, max(20, args.steps), args.warmup, torch)
+    dbytes = decode_alg_bytes(Bd, Hd, 128, 128, 2)
+    dgbs = dbytes / (dk_ms * 1e-3) / 1e9
+    return {"workload": name, "kernel_ms": dk_ms, "kernel_ms_min": dk_min, "achieved": dgbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_launch": dbytes,
+            "tokens_per_s": Bd / (dk_ms * 1e-3), "traffic": measured_traffic(name)}
+
+
+def measure_varlen(args, torch, kda, kda_inputs, device_inputs):
+    """Packed varlen prefill, 32 sequences (log-uniform lengths), H=16 d=128."""
+    name = "varlen_n32_h16_d128_bf16"
+    vspec = kda_inputs.workload(name)
+    vinp = kda_inputs.generate(vspec)
+    vd = device_inputs(vinp, batched=False)
+
+    def vstep():
+        kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"])
+
+    _, vk_ms, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
+    vbytes = chunk_alg_bytes(vspec.total * vspec.H, vspec.n_seq * vspec.H, 128, 128, 2, with_s0=True)
+    return {"workload": name, "tokens": vspec.total, "longest": max(vspec.lengths), "kernel_ms": vk_ms,
+            "kernel_ms_min": vk_min, "tokens_per_s": vspec.total / (vk_ms * 1e-3),
+            "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s", "alg_bytes_per_launch": vbytes}
 
 
 if __name__ == "__main__":

@@ -189,3 +189,15 @@ def test_s_final_may_alias_s0():
                            64, kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0 and torch.equal(st, sf) and torch.equal(o2, o)
+
+
+def test_workload_prefill_b1_h8_t1m_d128_bf16():
+    """Million-token prefill (long-memory gate): final state and outputs on sampled state
+    columns, each computed exactly by the oracle on its own (columns are independent)."""
+    spec = kda_inputs.workload("prefill_b1_h8_t1m_d128_bf16")
+    inp = kda_inputs.generate(spec)
+    o, s = run_chunk(inp)
+    cols = [0, 45, 127]
+    eo, es = check(inp, o, s, cols=cols)
+    # the state after a million tokens stays bounded (the update is a contraction plus a write)
+    assert np.isfinite(s).all() and np.abs(s).max() < 1e3
