@@ -31,7 +31,7 @@ kda_status ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kda_status check_head_dims(int H, int Dk, int Dv) {
-    if (H < 1) return fail(KDA_ERR_BAD_SHAPE, "H must be >= 1 (got %d)", H);
+    if (H < 1 || H > 65536) return fail(KDA_ERR_BAD_SHAPE, "H must be in [1, 65536] (got %d)", H);
     if (Dk != 64 && Dk != 128) return fail(KDA_ERR_BAD_SHAPE, "Dk must be 64 or 128 (got %d)", Dk);
     if (Dv != 64 && Dv != 128) return fail(KDA_ERR_BAD_SHAPE, "Dv must be 64 or 128 (got %d)", Dv);
     return KDA_OK;

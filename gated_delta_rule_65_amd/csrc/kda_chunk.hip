@@ -66,26 +66,39 @@ struct ChunkLds {
     static constexpr int BETA = GC + DK * 4;          // fp32 b [64]
     static constexpr int TOTAL = BETA + 64 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    // rows of sub-block 3 as Gram row operands (q e^{Gloc}, k e^{Gloc}) for the waves that take
+    // Gram blocks (3,0) and (3,1); they live in the M^{-1} planes, which are free until the
+    // inverse is formed
+    using MR = LMat<F32, 16, DK>;
+    static constexpr int RQ = N;
+    static constexpr int RK = N + MR::BYTES;
+    static_assert(2 * MR::BYTES <= MN::BYTES, "row-operand overlay");
 };
 
 // Row block W of a chunk (rows 16W..16W+15), one pass over the key channels:
-//   Gram blocks I <= W:  A_ri = b_r sum_c kE_rc col_ic (one pass, strictly lower in block W),
-//                        P_ri = sum_c qE_rc col_ic (full precision, lower in block W),
-//     with kE = k e^{Gloc}, qE = q e^{Gloc}; col = k e^{-Gloc} for I = W, and for I < W the
-//     LDS rows k_i e^{G_end(I) - G_i} times e^{G_start(W) - G_end(I)} (both factors <= 1);
+//   Gram blocks:  A_ri = b_r sum_c kE_rc col_ic (one pass, strictly lower in the diagonal block),
+//                 P_ri = sum_c qE_rc col_ic (full precision, lower in the diagonal block),
+//     with kE = k e^{Gloc}, qE = q e^{Gloc}; col = k e^{-Gloc} on the diagonal block, and for a
+//     block I below it the LDS rows k_i e^{G_end(I) - G_i} times e^{G_start(R) - G_end(I)}
+//     (both factors <= 1);
 //   chain 1:  X = b (V - Kt S) (one pass), O1 = Qt S (full), with Qt = q e^{G}, Kt = k e^{G}.
+// The ten Gram blocks are shared out 2/3/3/2: wave 3 keeps (3,2) and (3,3); blocks (3,0) and
+// (3,1) go to waves 0 and 1, which read sub-block 3's row operands from LDS.
 // X goes to LDS (transposed, for U = M^{-1} X), A and P to LDS, O1 stays in accO.
 template <int W, int DK, bool F32>
 __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>* pk, const float (*E)[8],
                                             const float (*Ei)[8], const float* tPw, const char* pCol,
-                                            const float* tD, const char* pS, const float* sBeta,
-                                            const float (*vD)[4], float* sA, char* pP, char* pX, f32x4_t* accO,
-                                            int m, int cg) {
+                                            const float* tD, const char* pS, const char* pRQ, const char* pRK,
+                                            const float* sBeta, const float (*vD)[4], float* sA, char* pP,
+                                            char* pX, f32x4_t* accO, int m, int cg) {
     using Fr = Frag<F32>;
     constexpr int KS = DK / 32;
-    f32x4_t accA[W + 1], accP[W + 1], accX[2];
+    constexpr int IMIN = (W == 3) ? 2 : 0;  // first own Gram block of this row block
+    constexpr bool FOREIGN = (W < 2);       // also takes block (3, W)
+    f32x4_t accA[W + 1], accP[W + 1], accX[2], accAf, accPf;
 #pragma unroll
     for (int I = 0; I <= W; ++I) accA[I] = accP[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accAf = accPf = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) accX[nb] = accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -119,9 +132,9 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
             accX[nb] = mma_fast(accX[nb], fKt, sf);
             accO[nb] = mma_full(accO[nb], fQt, sf);
         }
-        // Gram blocks below the diagonal
+        // own Gram blocks below the diagonal
 #pragma unroll
-        for (int I = 0; I < W; ++I) {
+        for (int I = IMIN; I < W; ++I) {
             float cx[8];
             lds_read8(reinterpret_cast<const float*>(pCol) + (16 * I + m) * (DK + 4) + c0, cx);
             if constexpr (W >= 2) {
@@ -141,6 +154,20 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
         // diagonal block
         accA[W] = mma_fast(accA[W], fkE, fkd);
         accP[W] = mma_full(accP[W], fqE, fkd);
+        // block (3, W) with sub-block 3's row operands
+        if constexpr (FOREIGN) {
+            float cx[8], d[8];
+            lds_read8(reinterpret_cast<const float*>(pCol) + (16 * W + m) * (DK + 4) + c0, cx);
+            lds_read8(&tD[(W == 0 ? 2 : 1) * DK + c0], d);  // e^{G_start(3) - G_end(W)}
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cx[j] *= d[j];
+            Fr colf;
+            colf.set(cx);
+            const Fr rq = lds_frag<F32, 16, DK>(pRQ, m, c0);
+            const Fr rk = lds_frag<F32, 16, DK>(pRK, m, c0);
+            accAf = mma_fast(accAf, rk, colf);
+            accPf = mma_full(accPf, rq, colf);
+        }
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -153,7 +180,7 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
         lds_store4<F32, kSlice, 64>(pX, 16 * nb + m, 16 * W + 4 * cg, xv);
     }
 #pragma unroll
-    for (int I = 0; I <= W; ++I) {
+    for (int I = IMIN; I <= W; ++I) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * cg + jj;  // row inside the sub-block
@@ -165,6 +192,14 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
             }
             sA[gr * 68 + gi] = a * sBeta[gr];
             lds_store1<F32, 64, 64>(pP, gr, gi, pv);
+        }
+    }
+    if constexpr (FOREIGN) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int gr = 48 + 4 * cg + jj, gi = 16 * W + m;
+            sA[gr * 68 + gi] = accAf[jj] * sBeta[gr];
+            lds_store1<F32, 64, 64>(pP, gr, gi, accPf[jj]);
         }
     }
 }
@@ -260,26 +295,36 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
     float pb = 0.f;
     // The next chunk's loads are issued in four parts spread over the current chunk,
     // so that the waves of all workgroups do not hit the memory system in one burst.
+    // Addresses: a per-lane pointer fixed for the whole sequence plus a 64-bit chunk offset
+    // (wave-uniform) plus a 32-bit row offset (row < 64, row stride < 2^25 elements).
+    const uint32_t rs_k = (uint32_t)H * DK, rs_v = (uint32_t)H * (uint32_t)Dv;
+    const In* __restrict__ q_l = q + (int64_t)h * DK + 8 * cg;
+    const In* __restrict__ k_l = k + (int64_t)h * DK + 8 * cg;
+    const float* __restrict__ g_l = g + (int64_t)h * DK + 8 * cg;
+    const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + m;
+    const float* __restrict__ b_l = beta + h;
+    float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + m;
     auto prefetch_part = [&](int part, int64_t t0, int nt) {
-        const int64_t base = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK;
+        const int64_t cq = t0 * (int64_t)rs_k;
+        const uint32_t rq = (uint32_t)min(r, nt - 1) * rs_k;
         if (part == 0) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) load_raw8(g + base + 32 * s + 8 * cg, pg[s]);
+            for (int s = 0; s < KS; ++s) load_raw8(g_l + cq + rq + 32 * s, pg[s]);
         } else if (part == 1) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) load_raw8(k + base + 32 * s + 8 * cg, pk[s]);
+            for (int s = 0; s < KS; ++s) load_raw8(k_l + cq + rq + 32 * s, pk[s]);
         } else if (part == 2) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) load_raw8(q + base + 32 * s + 8 * cg, pq[s]);
+            for (int s = 0; s < KS; ++s) load_raw8(q_l + cq + rq + 32 * s, pq[s]);
         } else {
+            const int64_t cv = t0 * (int64_t)rs_v;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int vr = min(16 * w + 4 * cg + jj, nt - 1);
+                const uint32_t rv = (uint32_t)min(16 * w + 4 * cg + jj, nt - 1) * rs_v;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    pv[nb][jj] = v[((t0 + vr) * H + h) * (int64_t)Dv + col0 + 16 * nb + m];
+                for (int nb = 0; nb < 2; ++nb) pv[nb][jj] = v_l[cv + rv + 16 * nb];
             }
-            pb = beta[(t0 + min(tid & 63, nt - 1)) * H + h];
+            pb = b_l[t0 * H + (uint32_t)min(tid & 63, nt - 1) * (uint32_t)H];
         }
     };
     auto prefetch = [&](int64_t t0, int nt) {
@@ -295,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rr = 16 * w + 4 * cg + jj;
-                if (rr < ntc) o[((tc + rr) * H + h) * (int64_t)Dv + col0 + 16 * nb + m] = oPrev[nb][jj];
+                if (rr < ntc) o_l[tc * (int64_t)rs_v + (uint32_t)rr * rs_v + 16 * nb] = oPrev[nb][jj];
             }
     };
 
@@ -317,7 +362,6 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
 #pragma unroll
             for (int j = 0; j < 8; ++j) gl[s][j] = rv ? gl[s][j] : 0.f;
         }
-        prefetch_part(0, t0_next, nt_next);  // g of the next chunk
         float vD[2][4];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
@@ -391,7 +435,19 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
                 xkf[j] = kf[j] * (bt[j] * Ei[s][j]);                // k e^{G_end(w) - G_r}, factor in [e^-80, 1]
                 xkb[j] = xkf[j] * af[j];                            // k e^{G_C - G_r}
             }
-            if (w < 3) lds_store8<true, 48, DK>(pCol, r, c0, xkf);
+            if (w < 3) {
+                lds_store8<true, 48, DK>(pCol, r, c0, xkf);
+            } else {
+                float qf[8], xqe[8], xke[8];
+                raw8_to_float<F32>(pq[s], qf);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    xqe[j] = qf[j] * gl[s][j];
+                    xke[j] = kf[j] * gl[s][j];
+                }
+                lds_store8<F32, 16, DK>(smem + L::RQ, m, c0, xqe);
+                lds_store8<F32, 16, DK>(smem + L::RK, m, c0, xke);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) lds_store1<F32, DK, kChunk>(pKB, c0 + j, r, xkb[j]);
         }
@@ -407,14 +463,14 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
         // accumulations interleave.
         f32x4_t accO[2];
         switch (w) {
-            case 0: gram_chain1<0, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            case 1: gram_chain1<1, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            case 2: gram_chain1<2, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            default: gram_chain1<3, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 0: gram_chain1<0, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 1: gram_chain1<1, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 2: gram_chain1<2, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            default: gram_chain1<3, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
         }
 
         lds_barrier();  // (4)
-        prefetch_part(1, t0_next, nt_next);  // k of the next chunk
+        prefetch_part(0, t0_next, nt_next);  // g of the next chunk
 
 
         // ---------------- diagonal blocks of M^{-1} = (I + A)^{-1}: forward substitution,
@@ -435,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
             for (int rr = 0; rr < 16; ++rr) sD[(w * 16 + rr) * 17 + cidx] = x[rr];
         }
         lds_barrier();  // (5)
-        prefetch_part(2, t0_next, nt_next);  // q of the next chunk
+        prefetch_part(1, t0_next, nt_next);  // k of the next chunk
 
         // ---------------- column block I = w of M^{-1}:  N_II = D_I,
         //   N_RI = -D_R sum_{J=I}^{R-1} A_RJ N_JI,  R = I+1..3  (fp32 MFMA, 16x16x4).
@@ -444,6 +500,13 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
         // in MFMA number j.
         {
             const int I = w;
+            // blocks above the diagonal were overwritten by the row-operand overlay: zero them
+#pragma unroll
+            for (int R = 0; R < 3; ++R) {
+                if (R >= I) continue;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) lds_store1<F32, 64, 64>(pN, 16 * R + 4 * cg + jj, 16 * I + m, 0.f);
+            }
             f32x4_t Nr[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R) Nr[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -478,6 +541,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
             }
         }
         lds_barrier();  // (6)
+        prefetch_part(2, t0_next, nt_next);  // q of the next chunk
 
         // ---------------- chain 2: U = M^{-1} X   (rows of sub-block w)
         const int nk = (w >= 2) ? 2 : 1;  // 32-token steps that reach the diagonal
