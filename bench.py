@@ -2,11 +2,13 @@
 
 Timed step: one kda_chunk_fwd call over the chunked-prefill batch B=4, H=16,
 T=8192, d_k=d_v=128 (bf16 q/k/v, fp32 gates, fp32 state and output), inputs
-resident in HBM.  value = B*T tokens per step / seconds per step.
+and the workspace resident in HBM (the call launches the per-chunk preparation
+kernel and the state-chain kernel).  value = B*T tokens per step / seconds per step.
 
 Also reported on the same JSON line:
-  roofline      chunk kernel against HBM bandwidth (algorithmic bytes / kernel time)
-  mfma          the same kernel's algorithmic FLOPs against the dense bf16 MFMA peak
+  roofline      the call's two kernels against HBM bandwidth (algorithmic bytes / time)
+  mfma          the same call's algorithmic FLOPs against the dense bf16 MFMA peak
+  fused         the single fused kernel (workspace NULL) on the same batch
   decode        single-token decode step, B=256, H=32, d=128: GB/s against HBM peak
   varlen        packed varlen prefill, 32 sequences, H=16, d=128: tokens/s
   cpu_baseline  the fp64 CPU oracle on the same chunked batch (rank 0 only)
@@ -139,9 +141,13 @@ def main():
     d = device_inputs(inp, batched=True)
     B, T, H, Dk, Dv = spec.n_seq, spec.lengths[0], spec.H, spec.Dk, spec.Dv
     out = {}
+    ws = torch.empty(kda.chunk_workspace_bytes(B, T, H, Dk, Dv), dtype=torch.uint8, device="cuda")
 
     def step():
-        out["o"], out["s"] = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+        out["o"], out["s"] = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws)
+
+    def step_fused():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=True)
 
     wall, k_ms, k_min = time_launches(step, args.steps, args.warmup, torch)
     ms_per_step = wall * 1e3 / args.steps
@@ -171,11 +177,17 @@ def main():
                    "qkv": "bf16", "gates": "fp32", "state": "fp32", "output": "fp32", "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_fwd_kernel<128,false>", "kernel_ms": k_ms, "kernel_ms_min": k_min,
-                     "alg_bytes_per_launch": alg_bytes},
+                     "kernel": "prep_kernel<128,false> + chain_kernel<128,false>", "kernel_ms": k_ms,
+                     "kernel_ms_min": k_min, "alg_bytes_per_launch": alg_bytes,
+                     "workspace_bytes": ws.numel()},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
     }
+    if args.only is None and not args.no_extras:
+        _, f_ms, f_min = time_launches(step_fused, max(10, args.steps // 2), args.warmup, torch)
+        line["fused"] = {"kernel": "chunk_fwd_kernel<128,false>", "kernel_ms": f_ms, "kernel_ms_min": f_min,
+                         "tokens_per_s": tokens / (f_ms * 1e-3),
+                         "achieved": alg_bytes / (f_ms * 1e-3) / 1e9, "unit": "GB/s"}
 
     if args.only is None and not args.no_extras:
         line["decode"] = measure_decode(args, torch, kda, kda_inputs, to_dev)
@@ -237,8 +249,12 @@ def measure_varlen(args, torch, kda, kda_inputs, device_inputs):
     vinp = kda_inputs.generate(vspec)
     vd = device_inputs(vinp, batched=False)
 
+    H, Dk, Dv = vspec.H, vspec.Dk, vspec.Dv
+    ws = torch.empty(kda.varlen_workspace_bytes(vspec.n_seq, vspec.total, H, Dk, Dv), dtype=torch.uint8,
+                     device="cuda")
+
     def vstep():
-        kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"])
+        kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"], workspace=ws)
 
     _, vk_ms, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
     vbytes = chunk_alg_bytes(vspec.total * vspec.H, vspec.n_seq * vspec.H, 128, 128, 2, with_s0=True)

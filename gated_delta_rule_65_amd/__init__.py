@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
-           "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "DTYPE"]
+           "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "chunk_workspace_bytes",
+           "varlen_workspace_bytes", "DTYPE"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -52,11 +53,15 @@ def load_library():
         raise ImportError(f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
                           f"g.build()'` or `python gated_delta_rule_65_amd/_build.py`")
     L = ctypes.CDLL(_LIB_PATH)
-    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, vp]
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, vp, sz, vp]
     L.kda_chunk_fwd.restype = ci
-    L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
     L.kda_varlen_fwd.restype = ci
+    L.kda_chunk_workspace_bytes.argtypes = [i64, i64, ci, ci, ci]
+    L.kda_chunk_workspace_bytes.restype = sz
+    L.kda_varlen_workspace_bytes.argtypes = [i64, i64, ci, ci, ci]
+    L.kda_varlen_workspace_bytes.restype = sz
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, vp]
     L.kda_decode_step.restype = ci
     L.kda_last_error.restype = ctypes.c_char_p
@@ -72,13 +77,24 @@ def _check(status: int):
 
 # ----------------------------------------------------------------- raw calls (ints in, status out)
 
-def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, stream) -> int:
-    return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, stream)
+def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, workspace, workspace_bytes,
+                  stream) -> int:
+    return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, workspace,
+                                        workspace_bytes, stream)
 
 
-def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, stream) -> int:
+def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, workspace,
+                   workspace_bytes, stream) -> int:
     return load_library().kda_varlen_fwd(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype,
-                                         stream)
+                                         workspace, workspace_bytes, stream)
+
+
+def chunk_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int) -> int:
+    return int(load_library().kda_chunk_workspace_bytes(B, T, H, Dk, Dv))
+
+
+def varlen_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int) -> int:
+    return int(load_library().kda_varlen_workspace_bytes(N, total, H, Dk, Dv))
 
 
 def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream) -> int:
@@ -108,14 +124,32 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _workspace(need: int, fused: bool, workspace: Optional[torch.Tensor], device
+               ) -> Tuple[Optional[torch.Tensor], int]:
+    """Pointer and size of the workspace to pass: none for the fused kernel, the caller's buffer,
+    or a fresh torch allocation (torch's caching allocator makes that cheap)."""
+    if fused or need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    else:
+        _need(workspace, "workspace")
+        if workspace.device != device:
+            raise ValueError("workspace must be on the same GPU as q")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-              s0: Optional[torch.Tensor] = None, chunk: int = 64, output_final_state: bool = True
+              s0: Optional[torch.Tensor] = None, chunk: int = 64, output_final_state: bool = True,
+              fused: bool = False, workspace: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill over equal-length sequences.
 
     q, k: [B, T, H, Dk]; v: [B, T, H, Dv] (bf16 or fp32, all the same);
     g (log forget gate, fp32): [B, T, H, Dk]; beta (fp32): [B, T, H]; s0 (fp32): [B, H, Dk, Dv] or None.
     Returns o (fp32) [B, T, H, Dv] and the final state [B, H, Dk, Dv] (or None).
+    By default the two-kernel path runs with a workspace (``workspace`` if given, else allocated);
+    ``fused=True`` selects the single fused kernel, which needs none.
     """
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, Dk]")
@@ -132,19 +166,22 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    ws, ws_bytes = _workspace(chunk_workspace_bytes(B, T, H, Dk, Dv), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(chunk_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
-                             B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], _stream(q.device)))
+                             B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes, _stream(q.device)))
     return o, sf
 
 
 def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                cu_seqlens: torch.Tensor, s0: Optional[torch.Tensor] = None, chunk: int = 64,
-               output_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               output_final_state: bool = True, fused: bool = False, workspace: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Packed variable-length prefill.
 
     q, k, g: [total, H, Dk]; v: [total, H, Dv]; beta: [total, H]; cu_seqlens: int32 [N+1] on the GPU;
     s0: [N, H, Dk, Dv] or None.  Returns o [total, H, Dv] (fp32) and the final states [N, H, Dk, Dv].
+    ``fused`` and ``workspace`` as for :func:`chunk_fwd`.
     """
     if q.dim() != 3:
         raise ValueError("q must be [total, H, Dk]")
@@ -165,9 +202,11 @@ def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
         _need(s0, "s0", torch.float32, (N, H, Dk, Dv))
     o = torch.empty((total, H, Dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
+    ws, ws_bytes = _workspace(varlen_workspace_bytes(N, total, H, Dk, Dv), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(varlen_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
-                              _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], _stream(q.device)))
+                              _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes,
+                              _stream(q.device)))
     return o, sf
 
 

@@ -61,12 +61,21 @@ kda_status launched(hipError_t e, const char* what) {
     return ok();
 }
 
-kda_status run_chunked(const kda::ChunkArgs& a, hipStream_t st, const char* what) {
+kda_status run_chunked(const kda::ChunkArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st,
+                       const char* what) {
     const int64_t grid = kda::chunk_grid_size(a.N, a.H, a.Dv);
     if (grid > 0x7fffffff) return fail(KDA_ERR_BAD_SHAPE, "%s: %lld sequence-heads exceed the grid limit", what,
                                        (long long)(a.N * a.H));
     if (grid == 0) return ok();
-    return launched(kda::launch_chunk_fwd(a, st), what);
+    if (!workspace) return launched(kda::launch_chunk_fwd(a, st), what);
+    if (kda::chunk_slots(a) * a.H > 0x7fffffffLL)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: %lld chunk-heads exceed the grid limit", what,
+                    (long long)(kda::chunk_slots(a) * a.H));
+    const int64_t need = kda::chunk_workspace_bytes(a);
+    if ((uint64_t)need > (uint64_t)workspace_bytes)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: workspace holds %llu bytes, %lld needed", what,
+                    (unsigned long long)workspace_bytes, (long long)need);
+    return launched(kda::launch_chunk_fwd_two_pass(a, workspace, st), what);
 }
 
 }  // namespace
@@ -75,7 +84,7 @@ extern "C" {
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk, int Dv,
-                         int chunk, kda_dtype dtype, void* stream) {
+                         int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
     kda_status st;
     if ((st = check_dtype(dtype)) != KDA_OK) return st;
     if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
@@ -85,16 +94,17 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     const bool tokens = B > 0 && T > 0;
     if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
                           {beta, "beta", tokens}, {o, "o", tokens}, {s0, "s0", false},
-                          {s_final, "s_final", false}})) != KDA_OK)
+                          {s_final, "s_final", false}, {workspace, "workspace", false}})) != KDA_OK)
         return st;
     if (B == 0 || (!tokens && !s_final)) return ok();
     kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, nullptr, T, B * T, B, H, Dk, Dv, dtype == KDA_F32};
-    return run_chunked(a, static_cast<hipStream_t>(stream), "kda_chunk_fwd");
+    return run_chunked(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_chunk_fwd");
 }
 
 kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                           const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
-                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* stream) {
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     kda_status st;
     if ((st = check_dtype(dtype)) != KDA_OK) return st;
     if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
@@ -105,11 +115,11 @@ kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const flo
     if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_ARG, "cu_seqlens is NULL");
     if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
                           {beta, "beta", tokens}, {o, "o", tokens}, {s0, "s0", false},
-                          {s_final, "s_final", false}})) != KDA_OK)
+                          {s_final, "s_final", false}, {workspace, "workspace", false}})) != KDA_OK)
         return st;
     if (N == 0 || (!tokens && !s_final)) return ok();
     kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, cu_seqlens, 0, total, N, H, Dk, Dv, dtype == KDA_F32};
-    return run_chunked(a, static_cast<hipStream_t>(stream), "kda_varlen_fwd");
+    return run_chunked(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_varlen_fwd");
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -136,8 +146,33 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
     return launched(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda_decode_step");
 }
 
+size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv) {
+    if (B <= 0 || T <= 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    kda::ChunkArgs a{};
+    a.T_fixed = T;
+    a.N = B;
+    a.total = B * T;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    return (size_t)kda::chunk_workspace_bytes(a);
+}
+
+size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv) {
+    if (N <= 0 || total <= 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    kda::ChunkArgs a{};
+    static const int32_t dummy = 0;
+    a.cu_seqlens = &dummy;  // only its presence matters for the size
+    a.N = N;
+    a.total = total;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    return (size_t)kda::chunk_workspace_bytes(a);
+}
+
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
-const char* kda_version(void) { return "kda-gfx950 0.1"; }
+const char* kda_version(void) { return "kda-gfx950 0.2"; }
 
 }  // extern "C"

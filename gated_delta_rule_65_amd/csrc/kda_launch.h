@@ -28,6 +28,10 @@ struct DecodeArgs {
 
 int64_t chunk_grid_size(int64_t N, int H, int Dv);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t st);
+// Two-kernel path: per-chunk preparation into a workspace, then the state chain.
+int64_t chunk_slots(const ChunkArgs& a);
+int64_t chunk_workspace_bytes(const ChunkArgs& a);
+hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kda

@@ -36,10 +36,24 @@
  *  - Supported head sizes: Dk, Dv in {64, 128}.  chunk must be 64.
  *  - Calls are reentrant; concurrent calls on different streams must not
  *    write the same buffers.
+ *
+ * Workspace of the prefill entry points
+ * -------------------------------------
+ * kda_chunk_fwd and kda_varlen_fwd take an optional caller-owned device
+ * workspace (16-byte aligned, at least kda_*_workspace_bytes() bytes; no
+ * initial contents needed).  With a workspace, one kernel first prepares every
+ * (chunk, head) in parallel -- the running sums of the gates, the lower
+ * triangular inverse (I + A)^-1 and the decay-weighted query-key block of the
+ * chunk -- and stores them there; a second kernel then carries the state
+ * through the chunks.  With workspace == NULL a single fused kernel does both
+ * and nothing extra is needed.  Both give the same results up to rounding.
+ * A workspace smaller than required is rejected with KDA_ERR_BAD_SHAPE.
+ * The workspace must not be shared by calls that may run concurrently.
  */
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -70,7 +84,15 @@ typedef enum {
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
-                         int Dv, int chunk, kda_dtype dtype, void* stream);
+                         int Dv, int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
+ * the sizes are unsupported): B * ceil(T/64) * H records of
+ * 64*Dk*4 + 2*64*64*4 bytes (about 64 KiB per chunk and head at Dk = 128).
+ */
+size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv);
 
 /*
  * Packed variable-length prefill: N independent sequences stored back to back.
@@ -85,7 +107,16 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  */
 kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                           const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
-                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* stream);
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes kda_varlen_fwd needs (0 if none or unsupported sizes): it
+ * depends only on N and total, not on the offsets, so a buffer sized once
+ * serves every packing of that many tokens: (floor(total/64) + N) * H records
+ * of the size given for kda_chunk_workspace_bytes.
+ */
+size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv);
 
 /*
  * One decoding step (one new token per sequence) on B sequences.

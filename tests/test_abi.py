@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_last_error", "kda_version"]:
+    for n in ["kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_last_error", "kda_version",
+              "kda_chunk_workspace_bytes", "kda_varlen_workspace_bytes"]:
         assert n in names
 
 
@@ -42,7 +43,7 @@ def last_error():
 
 def chunk(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, s_final=None, B=1, T=64, H=1, Dk=128,
-             Dv=128, chunk=64, dtype=1, stream=None)
+             Dv=128, chunk=64, dtype=1, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return kda.chunk_fwd_raw(*a.values())
 
@@ -53,7 +54,8 @@ def chunk(**kw):
     (dict(q=None), 1, "q"), (dict(k=None), 1, "k"), (dict(v=None), 1, "v"), (dict(g=None), 1, "g"),
     (dict(beta=None), 1, "beta"), (dict(o=None), 1, "o"),
     (dict(q=FAKE + 2), 4, "q"), (dict(v=FAKE + 8), 4, "v"), (dict(s0=FAKE + 4), 4, "s0"),
-    (dict(s_final=FAKE + 12), 4, "s_final"),
+    (dict(s_final=FAKE + 12), 4, "s_final"), (dict(workspace=FAKE + 8, workspace_bytes=1 << 30), 4, "workspace"),
+    (dict(workspace=FAKE, workspace_bytes=65535), 2, "workspace"),
 ])
 def test_chunk_validation(kw, status, msg):
     assert chunk(**kw) == status
@@ -69,7 +71,7 @@ def test_chunk_nothing_to_do_returns_ok():
 
 def varlen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, N=2, total=100, s0=None, o=FAKE, s_final=None, H=2,
-             Dk=128, Dv=128, chunk=64, dtype=1, stream=None)
+             Dk=128, Dv=128, chunk=64, dtype=1, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return kda.varlen_fwd_raw(*a.values())
 
@@ -78,10 +80,32 @@ def varlen(**kw):
     (dict(cu=None), 1, "cu_seqlens"), (dict(N=-1), 2, "N"), (dict(total=-5), 2, "total"),
     (dict(total=1 << 31), 2, "int32"), (dict(Dk=48), 2, "Dk"), (dict(chunk=128), 2, "chunk"),
     (dict(o=FAKE + 4), 4, "o"), (dict(dtype=-1), 3, "dtype"), (dict(g=None), 1, "g"),
+    (dict(workspace=FAKE, workspace_bytes=3 * 2 * 65536 - 1), 2, "workspace"),
 ])
 def test_varlen_validation(kw, status, msg):
     assert varlen(**kw) == status
     assert msg in last_error()
+
+
+RECORD = {128: 64 * 128 * 4 + 2 * 64 * 64 * 4, 64: 64 * 64 * 4 + 2 * 64 * 64 * 4}
+
+
+@pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 64, 1, 128, 128), (4, 8192, 16, 128, 128), (2, 65, 3, 64, 128),
+                                         (3, 1, 2, 64, 64)])
+def test_chunk_workspace_size(B, T, H, Dk, Dv):
+    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv) == B * (-(-T // 64)) * H * RECORD[Dk]
+
+
+@pytest.mark.parametrize("N,total,H,Dk", [(2, 100, 2, 128), (32, 65536, 16, 128), (1, 1, 1, 64)])
+def test_varlen_workspace_size(N, total, H, Dk):
+    assert kda.varlen_workspace_bytes(N, total, H, Dk, 128) == (total // 64 + N) * H * RECORD[Dk]
+
+
+def test_workspace_size_of_unsupported_or_empty_is_zero():
+    assert kda.chunk_workspace_bytes(0, 64, 1, 128, 128) == 0
+    assert kda.chunk_workspace_bytes(1, 0, 1, 128, 128) == 0
+    assert kda.chunk_workspace_bytes(1, 64, 1, 96, 128) == 0
+    assert kda.varlen_workspace_bytes(0, 10, 1, 128, 128) == 0
 
 
 def test_varlen_nothing_to_do():

@@ -16,21 +16,39 @@ from tests.gpu_util import TOL, device_inputs, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
+# both implementations of the prefill entry points: the two-kernel path (with a workspace)
+# and the single fused kernel (workspace NULL)
+PATHS = pytest.mark.parametrize("fused", [False, True], ids=["two_pass", "fused"])
 
-def run_chunk(inp, batched=True):
+
+def run_chunk(inp, batched=True, fused=False, workspace=None):
     d = device_inputs(inp, batched)
     if batched:
-        o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+        o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=fused, workspace=workspace)
     else:
-        o, sf = kda.varlen_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["s0"])
+        o, sf = kda.varlen_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["s0"], fused=fused,
+                               workspace=workspace)
     torch.cuda.synchronize()
     sp = inp.spec
     return o.reshape(sp.total, sp.H, sp.Dv).cpu().numpy(), sf.cpu().numpy()
 
 
+_ORACLE_CACHE = {}
+
+
+def reference(inp, cols=None):
+    """Oracle outputs; those of the named workloads are kept for the test of the other path."""
+    key = (inp.spec.name, tuple(cols) if cols is not None else None)
+    if inp.spec.name in kda_inputs.WORKLOADS:
+        if key not in _ORACLE_CACHE:
+            _ORACLE_CACHE[key] = oracle.forward_inputs(inp, cols=cols)
+        return _ORACLE_CACHE[key]
+    return oracle.forward_inputs(inp, cols=cols)
+
+
 def check(inp, o_gpu, s_gpu, cols=None, tol=None):
     tol = tol or TOL[inp.spec.dtype]
-    o_ref, s_ref = oracle.forward_inputs(inp, cols=cols)
+    o_ref, s_ref = reference(inp, cols=cols)
     if cols is not None:
         o_gpu, s_gpu = o_gpu[..., cols], s_gpu[..., cols]
     eo, es = rel_err(o_gpu, o_ref), rel_err(s_gpu, s_ref)
@@ -41,95 +59,106 @@ def check(inp, o_gpu, s_gpu, cols=None, tol=None):
 
 # ----------------------------------------------------------------- the five named workloads
 
-def test_workload_chunk_b1_h1_t256_d64_f32():
+@PATHS
+def test_workload_chunk_b1_h1_t256_d64_f32(fused):
     inp = kda_inputs.generate(kda_inputs.workload("chunk_b1_h1_t256_d64_f32"))
-    check(inp, *run_chunk(inp))
+    check(inp, *run_chunk(inp, fused=fused))
 
 
-def test_workload_chunk_b4_h16_t8192_d128_bf16():
+@PATHS
+def test_workload_chunk_b4_h16_t8192_d128_bf16(fused):
     inp = kda_inputs.generate(kda_inputs.workload("chunk_b4_h16_t8192_d128_bf16"))
-    check(inp, *run_chunk(inp))
+    check(inp, *run_chunk(inp, fused=fused))
 
 
-def test_workload_varlen_n32_h16_d128_bf16():
+@PATHS
+def test_workload_varlen_n32_h16_d128_bf16(fused):
     inp = kda_inputs.generate(kda_inputs.workload("varlen_n32_h16_d128_bf16"))
     cols = [0, 17, 31, 32, 63, 64, 100, 127]
-    check(inp, *run_chunk(inp, batched=False), cols=cols)
+    check(inp, *run_chunk(inp, batched=False, fused=fused), cols=cols)
 
 
 # ----------------------------------------------------------------- edge cases and shapes
 
+@PATHS
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_ragged_lengths(T, dtype):
+def test_ragged_lengths(T, dtype, fused):
     spec = kda_inputs.Spec([T] * 2, 3, 128, 128, dtype, "softplus_bounds", 0.05, s0_std=0.02, seed=11 + T,
                            name=f"T{T}-{dtype}")
     inp = kda_inputs.generate(spec)
-    check(inp, *run_chunk(inp))
+    check(inp, *run_chunk(inp, fused=fused))
 
 
+@PATHS
 @pytest.mark.parametrize("Dk,Dv", [(64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_head_dims(Dk, Dv, dtype):
+def test_head_dims(Dk, Dv, dtype, fused):
     spec = kda_inputs.Spec([150] * 2, 2, Dk, Dv, dtype, "softplus", s0_std=0.02, seed=5, name=f"{Dk}x{Dv}-{dtype}")
     inp = kda_inputs.generate(spec)
-    check(inp, *run_chunk(inp))
+    check(inp, *run_chunk(inp, fused=fused))
 
 
-def test_long_memory_gate():
+@PATHS
+def test_long_memory_gate(fused):
     spec = kda_inputs.Spec([2048], 4, 128, 128, "bf16", "longmem", seed=4, name="longmem-2048")
     inp = kda_inputs.generate(spec)
-    check(inp, *run_chunk(inp))
+    check(inp, *run_chunk(inp, fused=fused))
 
 
-def test_varlen_ragged_with_empty():
+@PATHS
+def test_varlen_ragged_with_empty(fused):
     spec = kda_inputs.Spec([0, 1, 64, 65, 130, 0, 7], 3, 128, 128, "bf16", "softplus", s0_std=0.02, seed=9,
                            packed=True, name="varlen-edge")
     inp = kda_inputs.generate(spec)
-    o, s = run_chunk(inp, batched=False)
+    o, s = run_chunk(inp, batched=False, fused=fused)
     check(inp, o, s)
     # empty sequences pass their initial state through unchanged
     assert np.array_equal(s[0], inp.s0[0]) and np.array_equal(s[5], inp.s0[5])
 
 
-def test_zero_length_returns_initial_state():
+@PATHS
+def test_zero_length_returns_initial_state(fused):
     spec = kda_inputs.Spec([0, 0], 2, 128, 64, "bf16", s0_std=0.5, seed=3)
     inp = kda_inputs.generate(spec)
     s0 = to_dev(inp.s0)
     q = torch.empty(2, 0, 2, 128, dtype=torch.bfloat16, device=s0.device)
     v = torch.empty(2, 0, 2, 64, dtype=torch.bfloat16, device=s0.device)
-    o, sf = kda.chunk_fwd(q, q, v, q.float(), torch.empty(2, 0, 2, device=s0.device), s0)
+    o, sf = kda.chunk_fwd(q, q, v, q.float(), torch.empty(2, 0, 2, device=s0.device), s0, fused=fused)
     torch.cuda.synchronize()
     assert o.numel() == 0 and torch.equal(sf, s0)
-    _, sz = kda.chunk_fwd(q, q, v, q.float(), torch.empty(2, 0, 2, device=s0.device), None)
+    _, sz = kda.chunk_fwd(q, q, v, q.float(), torch.empty(2, 0, 2, device=s0.device), None, fused=fused)
     torch.cuda.synchronize()
     assert not sz.any()
 
 
 # ----------------------------------------------------------------- invariants on the GPU
 
-def test_identity_gate_keeps_state():
+@PATHS
+def test_identity_gate_keeps_state(fused):
     """alpha = 1, beta = 0: S_T = S0 and o_t = S0^T q_t."""
     spec = kda_inputs.Spec([130] * 2, 2, 128, 128, "f32", "softplus", s0_std=0.3, seed=21)
     inp = kda_inputs.generate(spec)
     inp.g[:] = 0.0
     inp.beta[:] = 0.0
-    o, s = run_chunk(inp)
+    o, s = run_chunk(inp, fused=fused)
     np.testing.assert_allclose(s, inp.s0, rtol=0, atol=1e-6)
     check(inp, o, s)
 
 
-def test_zero_in_zero_out():
+@PATHS
+def test_zero_in_zero_out(fused):
     spec = kda_inputs.Spec([100] * 2, 2, 128, 128, "bf16", "softplus", seed=22)
     inp = kda_inputs.generate(spec)
     inp.q[:] = 0
     inp.k[:] = 0
     inp.v[:] = 0
-    o, s = run_chunk(inp)
+    o, s = run_chunk(inp, fused=fused)
     assert not o.any() and not s.any()
 
 
-def test_unit_key_full_write():
+@PATHS
+def test_unit_key_full_write(fused):
     """beta = 1 with unit keys (coordinate axes): k_t^T S_t = v_t; with q = k, o_t = v_t."""
     T, H, D = 96, 2, 128
     spec = kda_inputs.Spec([T], H, D, D, "f32", "softplus", seed=23)
@@ -140,53 +169,83 @@ def test_unit_key_full_write():
     inp.k[np.arange(T)[:, None], np.arange(H)[None, :], idx] = 1.0
     inp.q[:] = inp.k
     inp.beta[:] = 1.0
-    o, s = run_chunk(inp)
+    o, s = run_chunk(inp, fused=fused)
     np.testing.assert_allclose(o, inp.v, rtol=0, atol=1e-4)
 
 
-def test_split_resume_matches_unbroken():
+@PATHS
+def test_split_resume_matches_unbroken(fused):
     spec = kda_inputs.Spec([256], 2, 128, 128, "bf16", "softplus_bounds", 0.05, s0_std=0.02, seed=24)
     inp = kda_inputs.generate(spec)
     d = device_inputs(inp, True)
-    o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=fused)
     T1 = 100
     sl = lambda x, a, b: x[:, a:b].contiguous()
-    oa, sa = kda.chunk_fwd(*(sl(d[n], 0, T1) for n in "q k v g beta".split()), d["s0"])
-    ob, sb = kda.chunk_fwd(*(sl(d[n], T1, 256) for n in "q k v g beta".split()), sa)
+    oa, sa = kda.chunk_fwd(*(sl(d[n], 0, T1) for n in "q k v g beta".split()), d["s0"], fused=fused)
+    ob, sb = kda.chunk_fwd(*(sl(d[n], T1, 256) for n in "q k v g beta".split()), sa, fused=fused)
     torch.cuda.synchronize()
     ref = o.cpu().numpy()
     split = torch.cat([oa, ob], 1).cpu().numpy()
     assert rel_err(split, ref) < 2e-3 and rel_err(sb.cpu().numpy(), sf.cpu().numpy()) < 2e-3
 
 
-def test_varlen_equals_batched():
+@PATHS
+def test_varlen_equals_batched(fused):
     spec = kda_inputs.Spec([192] * 3, 2, 128, 128, "bf16", "softplus", s0_std=0.02, seed=25)
     inp = kda_inputs.generate(spec)
-    ob, sb = run_chunk(inp, batched=True)
-    ov, sv = run_chunk(inp, batched=False)
+    ob, sb = run_chunk(inp, batched=True, fused=fused)
+    ov, sv = run_chunk(inp, batched=False, fused=fused)
     assert np.array_equal(ob, ov) and np.array_equal(sb, sv)
 
 
-def test_bitwise_repeatable():
+def test_two_pass_with_caller_workspace_reused_and_dirty():
+    """The workspace needs no initial contents and one buffer serves calls of different sizes."""
+    big = kda_inputs.generate(kda_inputs.Spec([300] * 2, 3, 128, 128, "bf16", "softplus_bounds", 0.05,
+                                              s0_std=0.02, seed=31, name="ws-big"))
+    small = kda_inputs.generate(kda_inputs.Spec([70, 0, 129], 3, 128, 128, "bf16", "softplus", s0_std=0.02,
+                                                seed=32, packed=True, name="ws-small"))
+    need = kda.chunk_workspace_bytes(2, 300, 3, 128, 128)
+    assert kda.varlen_workspace_bytes(3, 199, 3, 128, 128) <= need
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    check(big, *run_chunk(big, workspace=ws))
+    check(small, *run_chunk(small, batched=False, workspace=ws))
+    ref_o, ref_s = run_chunk(big)
+    o2, s2 = run_chunk(big, workspace=ws)
+    assert np.array_equal(o2, ref_o) and np.array_equal(s2, ref_s)
+
+
+def test_two_pass_rejects_small_workspace():
+    inp = kda_inputs.generate(kda_inputs.Spec([128], 1, 128, 128, "bf16", seed=33))
+    ws = torch.empty(kda.chunk_workspace_bytes(1, 128, 1, 128, 128) - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kda.KDAError, match="workspace"):
+        run_chunk(inp, workspace=ws)
+
+
+@PATHS
+def test_bitwise_repeatable(fused):
     spec = kda_inputs.Spec([300] * 2, 4, 128, 128, "bf16", "softplus_bounds", 0.05, seed=26)
     inp = kda_inputs.generate(spec)
     d = device_inputs(inp, True)
-    o1, s1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
-    o2, s2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    o1, s1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], fused=fused)
+    o2, s2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], fused=fused)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-def test_s_final_may_alias_s0():
+@PATHS
+def test_s_final_may_alias_s0(fused):
     spec = kda_inputs.Spec([130] * 2, 2, 128, 128, "bf16", "softplus", s0_std=0.02, seed=27)
     inp = kda_inputs.generate(spec)
     d = device_inputs(inp, True)
-    o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=fused)
     st = d["s0"].clone()
     o2 = torch.empty_like(o)
+    nws = 0 if fused else kda.chunk_workspace_bytes(2, 130, 2, 128, 128)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     rc = kda.chunk_fwd_raw(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["g"].data_ptr(),
                            d["beta"].data_ptr(), st.data_ptr(), o2.data_ptr(), st.data_ptr(), 2, 130, 2, 128, 128,
-                           64, kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
+                           64, kda.DTYPE[torch.bfloat16], None if fused else ws.data_ptr(), nws,
+                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0 and torch.equal(st, sf) and torch.equal(o2, o)
 
