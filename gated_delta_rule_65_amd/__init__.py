@@ -58,9 +58,9 @@ def load_library():
     L.kda_chunk_fwd.restype = ci
     L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
     L.kda_varlen_fwd.restype = ci
-    L.kda_chunk_workspace_bytes.argtypes = [i64, i64, ci, ci, ci]
+    L.kda_chunk_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_chunk_workspace_bytes.restype = sz
-    L.kda_varlen_workspace_bytes.argtypes = [i64, i64, ci, ci, ci]
+    L.kda_varlen_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_varlen_workspace_bytes.restype = sz
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, vp]
     L.kda_decode_step.restype = ci
@@ -89,12 +89,16 @@ def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, ch
                                          workspace, workspace_bytes, stream)
 
 
-def chunk_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int) -> int:
-    return int(load_library().kda_chunk_workspace_bytes(B, T, H, Dk, Dv))
+def _dtype_code(dtype) -> int:
+    return DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
 
 
-def varlen_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int) -> int:
-    return int(load_library().kda_varlen_workspace_bytes(N, total, H, Dk, Dv))
+def chunk_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype=torch.bfloat16) -> int:
+    return int(load_library().kda_chunk_workspace_bytes(B, T, H, Dk, Dv, _dtype_code(dtype)))
+
+
+def varlen_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int, dtype=torch.bfloat16) -> int:
+    return int(load_library().kda_varlen_workspace_bytes(N, total, H, Dk, Dv, _dtype_code(dtype)))
 
 
 def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream) -> int:
@@ -166,7 +170,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
-    ws, ws_bytes = _workspace(chunk_workspace_bytes(B, T, H, Dk, Dv), fused, workspace, q.device)
+    ws, ws_bytes = _workspace(chunk_workspace_bytes(B, T, H, Dk, Dv, q.dtype), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(chunk_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
                              B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes, _stream(q.device)))
@@ -202,7 +206,7 @@ def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
         _need(s0, "s0", torch.float32, (N, H, Dk, Dv))
     o = torch.empty((total, H, Dv), dtype=torch.float32, device=q.device)
     sf = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device) if output_final_state else None
-    ws, ws_bytes = _workspace(varlen_workspace_bytes(N, total, H, Dk, Dv), fused, workspace, q.device)
+    ws, ws_bytes = _workspace(varlen_workspace_bytes(N, total, H, Dk, Dv, q.dtype), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(varlen_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
                               _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes,

@@ -146,9 +146,11 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
     return launched(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda_decode_step");
 }
 
-size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv) {
+size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype) {
     if (B <= 0 || T <= 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     kda::ChunkArgs a{};
+    a.f32 = dtype == KDA_F32;
     a.T_fixed = T;
     a.N = B;
     a.total = B * T;
@@ -158,9 +160,11 @@ size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv) {
     return (size_t)kda::chunk_workspace_bytes(a);
 }
 
-size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv) {
+size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv, kda_dtype dtype) {
     if (N <= 0 || total <= 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     kda::ChunkArgs a{};
+    a.f32 = dtype == KDA_F32;
     static const int32_t dummy = 0;
     a.cu_seqlens = &dummy;  // only its presence matters for the size
     a.N = N;

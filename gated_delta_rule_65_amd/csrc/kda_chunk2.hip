@@ -2,23 +2,23 @@
 //
 // The chunked form of the gated delta rule ("Kimi K3 Open Model Surpasses Closed
 // GPT and Anthropic Systems on Independent Benchmarks", worldcybernews, second and
-// third paragraphs; see kda_chunk.hip for the equations) splits into work that does
-// not depend on the carried state S and a short state-dependent chain:
+// third paragraphs; kda_chunk.hip derives the equations) splits into work that
+// does not depend on the carried state S and a short state-dependent chain.  With
+// G the running sum of the clamped gates inside a chunk (log2 units), Qt = e^G q,
+// Kt = e^G k, Kbar = e^{G_C - G} k, M = I + A and P the decay-folded Gram blocks:
 //
-//   state independent, per chunk:  G (running sum of clamped g, log2 units),
-//       A and P (decay-folded Gram blocks), M^{-1} = (I + A)^{-1}
-//   state dependent, per chunk:    X = b (V - (e^G k) S),  U = M^{-1} X,
-//       O = (e^G q) S + P U,  S' = Diag(e^{G_C}) S + (e^{G_C - G} k)^T U
+//   per chunk, state independent:  Qt, Kt, Kbar^T, M^{-1} Diag(b), P, gamma_C = e^{G_C}
+//   per chunk, state dependent:    X = V - Kt S,  U = M^{-1} Diag(b) X,
+//                                  O = Qt S + P U,  S' = Diag(gamma_C) S + Kbar^T U
 //
-// prep_kernel runs the first part for every (chunk, head) at once, one workgroup
-// each and two workgroups per CU, and writes G, M^{-1} and P to the workspace.
-// chain_kernel walks the chunks of one (sequence, head, 32-column slice) in order
-// and only runs the state-dependent products, with four barriers per chunk.
-//
-// Workspace record per (chunk slot, head): G fp32 [64][Dk]; then M^{-1} and P as
-// [64][64] planes (bf16 hi, bf16 lo for bf16 inputs; fp32 for fp32 inputs).
-// Chunk slots: equal-length sequences use n * ceil(T/64) + j; packed sequences use
-// floor(cu[n]/64) + n + j, which is unique and below floor(total/64) + N.
+// prep_kernel computes the first line for every (chunk, head) at once, one
+// workgroup each and two per CU, and stores the operands in MFMA fragment order:
+// each stored fragment is one 1 KiB plane per 64 lanes, so every load of the chain
+// kernel is a fully contiguous 1 KiB request.  chain_kernel walks the chunks of one
+// (sequence, head, 32-column slice) in order and only runs the products of the
+// second line, with three workgroup barriers per chunk; each chunk's operands are
+// loaded during the previous chunk, right after the registers they replace are
+// last read.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -28,16 +28,81 @@ namespace kda {
 
 namespace {
 
-constexpr int kC = 64;      // tokens per chunk
-constexpr int kS = 32;      // state columns per chain workgroup
+constexpr int kC = 64;  // tokens per chunk
+constexpr int kS = 32;  // state columns per chain workgroup
 constexpr float kL2e = 1.4426950408889634f;
 
-template <int DK>
-__host__ __device__ constexpr int64_t record_bytes() {
-    return 64 * DK * 4 + 2 * 64 * 64 * 4;
+// ---------------------------------------------------------------------------- fragments in HBM
+// A fragment (eight values per lane, see Frag) is stored as two planes of
+// 64 lanes x 16 B: bf16 hi and bf16 lo (split policy) or fp32 values 0-3 and
+// 4-7 (fp32 policy).  A hi-only fragment of the split policy has one plane.
+constexpr int kPlane = 1024;
+
+template <bool F32>
+__device__ __forceinline__ void gfrag_store(char* grp, int lane, const Frag<F32>& f) {
+    if constexpr (F32) {
+        *reinterpret_cast<float4*>(grp + lane * 16) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+        *reinterpret_cast<float4*>(grp + kPlane + lane * 16) = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+    } else {
+        *reinterpret_cast<bf16x8_t*>(grp + lane * 16) = f.hi;
+        *reinterpret_cast<bf16x8_t*>(grp + kPlane + lane * 16) = f.lo;
+    }
 }
 
-// Sequence range and chunk slot of (sequence n, chunk j).
+template <bool F32>
+__device__ __forceinline__ void gfrag_store_hi(char* grp, int lane, const Frag<F32>& f) {
+    if constexpr (F32) gfrag_store<true>(grp, lane, f);
+    else *reinterpret_cast<bf16x8_t*>(grp + lane * 16) = f.hi;
+}
+
+template <bool F32>
+__device__ __forceinline__ Frag<F32> gfrag_load(const char* grp, int lane) {
+    Frag<F32> f;
+    if constexpr (F32) {
+        const float4 a = *reinterpret_cast<const float4*>(grp + lane * 16);
+        const float4 b = *reinterpret_cast<const float4*>(grp + kPlane + lane * 16);
+        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    } else {
+        f.hi = *reinterpret_cast<const bf16x8_t*>(grp + lane * 16);
+        f.lo = *reinterpret_cast<const bf16x8_t*>(grp + kPlane + lane * 16);
+    }
+    return f;
+}
+
+// Split policy: only the hi plane (the fragment feeds one-pass products only).
+template <bool F32>
+__device__ __forceinline__ Frag<F32> gfrag_load_hi(const char* grp, int lane) {
+    if constexpr (F32) {
+        return gfrag_load<true>(grp, lane);
+    } else {
+        Frag<false> f;
+        f.hi = *reinterpret_cast<const bf16x8_t*>(grp + lane * 16);
+        f.lo = f.hi;  // never read by a one-pass product
+        return f;
+    }
+}
+
+// Row blocks of M^{-1} and P are lower triangular: row block w (16 rows) meets
+// 32-wide column steps kb < nk(w); the six (w, kb) pairs are stored in order.
+__host__ __device__ constexpr int steps_of(int w) { return w >= 2 ? 2 : 1; }
+__host__ __device__ constexpr int pair_of(int w, int kb) { return w < 2 ? w : 2 * w - 2 + kb; }
+
+// Operand record of one (chunk, head): byte offsets of its parts.
+template <int DK, bool F32>
+struct Rec {
+    static constexpr int KS = DK / 32;                      // 32-channel steps
+    static constexpr int KT_PLANES = F32 ? 2 : 1;
+    static constexpr int64_t QT = 0;                        // Qt rows:    [w 4][s KS], 2 planes
+    static constexpr int64_t KT = QT + 4 * KS * 2 * kPlane;  // Kt rows:    [w 4][s KS], KT_PLANES
+    static constexpr int64_t KB = KT + 4 * KS * KT_PLANES * kPlane;  // Kbar^T rows: [c-block DK/16][kb 2], 2 planes
+    static constexpr int64_t NM = KB + (DK / 16) * 2 * 2 * kPlane;   // M^{-1} Diag(b): [pair 6], 2 planes
+    static constexpr int64_t PM = NM + 6 * 2 * kPlane;               // P:            [pair 6], 2 planes
+    static constexpr int64_t GC = PM + 6 * 2 * kPlane;               // gamma_C fp32 [DK]
+    static constexpr int64_t BYTES = GC + DK * 4;
+    static_assert(BYTES % 256 == 0, "records stay 256-byte aligned");
+};
+
 struct SeqRange {
     int64_t start, end;
 };
@@ -54,64 +119,40 @@ __device__ __forceinline__ SeqRange seq_range(const int32_t* cu, int64_t n, int6
     return s;
 }
 
+// Chunk slot of chunk j of sequence n: n * ceil(T/64) + j for equal lengths;
+// floor(cu[n]/64) + n + j for packed sequences (unique, below floor(total/64) + N).
 __device__ __forceinline__ int64_t slot_of(const int32_t* cu, int64_t n, int64_t j, int64_t T_fixed, int64_t start) {
     if (cu) return start / kC + n + j;
     return n * ((T_fixed + kC - 1) / kC) + j;
-}
-
-// 16-bit / 32-bit stores of one element of a [64][64] plane pair.
-template <bool F32>
-__device__ __forceinline__ void ws_store1(char* planes, int row, int col, float x) {
-    if constexpr (F32) {
-        reinterpret_cast<float*>(planes)[row * 64 + col] = x;
-    } else {
-        __bf16* p = reinterpret_cast<__bf16*>(planes);
-        const __bf16 h = (__bf16)x;
-        p[row * 64 + col] = h;
-        p[4096 + row * 64 + col] = (__bf16)(x - (float)h);
-    }
-}
-
-// MFMA operand fragment (eight consecutive columns of one row) of a [64][64] plane pair.
-template <bool F32>
-__device__ __forceinline__ Frag<F32> ws_frag(const char* planes, int row, int col) {
-    Frag<F32> f;
-    if constexpr (F32) {
-        const float* p = reinterpret_cast<const float*>(planes) + row * 64 + col;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-        f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    } else {
-        const __bf16* p = reinterpret_cast<const __bf16*>(planes) + row * 64 + col;
-        f.hi = *reinterpret_cast<const bf16x8_t*>(p);
-        f.lo = *reinterpret_cast<const bf16x8_t*>(p + 4096);
-    }
-    return f;
 }
 
 }  // namespace
 
 // ============================================================================ prep kernel
 
-template <int DK>
+template <int DK, bool F32>
 struct PrepLds {
-    static constexpr int COL = 0;                            // fp32 k e^{G_end(blk)-G}, sub-blocks 0..2 [48][DK+4]
-    static constexpr int A = COL + 48 * (DK + 4) * 4;        // fp32 b_r A_ri [64][68]
-    static constexpr int D = A + 64 * 68 * 4;                // fp32 diagonal inverses [4][16][17]
-    static constexpr int TAB = D + 4 * 16 * 17 * 4;          // fp32 tables [11][DK]
-    static constexpr int GT = TAB + 11 * DK * 4;             // fp32 sub-block sums (log2) [4][DK]
-    static constexpr int BETA = GT + 4 * DK * 4;             // fp32 b [64]
+    using MKB = LMat<F32, DK, kC>;                       // Kbar^T staging [c][t]
+    static constexpr int COL = 0;                         // fp32 Gram column operands, sub-blocks 0..2 [48][DK+4]
+    static constexpr int PM = COL + 48 * (DK + 4) * 4;    // fp32 P [64][68]
+    static constexpr int KB = 0;                          // Kbar^T, over COL and PM once both are read
+    static constexpr int A0 = PM + 64 * 68 * 4;
+    static constexpr int A = A0 > MKB::BYTES ? A0 : MKB::BYTES;  // fp32 b_r A_ri [64][68], then M^{-1} Diag(b)
+    static constexpr int D = A + 64 * 68 * 4;             // fp32 diagonal inverses [4][16][17]
+    static constexpr int TAB = D + 4 * 16 * 17 * 4;       // fp32 tables [12][DK]
+    static constexpr int GT = TAB + 12 * DK * 4;          // fp32 sub-block sums (log2) [4][DK]
+    static constexpr int BETA = GT + 4 * DK * 4;          // fp32 b [64]
     static constexpr int TOTAL = BETA + 64 * 4;
     static_assert(TOTAL <= 80 * 1024, "two prep workgroups per CU");
 };
 
-// Gram row block W (rows 16W..16W+15): A (one pass) into sA (scaled by b_r, strictly lower on
-// the diagonal block), P (full precision) stored to the workspace planes, all blocks I <= W.
+// Gram row block W (rows 16W..16W+15), all column blocks I <= W: A (one pass) into sA,
+// scaled by b_r and strictly lower on the diagonal block; P (full precision) into sP,
+// lower with diagonal; blocks I > W of both are zero.
 template <int W, int DK, bool F32>
 __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf)[8], const float (*E)[8],
                                           const float (*Ei)[8], const float* sCol, const float* tD,
-                                          const float* sBeta, float* sA, char* wsP, int m, int cg) {
+                                          const float* sBeta, float* sA, float* sP, int m, int cg) {
     using Fr = Frag<F32>;
     constexpr int KS = DK / 32;
     f32x4_t accA[W + 1], accP[W + 1];
@@ -158,17 +199,17 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
         for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * cg + jj;
             const int gr = 16 * W + rr, gi = 16 * I + m;
+            float a = 0.f, pv = 0.f;
             if (I <= W) {
-                float a = accA[I][jj], pv = accP[I][jj];
+                a = accA[I][jj];
+                pv = accP[I][jj];
                 if (I == W) {
                     if (m >= rr) a = 0.f;
                     if (m > rr) pv = 0.f;
                 }
-                sA[gr * 68 + gi] = a * sBeta[gr];
-                ws_store1<F32>(wsP, gr, gi, pv);
-            } else {
-                ws_store1<F32>(wsP, gr, gi, 0.f);
             }
+            sA[gr * 68 + gi] = a * sBeta[gr];
+            sP[gr * 68 + gi] = pv;
         }
     }
 }
@@ -179,19 +220,23 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                       int64_t total, int64_t N, int H, char* __restrict__ ws) {
     using In = typename std::conditional<F32, float, uint16_t>::type;
-    using L = PrepLds<DK>;
+    using Fr = Frag<F32>;
+    using L = PrepLds<DK, F32>;
+    using R = Rec<DK, F32>;
     constexpr int KS = DK / 32;
-    constexpr int64_t RB = record_bytes<DK>();
     const In* __restrict__ q = static_cast<const In*>(qv);
     const In* __restrict__ k = static_cast<const In*>(kv);
 
     __shared__ __align__(16) char smem[L::TOTAL];
     float* sCol = reinterpret_cast<float*>(smem + L::COL);
+    float* sP = reinterpret_cast<float*>(smem + L::PM);
+    char* pKB = smem + L::KB;
     float* sA = reinterpret_cast<float*>(smem + L::A);
     float* sD = reinterpret_cast<float*>(smem + L::D);
     float* tCum = reinterpret_cast<float*>(smem + L::TAB);  // sum_{J<w} Gt_J (log2)  [4][DK]
     float* tBt = tCum + 4 * DK;                             // e^{Gt_w}               [4][DK]
     float* tD = tBt + 4 * DK;                               // e^{sum_{I<J<R} Gt_J}   [3][DK]
+    float* tGC = tD + 3 * DK;                               // G_C (log2)             [1][DK]
     float* sGt = reinterpret_cast<float*>(smem + L::GT);
     float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
 
@@ -220,11 +265,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     const int64_t t0 = sr.start + j * kC;
     if (j < 0 || t0 >= sr.end) return;  // unused slot
     const int nt = (int)min<int64_t>(kC, sr.end - t0);
-    char* rec = ws + (slot * H + h) * RB;
-    float* wsG = reinterpret_cast<float*>(rec);
-    char* wsN = rec + 64 * DK * 4;
-    char* wsP = wsN + 64 * 64 * 4;
+    char* rec = ws + (slot * H + h) * R::BYTES;
 
+    // ---- rows of sub-block w; running gate sums inside the sub-block (log2)
     const int r = 16 * w + m;
     const bool rv = r < nt;
     const int64_t base = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + 8 * cg;
@@ -249,7 +292,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
             *reinterpret_cast<float4*>(dst + 4) = make_float4(gl[s][4], gl[s][5], gl[s][6], gl[s][7]);
         }
     }
-    lds_barrier();
+    lds_barrier();  // (1)
+
+    // ---- per-channel tables; gamma_C to the record
     if (tid < DK) {
         const int c = tid;
         const float G0 = sGt[c], G1 = sGt[DK + c], G2 = sGt[2 * DK + c], G3 = sGt[3 * DK + c];
@@ -264,45 +309,51 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         tD[c] = __builtin_amdgcn_exp2f(G1);
         tD[DK + c] = __builtin_amdgcn_exp2f(G2);
         tD[2 * DK + c] = __builtin_amdgcn_exp2f(G1 + G2);
+        const float GC = ((G0 + G1) + G2) + G3;
+        tGC[c] = GC;
+        reinterpret_cast<float*>(rec + R::GC)[c] = __builtin_amdgcn_exp2f(GC);
     }
-    lds_barrier();
+    lds_barrier();  // (2)
 
-    // per-element factors; G to the workspace; Gram column operands to LDS
-    float Ei[KS][8];
+    // ---- Qt, Kt to the record; Gram factors E = e^{Gloc}, Ei = e^{-Gloc}; column operands to LDS
+    float E[KS][8], Ei[KS][8];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int c0 = 32 * s + 8 * cg;
-        float cum[8], bt[8], gout[8], xkf[8];
+        float cum[8], bt[8], xq[8], xk[8], xc[8];
         lds_read8(&tCum[w * DK + c0], cum);
         lds_read8(&tBt[w * DK + c0], bt);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            gout[jj] = cum[jj] + gl[s][jj];
-            const float E = __builtin_amdgcn_exp2f(gl[s][jj]);
+            const float gam = __builtin_amdgcn_exp2f(cum[jj] + gl[s][jj]);  // e^{G_r}
+            xq[jj] = qf[s][jj] * gam;
+            xk[jj] = kf[s][jj] * gam;
+            E[s][jj] = __builtin_amdgcn_exp2f(gl[s][jj]);
             Ei[s][jj] = __builtin_amdgcn_exp2f(-gl[s][jj]);
-            gl[s][jj] = E;
-            xkf[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);
+            xc[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);
         }
-        float* gdst = wsG + r * DK + c0;
-        *reinterpret_cast<float4*>(gdst) = make_float4(gout[0], gout[1], gout[2], gout[3]);
-        *reinterpret_cast<float4*>(gdst + 4) = make_float4(gout[4], gout[5], gout[6], gout[7]);
+        Fr fq, fk;
+        fq.set(xq);
+        fk.set_hi_only(xk);
+        gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);
+        gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane, fk);
         if (w < 3) {
             float* dst = sCol + r * (DK + 4) + c0;
-            *reinterpret_cast<float4*>(dst) = make_float4(xkf[0], xkf[1], xkf[2], xkf[3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(xkf[4], xkf[5], xkf[6], xkf[7]);
+            *reinterpret_cast<float4*>(dst) = make_float4(xc[0], xc[1], xc[2], xc[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(xc[4], xc[5], xc[6], xc[7]);
         }
     }
-    lds_barrier();
+    lds_barrier();  // (3)
 
     switch (w) {
-        case 0: prep_gram<0, DK, F32>(qf, kf, gl, Ei, sCol, tD, sBeta, sA, wsP, m, cg); break;
-        case 1: prep_gram<1, DK, F32>(qf, kf, gl, Ei, sCol, tD, sBeta, sA, wsP, m, cg); break;
-        case 2: prep_gram<2, DK, F32>(qf, kf, gl, Ei, sCol, tD, sBeta, sA, wsP, m, cg); break;
-        default: prep_gram<3, DK, F32>(qf, kf, gl, Ei, sCol, tD, sBeta, sA, wsP, m, cg); break;
+        case 0: prep_gram<0, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
+        case 1: prep_gram<1, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
+        case 2: prep_gram<2, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
+        default: prep_gram<3, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
     }
-    lds_barrier();
+    lds_barrier();  // (4)
 
-    // diagonal blocks of M^{-1} = (I + A)^{-1}: forward substitution, one column per lane
+    // ---- diagonal blocks of M^{-1} = (I + A)^{-1}: forward substitution, one column per lane
     if (lane < 16) {
         const int cidx = lane;
         const float* Ab = &sA[(16 * w) * 68 + 16 * w];
@@ -318,42 +369,89 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) sD[(w * 16 + rr) * 17 + cidx] = x[rr];
     }
-    lds_barrier();
+    // ---- P rows of block w to the record
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= steps_of(w)) continue;
+        float x[8];
+        lds_read8(&sP[r * 68 + 32 * kb + 8 * cg], x);
+        Fr f;
+        f.set(x);
+        gfrag_store<F32>(rec + R::PM + pair_of(w, kb) * 2 * kPlane, lane, f);
+    }
+    lds_barrier();  // (5)
 
-    // column block I = w of M^{-1}: N_II = D_I, N_RI = -D_R sum_{J=I}^{R-1} A_RJ N_JI (fp32 MFMA),
-    // each 16x16 result (lane: column m, rows 4cg..4cg+3) feeding the next product as B operand
+    // ---- column block I = w of M^{-1}: N_II = D_I, N_RI = -D_R sum_{J=I}^{R-1} A_RJ N_JI (fp32 MFMA);
+    // each 16x16 result (lane: column m, rows 4cg..4cg+3) feeds the next product as B operand
+    f32x4_t Nr[4];
     {
         const int I = w;
-        f32x4_t Nr[4];
 #pragma unroll
-        for (int R = 0; R < 4; ++R) Nr[R] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
+        for (int R_ = 0; R_ < 4; ++R_) {
             f32x4_t nv = {0.f, 0.f, 0.f, 0.f};
-            if (R == I) {
+            if (R_ == I) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) nv[jj] = sD[(I * 16 + 4 * cg + jj) * 17 + m];
-            } else if (R > I) {
+            } else if (R_ > I) {
                 f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J < 3; ++J) {
-                    if (J < I || J >= R) continue;
+                    if (J < I || J >= R_) continue;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
-                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R + m) * 68 + 16 * J + 4 * cg + jj],
+                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R_ + m) * 68 + 16 * J + 4 * cg + jj],
                                                                  Nr[J][jj], z, 0, 0, 0);
                 }
                 f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sD[(R * 16 + m) * 17 + 4 * cg + jj], z[jj], y, 0, 0, 0);
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sD[(R_ * 16 + m) * 17 + 4 * cg + jj], z[jj], y, 0, 0, 0);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) nv[jj] = -y[jj];
             }
-            Nr[R] = nv;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ws_store1<F32>(wsN, 16 * R + 4 * cg + jj, 16 * I + m, nv[jj]);
+            Nr[R_] = nv;
         }
+    }
+    // ---- Kbar = e^{G_C - G} k staged transposed ([c][t]) over the Gram operands and P
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c0 = 32 * s + 8 * cg;
+        float cum[8], gcl[8];
+        lds_read8(&tCum[w * DK + c0], cum);
+        lds_read8(&tGC[c0], gcl);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const float kbar = kf[s][jj] * __builtin_amdgcn_exp2f(gcl[jj] - (cum[jj] + gl[s][jj]));
+            lds_store1<F32, DK, kC>(pKB, c0 + jj, r, kbar);
+        }
+    }
+    lds_barrier();  // (6)
+
+    // ---- M^{-1} Diag(b) over A (A is no longer read); Kbar^T fragments to the record
+    {
+        const float bcol = sBeta[16 * w + m];
+#pragma unroll
+        for (int R_ = 0; R_ < 4; ++R_)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sA[(16 * R_ + 4 * cg + jj) * 68 + 16 * w + m] = Nr[R_][jj] * bcol;
+    }
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i) {  // (c-block, kb) groups w, w+4, ...
+        const int gidx = w + 4 * i;
+        const int cb = gidx >> 1, kb = gidx & 1;
+        const Fr f = lds_frag<F32, DK, kC>(pKB, 16 * cb + m, 32 * kb + 8 * cg);
+        gfrag_store<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane, f);
+    }
+    lds_barrier();  // (7)
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb >= steps_of(w)) continue;
+        float x[8];
+        lds_read8(&sA[r * 68 + 32 * kb + 8 * cg], x);
+        Fr f;
+        f.set(x);
+        gfrag_store<F32>(rec + R::NM + pair_of(w, kb) * 2 * kPlane, lane, f);
     }
 }
 
@@ -361,45 +459,32 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
 
 template <int DK, bool F32>
 struct ChainLds {
-    using MS = LMat<F32, kS, DK>;   // S^T           [n][c]
-    using MKB = LMat<F32, DK, kC>;  // Kbar^T        [c][t]
-    using MX = LMat<F32, kS, kC>;   // (b(V - Kt S))^T [n][t]
-    using MU = LMat<F32, kS, kC>;   // U^T           [n][t]
+    using MS = LMat<F32, kS, DK>;  // S^T  [n][c]
+    using MX = LMat<F32, kS, kC>;  // X^T, U^T  [n][t]
     static constexpr int S = 0;
-    static constexpr int KB = S + MS::BYTES;
-    static constexpr int X = KB + MKB::BYTES;
+    static constexpr int X = S + MS::BYTES;
     static constexpr int U = X + MX::BYTES;
-    static constexpr int GCL = U + MU::BYTES;   // fp32 G_C (log2) [DK]
-    static constexpr int GC = GCL + DK * 4;     // fp32 gamma_C    [DK]
-    static constexpr int BETA = GC + DK * 4;    // fp32 b          [64]
-    static constexpr int TOTAL = BETA + 64 * 4;
-    static_assert(TOTAL <= 96 * 1024, "chain LDS");
+    static constexpr int TOTAL = U + MX::BYTES;
 };
 
 template <int DK, bool F32>
-__global__ __launch_bounds__(256, 1) void chain_kernel(
-    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
-    const float* __restrict__ beta, const float* s0, float* __restrict__ o, float* s_final,
-    const int32_t* __restrict__ cu_seqlens, int64_t T_fixed, int64_t total, int64_t N, int H, int Dv,
-    const char* __restrict__ ws) {
+__global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
+                                                       float* __restrict__ o, float* s_final,
+                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
+                                                       int64_t total, int64_t N, int H, int Dv,
+                                                       const char* __restrict__ ws) {
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChainLds<DK, F32>;
+    using R = Rec<DK, F32>;
     constexpr int KS = DK / 32;
-    constexpr int CBW = DK / 64;
-    constexpr int64_t RB = record_bytes<DK>();
-    const In* __restrict__ q = static_cast<const In*>(qv);
-    const In* __restrict__ k = static_cast<const In*>(kv);
+    constexpr int CBW = DK / 64;  // 16-channel blocks of S per wave
     const In* __restrict__ v = static_cast<const In*>(vv);
 
     __shared__ __align__(16) char smem[L::TOTAL];
     char* pS = smem + L::S;
-    char* pKB = smem + L::KB;
     char* pX = smem + L::X;
     char* pU = smem + L::U;
-    float* sGCl = reinterpret_cast<float*>(smem + L::GCL);
-    float* sGC = reinterpret_cast<float*>(smem + L::GC);
-    float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int NS = Dv / kS;
@@ -414,6 +499,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
     const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
     const int64_t start = sr.start, end = sr.end;
     const int col0 = sl * kS;
+    const int nk = steps_of(w);
 
     // initial state (wave w: channel blocks w*CBW.., both 16-column halves)
     f32x4_t accS[CBW][2];
@@ -431,32 +517,28 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
         }
     }
 
-    const int r = 16 * w + m;
-    const int nk = (w >= 2) ? 2 : 1;  // 32-token steps of M^{-1} / P rows that reach the diagonal
-    const uint32_t rs_k = (uint32_t)H * DK, rs_v = (uint32_t)H * (uint32_t)Dv;
-    const In* __restrict__ q_l = q + (int64_t)h * DK + 8 * cg;
-    const In* __restrict__ k_l = k + (int64_t)h * DK + 8 * cg;
+    const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
     const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + m;
-    const float* __restrict__ b_l = beta + h;
     float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + m;
+    auto record = [&](int64_t jc) -> const char* {
+        return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
+    };
 
-    // prefetch registers for one chunk
-    Raw8<F32> pq[KS], pk[KS];
-    Raw8<true> pg[KS];
+    // operands of one chunk, loaded in three groups during the previous chunk
+    Fr fQ[KS], fK[KS], fN[2], fP[2], fKB[CBW][2];
     In pv[2][4];
-    float pb = 0.f;
-    Fr pN[2], pP[2];
-    auto prefetch = [&](int64_t t0, int nt, int64_t jc) {
-        const char* rec = ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * RB;
-        const float* G = reinterpret_cast<const float*>(rec) + r * DK + 8 * cg;
-        const int64_t cq = t0 * (int64_t)rs_k;
-        const uint32_t rq = (uint32_t)min(r, nt - 1) * rs_k;
+    float4 gC[CBW];
+    auto load_qk = [&](const char* rec) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            load_raw8(G + 32 * s, pg[s]);
-            load_raw8(q_l + cq + rq + 32 * s, pq[s]);
-            load_raw8(k_l + cq + rq + 32 * s, pk[s]);
+            fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
+            fK[s] = gfrag_load_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane);
         }
+    };
+    auto load_nv = [&](const char* rec, int64_t t0, int nt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)  // rows of waves 0, 1 stop at token 31: their second step repeats the first
+            fN[kb] = gfrag_load<F32>(rec + R::NM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
         const int64_t cv = t0 * (int64_t)rs_v;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -464,15 +546,17 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) pv[nb][jj] = v_l[cv + rvo + 16 * nb];
         }
-        pb = b_l[t0 * H + (uint32_t)min(tid & 63, nt - 1) * (uint32_t)H];
-        const char* planesN = rec + 64 * DK * 4;
-        const char* planesP = planesN + 64 * 64 * 4;
+    };
+    auto load_pkb = [&](const char* rec) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            // rows 16w..16w+15 only reach tokens below 32*nk; the other step is not needed
-            const int kk = min(kb, nk - 1);
-            pN[kb] = ws_frag<F32>(planesN, r, 32 * kk + 8 * cg);
-            pP[kb] = ws_frag<F32>(planesP, r, 32 * kk + 8 * cg);
+        for (int kb = 0; kb < 2; ++kb)
+            fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
+#pragma unroll
+        for (int ci = 0; ci < CBW; ++ci) {
+            const int cb = w * CBW + ci;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) fKB[ci][kb] = gfrag_load<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane);
+            gC[ci] = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cb + 4 * cg) * 4);
         }
     };
 
@@ -487,98 +571,51 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
             }
     };
 
-    if (start < end) prefetch(start, (int)min<int64_t>(kC, end - start), 0);
+    if (start < end) {
+        const char* rec = record(0);
+        load_qk(rec);
+        load_nv(rec, start, (int)min<int64_t>(kC, end - start));
+        load_pkb(rec);
+    }
     lds_barrier();
 
     int64_t jc = 0;
     for (int64_t t0 = start; t0 < end; t0 += kC, ++jc) {
-        const int nt = (int)min<int64_t>(kC, end - t0);
         const bool more = t0 + kC < end;
         const int64_t t0n = more ? t0 + kC : t0;
-        const int ntn = more ? (int)min<int64_t>(kC, end - t0 - kC) : nt;
-        const int64_t jn = more ? jc + 1 : jc;
+        const int ntn = more ? (int)min<int64_t>(kC, end - t0 - kC) : (int)min<int64_t>(kC, end - t0);
+        const char* recn = record(more ? jc + 1 : jc);  // the current chunk again after the last one
 
-        // ---- take this chunk's prefetched inputs
-        float G[KS][8];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) raw8_to_float<true>(pg[s], G[s]);
-        float vD[2][4];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                if constexpr (F32) vD[nb][jj] = pv[nb][jj];
-                else vD[nb][jj] = bf16_bits_to_float(pv[nb][jj]);
-            }
-        Fr fN[2], fP[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            fN[kb] = pN[kb];
-            fP[kb] = pP[kb];
-        }
-        const float bval = (tid < nt) ? pb : 0.f;
-        if (tid < kC) sBeta[tid] = bval;
-        if (r == 63) {  // the chunk's total decay per channel (G of its last row)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                float* dst = &sGCl[32 * s + 8 * cg];
-                *reinterpret_cast<float4*>(dst) = make_float4(G[s][0], G[s][1], G[s][2], G[s][3]);
-                *reinterpret_cast<float4*>(dst + 4) = make_float4(G[s][4], G[s][5], G[s][6], G[s][7]);
-            }
-        }
-        lds_barrier();  // (1)
-
-        // ---- operands and chain 1:  X = b (V - Kt S) (one pass), O1 = Qt S (full)
-        float qf[KS][8], kf[KS][8];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            raw8_to_float<F32>(pq[s], qf[s]);
-            raw8_to_float<F32>(pk[s], kf[s]);
-        }
-        if (tid < DK) sGC[tid] = __builtin_amdgcn_exp2f(sGCl[tid]);
-        prefetch(t0n, ntn, jn);  // next chunk (the current one again on the last chunk)
+        // ---- chain 1:  X = V - Kt S (one pass), O1 = Qt S (full)
         f32x4_t accO[2], accX[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) accX[nb] = accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const int c0 = 32 * s + 8 * cg;
-            float gc[8], xq[8], xk[8], xb[8];
-            lds_read8(&sGCl[c0], gc);
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float gam = __builtin_amdgcn_exp2f(G[s][jj]);            // e^{G_r}
-                const float gbar = __builtin_amdgcn_exp2f(gc[jj] - G[s][jj]);  // e^{G_C - G_r}
-                xq[jj] = qf[s][jj] * gam;
-                xk[jj] = kf[s][jj] * gam;
-                xb[jj] = kf[s][jj] * gbar;
-            }
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) lds_store1<F32, DK, kC>(pKB, c0 + jj, r, xb[jj]);
-            Fr fQt, fKt;
-            fQt.set(xq);
-            fKt.set_hi_only(xk);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                const Fr sf = lds_frag<F32, kS, DK>(pS, 16 * nb + m, c0);
-                accX[nb] = mma_fast(accX[nb], fKt, sf);
-                accO[nb] = mma_full(accO[nb], fQt, sf);
+                const Fr sf = lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg);
+                accX[nb] = mma_fast(accX[nb], fK[s], sf);
+                accO[nb] = mma_full(accO[nb], fQ[s], sf);
             }
         }
+        load_qk(recn);
         if (t0 > start) store_o(t0 - kC, kC);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             f32x4_t xv;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int rr = 16 * w + 4 * cg + jj;
-                xv[jj] = sBeta[rr] * (vD[nb][jj] - accX[nb][jj]);
+                float vj;
+                if constexpr (F32) vj = pv[nb][jj];
+                else vj = bf16_bits_to_float(pv[nb][jj]);
+                xv[jj] = vj - accX[nb][jj];
             }
             lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
         }
-        lds_barrier();  // (2)
+        lds_barrier();  // (1)
 
-        // ---- chain 2: U = M^{-1} X (rows of sub-block w)
+        // ---- chain 2:  U = M^{-1} Diag(b) X  (rows of sub-block w)
         {
             f32x4_t accU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -590,12 +627,13 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
                     accU[nb] = mma_full(accU[nb], fN[kb], xf);
                 }
             }
+            load_nv(recn, t0n, ntn);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
         }
-        lds_barrier();  // (3)
+        lds_barrier();  // (2)
 
-        // ---- chain 3: O = O1 + P U, S = gamma_C S + Kbar^T U
+        // ---- chain 3:  O = O1 + P U,  S = gamma_C S + Kbar^T U
         {
             Fr uf[2][2];
 #pragma unroll
@@ -610,27 +648,27 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(
             }
 #pragma unroll
             for (int ci = 0; ci < CBW; ++ci) {
-                const int cb = w * CBW + ci;
-                float gcv[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) gcv[jj] = sGC[16 * cb + 4 * cg + jj];
+                const float gcv[4] = {gC[ci].x, gC[ci].y, gC[ci].z, gC[ci].w};
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) accS[ci][nb][jj] *= gcv[jj];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const Fr af = lds_frag<F32, DK, kC>(pKB, 16 * cb + m, 32 * kb + 8 * cg);
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], af, uf[nb][kb]);
-                }
+                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], fKB[ci][kb], uf[nb][kb]);
+            }
+            load_pkb(recn);
+#pragma unroll
+            for (int ci = 0; ci < CBW; ++ci) {
+                const int cb = w * CBW + ci;
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
         }
-        lds_barrier();  // (4)
+        lds_barrier();  // (3)
     }
     if (start < end) {
         const int64_t t_last = start + ((end - start - 1) / kC) * kC;
@@ -658,10 +696,12 @@ int64_t chunk_slots(const ChunkArgs& a) {
     return a.N * ((a.T_fixed + kC - 1) / kC);
 }
 
-int64_t chunk_workspace_bytes(const ChunkArgs& a) {
-    const int64_t rb = a.Dk == 128 ? record_bytes<128>() : record_bytes<64>();
-    return chunk_slots(a) * a.H * rb;
+int64_t chunk_record_bytes(int Dk, bool f32) {
+    if (Dk == 128) return f32 ? Rec<128, true>::BYTES : Rec<128, false>::BYTES;
+    return f32 ? Rec<64, true>::BYTES : Rec<64, false>::BYTES;
 }
+
+int64_t chunk_workspace_bytes(const ChunkArgs& a) { return chunk_slots(a) * a.H * chunk_record_bytes(a.Dk, a.f32); }
 
 template <int DK, bool F32>
 static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
@@ -672,9 +712,8 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t grid = chunk_grid_size(a.N, a.H, a.Dv);
-    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)grid), dim3(256), 0, st, a.q, a.k, a.v, a.beta, a.s0,
-                       a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv,
-                       static_cast<const char*>(ws));
+    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)grid), dim3(256), 0, st, a.v, a.s0, a.o, a.s_final,
+                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, static_cast<const char*>(ws));
     return hipGetLastError();
 }
 

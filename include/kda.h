@@ -42,10 +42,10 @@
  * kda_chunk_fwd and kda_varlen_fwd take an optional caller-owned device
  * workspace (16-byte aligned, at least kda_*_workspace_bytes() bytes; no
  * initial contents needed).  With a workspace, one kernel first prepares every
- * (chunk, head) in parallel -- the running sums of the gates, the lower
- * triangular inverse (I + A)^-1 and the decay-weighted query-key block of the
- * chunk -- and stores them there; a second kernel then carries the state
- * through the chunks.  With workspace == NULL a single fused kernel does both
+ * (chunk, head) in parallel -- the decay-weighted queries and keys, the lower
+ * triangular inverse (I + A)^-1 scaled by beta and the decay-weighted
+ * query-key block of the chunk, in matrix-core operand order -- and stores
+ * them there; a second kernel then carries the state through the chunks.  With workspace == NULL a single fused kernel does both
  * and nothing extra is needed.  Both give the same results up to rounding.
  * A workspace smaller than required is rejected with KDA_ERR_BAD_SHAPE.
  * The workspace must not be shared by calls that may run concurrently.
@@ -89,10 +89,11 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
 /*
  * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
- * the sizes are unsupported): B * ceil(T/64) * H records of
- * 64*Dk*4 + 2*64*64*4 bytes (about 64 KiB per chunk and head at Dk = 128).
+ * the arguments are unsupported): B * ceil(T/64) * H records of
+ * 64*Dk*10 (bf16) or 64*Dk*12 (fp32) + 24576 + 4*Dk bytes
+ * (104.5 KiB per chunk and head at Dk = 128 with bf16 inputs).
  */
-size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv);
+size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype);
 
 /*
  * Packed variable-length prefill: N independent sequences stored back to back.
@@ -116,7 +117,7 @@ kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const flo
  * serves every packing of that many tokens: (floor(total/64) + N) * H records
  * of the size given for kda_chunk_workspace_bytes.
  */
-size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv);
+size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv, kda_dtype dtype);
 
 /*
  * One decoding step (one new token per sequence) on B sequences.

@@ -55,7 +55,7 @@ def chunk(**kw):
     (dict(beta=None), 1, "beta"), (dict(o=None), 1, "o"),
     (dict(q=FAKE + 2), 4, "q"), (dict(v=FAKE + 8), 4, "v"), (dict(s0=FAKE + 4), 4, "s0"),
     (dict(s_final=FAKE + 12), 4, "s_final"), (dict(workspace=FAKE + 8, workspace_bytes=1 << 30), 4, "workspace"),
-    (dict(workspace=FAKE, workspace_bytes=65535), 2, "workspace"),
+    (dict(workspace=FAKE, workspace_bytes=107007), 2, "workspace"),
 ])
 def test_chunk_validation(kw, status, msg):
     assert chunk(**kw) == status
@@ -80,31 +80,43 @@ def varlen(**kw):
     (dict(cu=None), 1, "cu_seqlens"), (dict(N=-1), 2, "N"), (dict(total=-5), 2, "total"),
     (dict(total=1 << 31), 2, "int32"), (dict(Dk=48), 2, "Dk"), (dict(chunk=128), 2, "chunk"),
     (dict(o=FAKE + 4), 4, "o"), (dict(dtype=-1), 3, "dtype"), (dict(g=None), 1, "g"),
-    (dict(workspace=FAKE, workspace_bytes=3 * 2 * 65536 - 1), 2, "workspace"),
+    (dict(workspace=FAKE, workspace_bytes=(100 // 64 + 2) * 2 * 107008 - 1), 2, "workspace"),
 ])
 def test_varlen_validation(kw, status, msg):
     assert varlen(**kw) == status
     assert msg in last_error()
 
 
-RECORD = {128: 64 * 128 * 4 + 2 * 64 * 64 * 4, 64: 64 * 64 * 4 + 2 * 64 * 64 * 4}
+def record_bytes(Dk, dtype):
+    """Operand record of one (chunk, head): Qt (split, 4 B/value), Kt (bf16 hi 2 B or fp32 4 B),
+    Kbar^T (4 B), six 2 KiB fragments each of M^{-1} Diag(b) and of P, gamma_C (fp32)."""
+    kt = 4 if dtype == 0 else 2
+    return 64 * Dk * (4 + kt + 4) + 2 * 6 * 2048 + 4 * Dk
 
 
+def test_record_sizes():
+    assert record_bytes(128, 1) == 107008 and record_bytes(128, 0) == 123392
+    assert record_bytes(64, 1) == 65792 and record_bytes(64, 0) == 73984
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 64, 1, 128, 128), (4, 8192, 16, 128, 128), (2, 65, 3, 64, 128),
                                          (3, 1, 2, 64, 64)])
-def test_chunk_workspace_size(B, T, H, Dk, Dv):
-    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv) == B * (-(-T // 64)) * H * RECORD[Dk]
+def test_chunk_workspace_size(B, T, H, Dk, Dv, dtype):
+    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv, dtype) == B * (-(-T // 64)) * H * record_bytes(Dk, dtype)
 
 
+@pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("N,total,H,Dk", [(2, 100, 2, 128), (32, 65536, 16, 128), (1, 1, 1, 64)])
-def test_varlen_workspace_size(N, total, H, Dk):
-    assert kda.varlen_workspace_bytes(N, total, H, Dk, 128) == (total // 64 + N) * H * RECORD[Dk]
+def test_varlen_workspace_size(N, total, H, Dk, dtype):
+    assert kda.varlen_workspace_bytes(N, total, H, Dk, 128, dtype) == (total // 64 + N) * H * record_bytes(Dk, dtype)
 
 
 def test_workspace_size_of_unsupported_or_empty_is_zero():
     assert kda.chunk_workspace_bytes(0, 64, 1, 128, 128) == 0
     assert kda.chunk_workspace_bytes(1, 0, 1, 128, 128) == 0
     assert kda.chunk_workspace_bytes(1, 64, 1, 96, 128) == 0
+    assert kda.chunk_workspace_bytes(1, 64, 1, 128, 128, 7) == 0
     assert kda.varlen_workspace_bytes(0, 10, 1, 128, 128) == 0
 
 
