@@ -464,7 +464,18 @@ struct ChainLds {
     static constexpr int S = 0;
     static constexpr int X = S + MS::BYTES;
     static constexpr int U = X + MX::BYTES;
-    static constexpr int TOTAL = U + MX::BYTES;
+    static constexpr int O = U + MX::BYTES;     // fp32 output rows [64][kS + 4] on their way to HBM
+    static constexpr int V = O + 64 * (kS + 4) * 4;  // v rows [64][kS] (input type) on their way from HBM
+    static constexpr int TOTAL = V + 64 * kS * 4;
+};
+
+// Operands of one chunk for one wave of the chain kernel.
+template <int DK, bool F32>
+struct ChainOps {
+    static constexpr int KS = DK / 32, CBW = DK / 64;
+    Frag<F32> fQ[KS], fK[KS], fN[2], fP[2], fKB[CBW][2];
+    float4 gC[CBW];
+    uint4 vraw[F32 ? 2 : 1];  // this lane's 16-byte pieces of the wave's v rows
 };
 
 template <int DK, bool F32>
@@ -472,19 +483,23 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
                                                        float* __restrict__ o, float* s_final,
                                                        const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                        int64_t total, int64_t N, int H, int Dv,
-                                                       const char* __restrict__ ws) {
+                                                       const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChainLds<DK, F32>;
     using R = Rec<DK, F32>;
+    using Ops = ChainOps<DK, F32>;
     constexpr int KS = DK / 32;
     constexpr int CBW = DK / 64;  // 16-channel blocks of S per wave
+    constexpr int VPL = 16 / (int)sizeof(In);  // v values per 16-byte lane load
     const In* __restrict__ v = static_cast<const In*>(vv);
 
     __shared__ __align__(16) char smem[L::TOTAL];
     char* pS = smem + L::S;
     char* pX = smem + L::X;
     char* pU = smem + L::U;
+    float* sO = reinterpret_cast<float*>(smem + L::O);
+    In* sV = reinterpret_cast<In*>(smem + L::V);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int NS = Dv / kS;
@@ -498,6 +513,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     const int h = (int)(pr % H);
     const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
     const int64_t start = sr.start, end = sr.end;
+    const int64_t nch = (end - start + kC - 1) / kC;
     const int col0 = sl * kS;
     const int nk = steps_of(w);
 
@@ -517,74 +533,85 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
         }
     }
 
+    // global row traffic of this wave (rows 16w..16w+15 of a chunk): v and o move as whole
+    // row slices of the workgroup's 32 columns, one 16-byte piece per lane and load
     const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
-    const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + m;
-    float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + m;
+    constexpr int VLPR = kS / VPL;        // lanes per v row slice (bf16: 4, fp32: 8)
+    constexpr int VROWS = 64 / VLPR;      // v rows per load (bf16: 16, fp32: 8)
+    constexpr int VLOADS = 16 / VROWS;    // loads per lane (bf16: 1, fp32: 2)
+    const int vrow = 16 * w + lane / VLPR, vpiece = lane % VLPR;
+    const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * VPL;
+    float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + (lane & 7) * 4;
+
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
     };
-
-    // operands of one chunk, loaded in three groups during the previous chunk
-    Fr fQ[KS], fK[KS], fN[2], fP[2], fKB[CBW][2];
-    In pv[2][4];
-    float4 gC[CBW];
-    auto load_qk = [&](const char* rec) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
-            fK[s] = gfrag_load_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane);
-        }
+    // loads of one chunk's operands, in the three groups they are consumed in
+    auto load_qk = [&](Ops& d, const char* rec, int s) {
+        d.fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
+        d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane);
     };
-    auto load_nv = [&](const char* rec, int64_t t0, int nt) {
+    auto load_nv = [&](Ops& d, const char* rec, int64_t t0, int nt) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)  // rows of waves 0, 1 stop at token 31: their second step repeats the first
-            fN[kb] = gfrag_load<F32>(rec + R::NM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
-        const int64_t cv = t0 * (int64_t)rs_v;
+            d.fN[kb] = gfrag_load<F32>(rec + R::NM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t rvo = (uint32_t)min(16 * w + 4 * cg + jj, nt - 1) * rs_v;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) pv[nb][jj] = v_l[cv + rvo + 16 * nb];
+        for (int i = 0; i < VLOADS; ++i) {
+            const uint32_t rvo = (uint32_t)min(vrow + i * VROWS, nt - 1) * rs_v;
+            d.vraw[i] = *reinterpret_cast<const uint4*>(v_l + t0 * (int64_t)rs_v + rvo);
         }
     };
-    auto load_pkb = [&](const char* rec) {
+    auto load_pkb = [&](Ops& d, const char* rec, int ci) {
+        const int cb = w * CBW + ci;
+        if (ci == 0) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
-#pragma unroll
-        for (int ci = 0; ci < CBW; ++ci) {
-            const int cb = w * CBW + ci;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) fKB[ci][kb] = gfrag_load<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane);
-            gC[ci] = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cb + 4 * cg) * 4);
+            for (int kb = 0; kb < 2; ++kb)
+                d.fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
         }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) d.fKB[ci][kb] = gfrag_load<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane);
+        d.gC[ci] = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cb + 4 * cg) * 4);
+    };
+    auto load_all = [&](Ops& d, int64_t jc) {
+        const char* rec = record(jc);
+        const int64_t t0 = start + jc * kC;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) load_qk(d, rec, s);
+        load_nv(d, rec, t0, (int)min<int64_t>(kC, end - t0));
+#pragma unroll
+        for (int ci = 0; ci < CBW; ++ci) load_pkb(d, rec, ci);
     };
 
+    // o rows of a finished chunk: D-layout registers -> LDS -> whole row slices
     f32x4_t oPrev[2];
-    auto store_o = [&](int64_t tc, int ntc) {
+    auto stage_o = [&]() {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rr = 16 * w + 4 * cg + jj;
-                if (rr < ntc) o_l[tc * (int64_t)rs_v + (uint32_t)rr * rs_v + 16 * nb] = oPrev[nb][jj];
-            }
+            for (int jj = 0; jj < 4; ++jj) sO[(16 * w + 4 * cg + jj) * (kS + 4) + 16 * nb + m] = oPrev[nb][jj];
+    };
+    auto store_o = [&](int64_t tc, int ntc) {  // this wave's 16 rows; staged by this wave only
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int rr = 16 * w + 8 * half + (lane >> 3);
+            const float4 x = *reinterpret_cast<const float4*>(&sO[rr * (kS + 4) + (lane & 7) * 4]);
+            if (rr < ntc) *reinterpret_cast<float4*>(o_l + (tc + rr) * (int64_t)rs_v) = x;
+        }
     };
 
-    if (start < end) {
-        const char* rec = record(0);
-        load_qk(rec);
-        load_nv(rec, start, (int)min<int64_t>(kC, end - start));
-        load_pkb(rec);
-    }
-    lds_barrier();
+    // one chunk with operands `cur`, loading the next chunk's operands into `nxt` on the way
+    auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
+        const int64_t t0 = start + jc * kC;
+        const int nt = (int)min<int64_t>(kC, end - t0);
+        const int64_t jn = jc + 1 < nch ? jc + 1 : jc;  // the current chunk again after the last one
+        const int64_t t0n = start + jn * kC;
+        const int ntn = (int)min<int64_t>(kC, end - t0n);
+        const char* recn = record(jn);
 
-    int64_t jc = 0;
-    for (int64_t t0 = start; t0 < end; t0 += kC, ++jc) {
-        const bool more = t0 + kC < end;
-        const int64_t t0n = more ? t0 + kC : t0;
-        const int ntn = more ? (int)min<int64_t>(kC, end - t0 - kC) : (int)min<int64_t>(kC, end - t0);
-        const char* recn = record(more ? jc + 1 : jc);  // the current chunk again after the last one
+        // v rows of this chunk (loaded during the previous chunk) into LDS, for the D layout
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i)
+            *reinterpret_cast<uint4*>(&sV[(vrow + i * VROWS) * kS + vpiece * VPL]) = cur.vraw[i];
 
         // ---- chain 1:  X = V - Kt S (one pass), O1 = Qt S (full)
         f32x4_t accO[2], accX[2];
@@ -595,20 +622,21 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 const Fr sf = lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg);
-                accX[nb] = mma_fast(accX[nb], fK[s], sf);
-                accO[nb] = mma_full(accO[nb], fQ[s], sf);
+                accX[nb] = mma_fast(accX[nb], cur.fK[s], sf);
+                accO[nb] = mma_full(accO[nb], cur.fQ[s], sf);
             }
+            load_qk(nxt, recn, s);
         }
-        load_qk(recn);
-        if (t0 > start) store_o(t0 - kC, kC);
+        if (jc > 0) store_o(t0 - kC, kC);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             f32x4_t xv;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
+                const In raw = sV[(16 * w + 4 * cg + jj) * kS + 16 * nb + m];
                 float vj;
-                if constexpr (F32) vj = pv[nb][jj];
-                else vj = bf16_bits_to_float(pv[nb][jj]);
+                if constexpr (F32) vj = raw;
+                else vj = bf16_bits_to_float(raw);
                 xv[jj] = vj - accX[nb][jj];
             }
             lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
@@ -624,10 +652,10 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
                     const Fr xf = lds_frag<F32, kS, kC>(pX, 16 * nb + m, 32 * kb + 8 * cg);
-                    accU[nb] = mma_full(accU[nb], fN[kb], xf);
+                    accU[nb] = mma_full(accU[nb], cur.fN[kb], xf);
                 }
             }
-            load_nv(recn, t0n, ntn);
+            load_nv(nxt, recn, t0n, ntn);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
         }
@@ -644,11 +672,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb >= nk) continue;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], fP[kb], uf[nb][kb]);
+                for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
             }
 #pragma unroll
             for (int ci = 0; ci < CBW; ++ci) {
-                const float gcv[4] = {gC[ci].x, gC[ci].y, gC[ci].z, gC[ci].w};
+                const float gcv[4] = {cur.gC[ci].x, cur.gC[ci].y, cur.gC[ci].z, cur.gC[ci].w};
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -656,9 +684,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], fKB[ci][kb], uf[nb][kb]);
+                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], cur.fKB[ci][kb], uf[nb][kb]);
+                load_pkb(nxt, recn, ci);
             }
-            load_pkb(recn);
 #pragma unroll
             for (int ci = 0; ci < CBW; ++ci) {
                 const int cb = w * CBW + ci;
@@ -667,11 +695,20 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
+            stage_o();
         }
         lds_barrier();  // (3)
+    };
+
+    Ops opsA, opsB;
+    if (nch > 0) load_all(opsA, 0);
+    lds_barrier();
+    for (int64_t jc = 0; jc < nch; jc += 2) {
+        step(opsA, opsB, jc);
+        if (jc + 1 < nch) step(opsB, opsA, jc + 1);
     }
-    if (start < end) {
-        const int64_t t_last = start + ((end - start - 1) / kC) * kC;
+    if (nch > 0) {
+        const int64_t t_last = start + (nch - 1) * kC;
         store_o(t_last, (int)(end - t_last));
     }
     if (s_final) {
