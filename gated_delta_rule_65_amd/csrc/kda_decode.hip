@@ -40,23 +40,34 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
     const int tid = threadIdx.x, c4 = tid % C4, rg = tid / C4;
     const int64_t bh = blockIdx.x;
 
-    auto ld = [](const In* p, int64_t i) -> float {
-        if constexpr (F32) return p[i];
-        else return bf16_bits_to_float(p[i]);
-    };
-    if (tid < DK) {
-        sk[tid] = ld(k, bh * DK + tid);
-        sq[tid] = ld(q, bh * DK + tid);
-        sa[tid] = __expf(fminf(fmaxf(g[bh * DK + tid], -5.f), 0.f));
-    }
-    __syncthreads();
-
+    // Load order: the token vectors (k, q, g, v, beta; small), then the whole state slice; memory
+    // returns in order, so the vectors are waited for without waiting for the state.
+    // (every thread loads, at wrapped indices, so that no branch separates these loads from the
+    // state loads; only threads tid < DK / tid < C4 use them)
+    const int ti = tid % DK, tv = tid % C4;
+    const In kr = k[bh * DK + ti], qr = q[bh * DK + ti];
+    const float gr = g[bh * DK + ti], b = beta[bh];
+    In vr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vr[j] = v[bh * DV + 4 * tv + j];
+    __builtin_amdgcn_sched_barrier(0);  // keep the vector loads ahead of the state loads
     const f32x4_t* S = reinterpret_cast<const f32x4_t*>(s_in + bh * (int64_t)DK * DV);
     f32x4_t* So = reinterpret_cast<f32x4_t*>(s_out + bh * (int64_t)DK * DV);
     f32x4_t st[RPT];
-    float4 wp = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int mm = 0; mm < RPT; ++mm) st[mm] = __builtin_nontemporal_load(&S[(rg + RG * mm) * C4 + c4]);
+    auto tof = [](In x) -> float {
+        if constexpr (F32) return x;
+        else return bf16_bits_to_float(x);
+    };
+    // every thread writes (threads beyond DK repeat the values of thread tid % DK): no branch for the
+    // compiler to sink the vector loads into
+    sk[ti] = tof(kr);
+    sq[ti] = tof(qr);
+    sa[ti] = __expf(fminf(fmaxf(gr, -5.f), 0.f));
+    __syncthreads();
+
+    float4 wp = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int mm = 0; mm < RPT; ++mm) {
         const int i = rg + RG * mm;
@@ -75,12 +86,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
             const float4 x = sred[r][tid];
             acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
         }
-        const float b = beta[bh];
-        const int64_t vb = bh * DV + 4 * tid;
-        su[4 * tid + 0] = b * (ld(v, vb + 0) - acc.x);
-        su[4 * tid + 1] = b * (ld(v, vb + 1) - acc.y);
-        su[4 * tid + 2] = b * (ld(v, vb + 2) - acc.z);
-        su[4 * tid + 3] = b * (ld(v, vb + 3) - acc.w);
+        su[4 * tid + 0] = b * (tof(vr[0]) - acc.x);
+        su[4 * tid + 1] = b * (tof(vr[1]) - acc.y);
+        su[4 * tid + 2] = b * (tof(vr[2]) - acc.z);
+        su[4 * tid + 3] = b * (tof(vr[3]) - acc.w);
     }
     __syncthreads();
     const float4 u = make_float4(su[4 * c4], su[4 * c4 + 1], su[4 * c4 + 2], su[4 * c4 + 3]);
