@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
-    ap.add_argument("--only", choices=["chunk", "decode", "varlen"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m"], default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
@@ -132,6 +132,9 @@ def main():
         return
     if args.only == "varlen":
         print(json.dumps({"varlen": measure_varlen(args, torch, kda, kda_inputs, device_inputs)}))
+        return
+    if args.only == "prefill_1m":
+        print(json.dumps({"prefill_1m": measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)}))
         return
 
     # ------------------------------------------------ chunked prefill, B=4 H=16 T=8192 d=128 bf16
@@ -192,6 +195,7 @@ def main():
     if args.only is None and not args.no_extras:
         line["decode"] = measure_decode(args, torch, kda, kda_inputs, to_dev)
         line["varlen"] = measure_varlen(args, torch, kda, kda_inputs, device_inputs)
+        line["prefill_1m"] = measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)
 
     if args.only is None and not args.no_cpu_baseline:
         import oracle
@@ -261,6 +265,26 @@ def measure_varlen(args, torch, kda, kda_inputs, device_inputs):
     return {"workload": name, "tokens": vspec.total, "longest": max(vspec.lengths), "kernel_ms": vk_ms,
             "kernel_ms_min": vk_min, "tokens_per_s": vspec.total / (vk_ms * 1e-3),
             "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s", "alg_bytes_per_launch": vbytes}
+
+
+def measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs):
+    """Million-token prefill, B=1, H=8, d=128, bf16 (long-memory gates): tokens/s of one call."""
+    name = "prefill_b1_h8_t1m_d128_bf16"
+    spec = kda_inputs.workload(name)
+    inp = kda_inputs.generate(spec)
+    d = device_inputs(inp, batched=True)
+    B, T, H, Dk, Dv = spec.n_seq, spec.lengths[0], spec.H, spec.Dk, spec.Dv
+    ws = torch.empty(kda.chunk_workspace_bytes(B, T, H, Dk, Dv), dtype=torch.uint8, device="cuda")
+
+    def pstep():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws)
+
+    _, k_ms, k_min = time_launches(pstep, 3, 1, torch)
+    alg = chunk_alg_bytes(B * T * H, B * H, Dk, Dv, 2, with_s0=False)
+    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+            "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
+            "workspace_bytes": ws.numel()}
 
 
 if __name__ == "__main__":

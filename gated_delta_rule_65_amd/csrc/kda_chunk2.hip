@@ -478,11 +478,27 @@ struct ChainOps {
     uint4 vraw[F32 ? 2 : 1];  // this lane's 16-byte pieces of the wave's v rows
 };
 
+// Long sequences with few heads split the chunk range into P segments of L chunks (the one-GPU
+// form of the segment scan the worldcybernews page's third paragraph describes across GPUs):
+//   mode 1 (segment maps), items (n, h, p < P-1), (Dv + Dk)/32 column slices: the segment run
+//     from a zero state gives S0_p (its Dv value columns); run on the identity with V = 0 it gives
+//     the segment's transition Phi_p (Dk more columns).  Both go to sx [item][Dk][Dv + Dk]; no o.
+//   mode 2 (outputs), items (n, h, p): segment p from its true initial state (s0 for p = 0,
+//     else sfold [n][h][p][Dk][Dv] from the fold kernel), o written, s_final from p = P - 1.
+//   mode 0: whole sequences (items (n, h)), s0 -> s_final.
+struct ChainMode {
+    int mode;      // 0, 1 or 2
+    int P;         // segments per sequence (modes 1, 2)
+    int64_t L;     // chunks per segment (modes 1, 2)
+    float* sx;     // mode 1 output
+    const float* sfold;  // mode 2 input
+};
+
 template <int DK, bool F32>
 __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                        float* __restrict__ o, float* s_final,
                                                        const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
-                                                       int64_t total, int64_t N, int H, int Dv,
+                                                       int64_t total, int64_t N, int H, int Dv, ChainMode cm,
                                                        const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
@@ -502,20 +518,42 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     In* sV = reinterpret_cast<In*>(smem + L::V);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
-    const int NS = Dv / kS;
-    const int64_t pairs = N * (int64_t)H;
+    const int NV = Dv / kS;                                // value-column slices
+    const int NS = cm.mode == 1 ? NV + DK / kS : NV;       // + identity-column slices in mode 1
+    const int segs = cm.mode == 1 ? cm.P - 1 : (cm.mode == 2 ? cm.P : 1);
+    const int64_t items = N * (int64_t)H * segs;
     const int64_t bid = blockIdx.x;
     const int64_t loc = bid >> 3;
     const int sl = (int)(loc % NS);
-    const int64_t pr = (loc / NS) * 8 + (bid & 7);  // slices of one head on one XCD
-    if (pr >= pairs) return;
-    const int64_t n = pr / H;
-    const int h = (int)(pr % H);
+    const int64_t pr = (loc / NS) * 8 + (bid & 7);  // slices of one item on one XCD
+    if (pr >= items) return;
+    const int64_t n = pr / ((int64_t)H * segs);
+    const int h = (int)((pr / segs) % H);
+    const int p = (int)(pr % segs);
     const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
     const int64_t start = sr.start, end = sr.end;
-    const int64_t nch = (end - start + kC - 1) / kC;
-    const int col0 = sl * kS;
+    const int64_t nall = (end - start + kC - 1) / kC;
+    const int64_t jbeg = cm.mode ? min<int64_t>(p * cm.L, nall) : 0;
+    const int64_t jend = cm.mode ? min<int64_t>((p + 1) * cm.L, nall) : nall;
+    const bool ident = sl >= NV;                           // identity columns (mode 1)
+    const int col0 = ident ? 0 : sl * kS;                  // value columns read (v) by this slice
+    const int colx = sl * kS;                              // column of this slice in sx rows (mode 1)
+    const float vscale = ident ? 0.f : 1.f;                // V = 0 for the identity columns
+    const bool write_o = cm.mode != 1;
     const int nk = steps_of(w);
+
+    // state of this slice at the segment start / its destination
+    auto state_in = [&](int c, int col) -> float {
+        if (cm.mode == 1) return ident ? (c == colx - Dv + col - col0 ? 1.f : 0.f) : 0.f;
+        if (cm.mode == 2 && p > 0)
+            return cm.sfold[((((n * H + h) * (int64_t)cm.P + p) * DK + c) * Dv) + col];
+        return s0 ? s0[((n * H + h) * DK + c) * (int64_t)Dv + col] : 0.f;
+    };
+    float* const sdst = cm.mode == 1 ? cm.sx + (pr * DK) * (int64_t)(Dv + DK)
+                                     : ((cm.mode == 0 || p == cm.P - 1) && s_final
+                                            ? s_final + (n * H + h) * (int64_t)DK * Dv : nullptr);
+    const int ld_dst = cm.mode == 1 ? Dv + DK : Dv;
+    const int col_dst = cm.mode == 1 ? colx : col0;
 
     // initial state (wave w: channel blocks w*CBW.., both 16-column halves)
     f32x4_t accS[CBW][2];
@@ -527,7 +565,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int c = 16 * cb + 4 * cg + jj;
-                accS[ci][nb][jj] = s0 ? s0[((n * H + h) * DK + c) * (int64_t)Dv + col0 + 16 * nb + m] : 0.f;
+                accS[ci][nb][jj] = state_in(c, col0 + 16 * nb + m);
             }
             lds_store4<F32, kS, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
         }
@@ -603,7 +641,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
         const int64_t t0 = start + jc * kC;
         const int nt = (int)min<int64_t>(kC, end - t0);
-        const int64_t jn = jc + 1 < nch ? jc + 1 : jc;  // the current chunk again after the last one
+        const int64_t jn = jc + 1 < jend ? jc + 1 : jc;  // the current chunk again after the last one
         const int64_t t0n = start + jn * kC;
         const int ntn = (int)min<int64_t>(kC, end - t0n);
         const char* recn = record(jn);
@@ -627,7 +665,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             }
             load_qk(nxt, recn, s);
         }
-        if (jc > 0) store_o(t0 - kC, kC);
+        if (write_o && jc > jbeg) store_o(t0 - kC, kC);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             f32x4_t xv;
@@ -637,7 +675,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
                 float vj;
                 if constexpr (F32) vj = raw;
                 else vj = bf16_bits_to_float(raw);
-                xv[jj] = vj - accX[nb][jj];
+                xv[jj] = vscale * vj - accX[nb][jj];
             }
             lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
         }
@@ -701,17 +739,17 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     };
 
     Ops opsA, opsB;
-    if (nch > 0) load_all(opsA, 0);
+    if (jbeg < jend) load_all(opsA, jbeg);
     lds_barrier();
-    for (int64_t jc = 0; jc < nch; jc += 2) {
+    for (int64_t jc = jbeg; jc < jend; jc += 2) {
         step(opsA, opsB, jc);
-        if (jc + 1 < nch) step(opsB, opsA, jc + 1);
+        if (jc + 1 < jend) step(opsB, opsA, jc + 1);
     }
-    if (nch > 0) {
-        const int64_t t_last = start + (nch - 1) * kC;
-        store_o(t_last, (int)(end - t_last));
+    if (write_o && jbeg < jend) {
+        const int64_t t_last = start + (jend - 1) * kC;
+        store_o(t_last, (int)min<int64_t>(kC, end - t_last));
     }
-    if (s_final) {
+    if (sdst) {
 #pragma unroll
         for (int ci = 0; ci < CBW; ++ci) {
             const int cb = w * CBW + ci;
@@ -720,9 +758,58 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int c = 16 * cb + 4 * cg + jj;
-                    s_final[((n * H + h) * DK + c) * (int64_t)Dv + col0 + 16 * nb + m] = accS[ci][nb][jj];
+                    sdst[c * (int64_t)ld_dst + col_dst + 16 * nb + m] = accS[ci][nb][jj];
                 }
         }
+    }
+}
+
+// ============================================================================ segment fold
+
+// Initial states of the segments of a split sequence, one workgroup per (sequence, head,
+// 32-column slice): S_in(0) = s0 (or 0), S_in(p+1) = Phi_p S_in(p) + S0_p for p < P - 1, written
+// to sfold [n][h][p][Dk][Dv] (p >= 1).  fp32 throughout; the running state stays in LDS.
+template <int DK>
+__global__ __launch_bounds__(256) void fold_kernel(const float* s0, const float* __restrict__ sx,
+                                                   float* __restrict__ sfold, int H, int Dv, int P) {
+    __shared__ float sS[DK][kS + 1];
+    const int tid = threadIdx.x, j = tid % kS, r0 = tid / kS;  // column j, rows r0 + 8i
+    constexpr int RPT = DK / 8;
+    const int NV = Dv / kS;
+    const int64_t item = blockIdx.x / NV;  // n * H + h
+    const int col = (int)(blockIdx.x % NV) * kS + j;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = r0 + 8 * i;
+        sS[c][j] = s0 ? s0[(item * DK + c) * (int64_t)Dv + col] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p + 1 < P; ++p) {
+        const float* X = sx + ((item * (P - 1) + p) * DK) * (int64_t)(Dv + DK);  // [Dk][Dv + Dk]
+        float acc[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int c = r0 + 8 * i;
+            const float* phi = X + c * (int64_t)(Dv + DK) + Dv;  // row c of Phi_p
+            float a = X[c * (int64_t)(Dv + DK) + col];           // S0_p
+            for (int cc = 0; cc < DK; cc += 4) {
+                const float4 f = *reinterpret_cast<const float4*>(phi + cc);
+                a = fmaf(f.x, sS[cc][j], a);
+                a = fmaf(f.y, sS[cc + 1][j], a);
+                a = fmaf(f.z, sS[cc + 2][j], a);
+                a = fmaf(f.w, sS[cc + 3][j], a);
+            }
+            acc[i] = a;
+        }
+        __syncthreads();
+        float* dst = sfold + (((item * P + p + 1) * DK) * (int64_t)Dv);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int c = r0 + 8 * i;
+            sS[c][j] = acc[i];
+            dst[c * (int64_t)Dv + col] = acc[i];
+        }
+        __syncthreads();
     }
 }
 
@@ -738,7 +825,32 @@ int64_t chunk_record_bytes(int Dk, bool f32) {
     return f32 ? Rec<64, true>::BYTES : Rec<64, false>::BYTES;
 }
 
-int64_t chunk_workspace_bytes(const ChunkArgs& a) { return chunk_slots(a) * a.H * chunk_record_bytes(a.Dk, a.f32); }
+// Segments of the split-T path: equal-length sequences whose chain would occupy fewer than half
+// of 256 workgroup slots are cut into P segments so that the output pass has about 256
+// workgroups, each segment at least 64 chunks long.  (A fixed target keeps the workspace size a
+// function of the arguments alone.)
+int chunk_segments(const ChunkArgs& a) {
+    if (a.cu_seqlens) return 1;
+    constexpr int64_t kTarget = 256;
+    const int64_t slices = a.N * a.H * (a.Dv / kS);
+    if (slices * 2 > kTarget) return 1;
+    int64_t P = kTarget / slices;
+    const int64_t nch = (a.T_fixed + kC - 1) / kC;
+    if (P > nch / 64) P = nch / 64;
+    return P >= 2 ? (int)P : 1;
+}
+
+static int64_t records_bytes(const ChunkArgs& a) { return chunk_slots(a) * a.H * chunk_record_bytes(a.Dk, a.f32); }
+
+// split-T state areas: segment maps [N][H][P-1][Dk][Dv + Dk], segment initial states [N][H][P][Dk][Dv]
+static int64_t segment_bytes(const ChunkArgs& a, int P) {
+    if (P < 2) return 0;
+    return a.N * a.H * (int64_t)a.Dk * 4 * ((P - 1) * (int64_t)(a.Dv + a.Dk) + P * (int64_t)a.Dv);
+}
+
+int64_t chunk_workspace_bytes(const ChunkArgs& a) { return records_bytes(a) + segment_bytes(a, chunk_segments(a)); }
+
+static int64_t chain_grid(int64_t items, int slices) { return ((items + 7) / 8) * 8 * slices; }
 
 template <int DK, bool F32>
 static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
@@ -748,9 +860,32 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
                            a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, static_cast<char*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t grid = chunk_grid_size(a.N, a.H, a.Dv);
-    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)grid), dim3(256), 0, st, a.v, a.s0, a.o, a.s_final,
-                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, static_cast<const char*>(ws));
+    const int P = chunk_segments(a);
+    const int NV = a.Dv / kS;
+    if (P < 2) {
+        const ChainMode cm{0, 1, 0, nullptr, nullptr};
+        hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(256), 0, st,
+                           a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, cm,
+                           static_cast<const char*>(ws));
+        return hipGetLastError();
+    }
+    // split-T: segment maps, fold, outputs
+    const int64_t nch = (a.T_fixed + kC - 1) / kC;
+    const int64_t L = (nch + P - 1) / P;
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(ws) + records_bytes(a));
+    float* sfold = sx + a.N * a.H * (int64_t)(P - 1) * a.Dk * (a.Dv + a.Dk);
+    const ChainMode c1{1, P, L, sx, nullptr};
+    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H * (P - 1), NV + DK / kS)),
+                       dim3(256), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H,
+                       a.Dv, c1, static_cast<const char*>(ws));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((fold_kernel<DK>), dim3((unsigned)(a.N * a.H * NV)), dim3(256), 0, st, a.s0, sx, sfold, a.H,
+                       a.Dv, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const ChainMode c2{2, P, L, nullptr, sfold};
+    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(256), 0, st,
+                       a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, c2,
+                       static_cast<const char*>(ws));
     return hipGetLastError();
 }
 

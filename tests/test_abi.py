@@ -99,11 +99,33 @@ def test_record_sizes():
     assert record_bytes(64, 1) == 65792 and record_bytes(64, 0) == 73984
 
 
+def segments(B, T, H, Dv):
+    """Split-T segments: equal-length batches whose chain fills under half of 256 workgroups are cut
+    so that the output pass has about 256 workgroups, segments of at least 64 chunks."""
+    slices = B * H * (Dv // 32)
+    if 2 * slices > 256:
+        return 1
+    P = min(256 // slices, (-(-T // 64)) // 64)
+    return P if P >= 2 else 1
+
+
+def segment_bytes(B, H, Dk, Dv, P):
+    return 0 if P < 2 else B * H * Dk * 4 * ((P - 1) * (Dv + Dk) + P * Dv)
+
+
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 64, 1, 128, 128), (4, 8192, 16, 128, 128), (2, 65, 3, 64, 128),
-                                         (3, 1, 2, 64, 64)])
+                                         (3, 1, 2, 64, 64), (1, 1 << 20, 8, 128, 128), (1, 16421, 2, 128, 128),
+                                         (1, 8192, 1, 64, 64)])
 def test_chunk_workspace_size(B, T, H, Dk, Dv, dtype):
-    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv, dtype) == B * (-(-T // 64)) * H * record_bytes(Dk, dtype)
+    P = segments(B, T, H, Dv)
+    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv, dtype) == (B * (-(-T // 64)) * H * record_bytes(Dk, dtype)
+                                                                 + segment_bytes(B, H, Dk, Dv, P))
+
+
+def test_segment_counts():
+    assert segments(1, 1 << 20, 8, 128) == 8 and segments(4, 8192, 16, 128) == 1
+    assert segments(1, 16421, 2, 128) == 4 and segments(1, 8192, 1, 64) == 2
 
 
 @pytest.mark.parametrize("dtype", [0, 1])

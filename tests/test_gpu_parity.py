@@ -198,6 +198,21 @@ def test_varlen_equals_batched(fused):
     assert np.array_equal(ob, ov) and np.array_equal(sb, sv)
 
 
+@pytest.mark.parametrize("T,H,Dk,Dv,dtype,with_s0", [
+    (8192, 1, 128, 128, "bf16", True),     # 2 segments
+    (16421, 2, 128, 128, "bf16", True),    # 4 uneven segments, ragged last chunk
+    (12800, 1, 128, 64, "bf16", False),    # 3 segments, Dv = 64
+    (8192, 1, 64, 64, "f32", True),        # fp32, Dk = 64
+])
+def test_split_t_segments(T, H, Dk, Dv, dtype, with_s0):
+    """Few heads, long sequence: the chunk range is cut into segments (zero-start runs and
+    transitions, fold, output pass); results match the token recurrence."""
+    spec = kda_inputs.Spec([T], H, Dk, Dv, dtype, "softplus_bounds", 0.05, s0_std=0.02 if with_s0 else None,
+                           seed=50 + T % 97, name=f"split-T{T}-H{H}-{Dk}x{Dv}-{dtype}")
+    inp = kda_inputs.generate(spec)
+    check(inp, *run_chunk(inp))
+
+
 def test_two_pass_with_caller_workspace_reused_and_dirty():
     """The workspace needs no initial contents and one buffer serves calls of different sizes."""
     big = kda_inputs.generate(kda_inputs.Spec([300] * 2, 3, 128, 128, "bf16", "softplus_bounds", 0.05,
