@@ -494,7 +494,8 @@ struct ChainMode {
     const float* sfold;  // mode 2 input
 };
 
-template <int DK, bool F32>
+// SO (state only, mode 1): the output products, their operands and the o traffic are compiled out.
+template <int DK, bool F32, bool SO>
 __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                        float* __restrict__ o, float* s_final,
                                                        const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
@@ -539,7 +540,6 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     const int col0 = ident ? 0 : sl * kS;                  // value columns read (v) by this slice
     const int colx = sl * kS;                              // column of this slice in sx rows (mode 1)
     const float vscale = ident ? 0.f : 1.f;                // V = 0 for the identity columns
-    const bool write_o = cm.mode != 1;
     const int nk = steps_of(w);
 
     // state of this slice at the segment start / its destination
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     };
     // loads of one chunk's operands, in the three groups they are consumed in
     auto load_qk = [&](Ops& d, const char* rec, int s) {
-        d.fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
+        if constexpr (!SO) d.fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
         d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane);
     };
     auto load_nv = [&](Ops& d, const char* rec, int64_t t0, int nt) {
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     };
     auto load_pkb = [&](Ops& d, const char* rec, int ci) {
         const int cb = w * CBW + ci;
-        if (ci == 0) {
+        if (!SO && ci == 0) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
                 d.fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
@@ -661,11 +661,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             for (int nb = 0; nb < 2; ++nb) {
                 const Fr sf = lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg);
                 accX[nb] = mma_fast(accX[nb], cur.fK[s], sf);
-                accO[nb] = mma_full(accO[nb], cur.fQ[s], sf);
+                if constexpr (!SO) accO[nb] = mma_full(accO[nb], cur.fQ[s], sf);
             }
             load_qk(nxt, recn, s);
         }
-        if (write_o && jc > jbeg) store_o(t0 - kC, kC);
+        if (!SO && jc > jbeg) store_o(t0 - kC, kC);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             f32x4_t xv;
@@ -708,7 +708,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
                 for (int kb = 0; kb < 2; ++kb) uf[nb][kb] = lds_frag<F32, kS, kC>(pU, 16 * nb + m, 32 * kb + 8 * cg);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                if (kb >= nk) continue;
+                if (SO || kb >= nk) continue;
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
             }
@@ -731,9 +731,11 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
             }
+            if constexpr (!SO) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
-            stage_o();
+                for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
+                stage_o();
+            }
         }
         lds_barrier();  // (3)
     };
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
         step(opsA, opsB, jc);
         if (jc + 1 < jend) step(opsB, opsA, jc + 1);
     }
-    if (write_o && jbeg < jend) {
+    if (!SO && jbeg < jend) {
         const int64_t t_last = start + (jend - 1) * kC;
         store_o(t_last, (int)min<int64_t>(kC, end - t_last));
     }
@@ -864,7 +866,7 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int NV = a.Dv / kS;
     if (P < 2) {
         const ChainMode cm{0, 1, 0, nullptr, nullptr};
-        hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(256), 0, st,
+        hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(256), 0, st,
                            a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, cm,
                            static_cast<const char*>(ws));
         return hipGetLastError();
@@ -875,7 +877,7 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     float* sx = reinterpret_cast<float*>(static_cast<char*>(ws) + records_bytes(a));
     float* sfold = sx + a.N * a.H * (int64_t)(P - 1) * a.Dk * (a.Dv + a.Dk);
     const ChainMode c1{1, P, L, sx, nullptr};
-    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H * (P - 1), NV + DK / kS)),
+    hipLaunchKernelGGL((chain_kernel<DK, F32, true>), dim3((unsigned)chain_grid(a.N * a.H * (P - 1), NV + DK / kS)),
                        dim3(256), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H,
                        a.Dv, c1, static_cast<const char*>(ws));
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -883,7 +885,7 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
                        a.Dv, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const ChainMode c2{2, P, L, nullptr, sfold};
-    hipLaunchKernelGGL((chain_kernel<DK, F32>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(256), 0, st,
+    hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(256), 0, st,
                        a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, c2,
                        static_cast<const char*>(ws));
     return hipGetLastError();
