@@ -31,9 +31,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def chunk_alg_bytes(n_head_tokens, n_heads, Dk, Dv, in_bytes, with_s0):
-    # q, k, v in the input type; g fp32 (Dk); beta fp32; o fp32 (Dv); final state fp32 (+ initial state if given)
-    per_tok = (2 * Dk + Dv) * in_bytes + 4 * Dk + 4 + 4 * Dv
+def chunk_alg_bytes(n_head_tokens, n_heads, Dk, Dv, in_bytes, with_s0, gate_bytes=4):
+    # q, k, v in the input type; g (Dk) and beta in the gate type (fp32 unless given); o fp32 (Dv);
+    # final state fp32 (+ initial state if given)
+    per_tok = (2 * Dk + Dv) * in_bytes + gate_bytes * (Dk + 1) + 4 * Dv
     return n_head_tokens * per_tok + n_heads * Dk * Dv * 4 * (2 if with_s0 else 1)
 
 
@@ -96,7 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
-    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m", "raw_gates"], default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
@@ -135,6 +136,9 @@ def main():
         return
     if args.only == "prefill_1m":
         print(json.dumps({"prefill_1m": measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)}))
+        return
+    if args.only == "raw_gates":
+        print(json.dumps({"raw_gates": measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)}))
         return
 
     # ------------------------------------------------ chunked prefill, B=4 H=16 T=8192 d=128 bf16
@@ -180,7 +184,7 @@ def main():
                    "qkv": "bf16", "gates": "fp32", "state": "fp32", "output": "fp32", "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prep_kernel<128,false> + chain_kernel<128,false>", "kernel_ms": k_ms,
+                     "kernel": "prep_kernel<128,false,false> + chain_kernel<128,false,false>", "kernel_ms": k_ms,
                      "kernel_ms_min": k_min, "alg_bytes_per_launch": alg_bytes,
                      "workspace_bytes": ws.numel()},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -196,6 +200,7 @@ def main():
         line["decode"] = measure_decode(args, torch, kda, kda_inputs, to_dev)
         line["varlen"] = measure_varlen(args, torch, kda, kda_inputs, device_inputs)
         line["prefill_1m"] = measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)
+        line["raw_gates"] = measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)
 
     if args.only is None and not args.no_cpu_baseline:
         import oracle
@@ -234,7 +239,7 @@ def measure_decode(args, torch, kda, kda_inputs, to_dev):
         a = flip[0]
         rc = kda.decode_step_raw(dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
                                  st[a].data_ptr(), st[1 - a].data_ptr(), o.data_ptr(), Bd, Hd, 128, 128,
-                                 kda.DTYPE[torch.bfloat16], torch.cuda.current_stream().cuda_stream)
+                                 kda.DTYPE[torch.bfloat16], None, torch.cuda.current_stream().cuda_stream)
         assert rc == 0
         flip[0] = 1 - a
 
@@ -285,6 +290,29 @@ def measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs):
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
             "workspace_bytes": ws.numel()}
+
+
+def measure_raw_gates(args, torch, kda, kda_inputs, device_inputs):
+    """The B=4 H=16 T=8192 batch fed raw: bf16 gate and beta logits, q and k not normalised; the
+    kernels apply -softplus, the clamp, the logistic function and the L2 norm while loading."""
+    name = "chunk_b4_h16_t8192_d128_bf16_raw_gates"
+    base = kda_inputs.workload("chunk_b4_h16_t8192_d128_bf16")
+    spec = kda_inputs.Spec(base.lengths, base.H, base.Dk, base.Dv, "bf16", "softplus", seed=base.seed,
+                           g_logit=True, beta_logit=True, qk_l2norm=True, gate_dtype="bf16", name=name)
+    inp = kda_inputs.generate(spec)
+    d = device_inputs(inp, batched=True)
+    B, T, H, Dk, Dv = spec.n_seq, spec.lengths[0], spec.H, spec.Dk, spec.Dv
+    ws = torch.empty(kda.chunk_workspace_bytes(B, T, H, Dk, Dv), dtype=torch.uint8, device="cuda")
+
+    def rstep():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws, g_logit=True,
+                      beta_logit=True, qk_l2norm=True)
+
+    _, k_ms, k_min = time_launches(rstep, max(10, args.steps // 2), args.warmup, torch)
+    alg = chunk_alg_bytes(B * T * H, B * H, Dk, Dv, 2, with_s0=False, gate_bytes=2)
+    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+            "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg}
 
 
 if __name__ == "__main__":

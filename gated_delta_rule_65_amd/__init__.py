@@ -10,6 +10,11 @@ Recurrence per head (worldcybernews page "Kimi K3 Open Model Surpasses Closed
 GPT and Anthropic Systems on Independent Benchmarks", second paragraph, read as
 the gated delta rule):  S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
 o_t = S_t^T q_t, a_t = exp(clamp(g_t, -5, 0)).
+
+Input prologue (every entry point): g and beta may be float32 or bfloat16;
+``g_logit=True`` reads g as gate logits x with log a = -softplus(x);
+``beta_logit=True`` reads beta as logits (b = sigmoid(beta)); ``qk_l2norm=True``
+scales q and k to unit length per token and head inside the kernels.
 """
 from __future__ import annotations
 
@@ -21,7 +26,7 @@ import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
            "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "chunk_workspace_bytes",
-           "varlen_workspace_bytes", "DTYPE"]
+           "varlen_workspace_bytes", "DTYPE", "Prologue", "prologue"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -29,6 +34,21 @@ _LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 DTYPE = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 STATUS = {0: "OK", 1: "NULL_ARG", 2: "BAD_SHAPE", 3: "BAD_DTYPE", 4: "MISALIGNED", 5: "HIP_ERROR"}
+
+
+class Prologue(ctypes.Structure):
+    """kda_prologue of the C ABI."""
+    _fields_ = [("g_dtype", ctypes.c_int), ("g_logit", ctypes.c_int), ("beta_dtype", ctypes.c_int),
+                ("beta_logit", ctypes.c_int), ("qk_l2norm", ctypes.c_int)]
+
+
+def prologue(g_dtype=torch.float32, g_logit=False, beta_dtype=torch.float32, beta_logit=False, qk_l2norm=False):
+    """A ctypes pointer to a kda_prologue, or None when every field has its default."""
+    codes = (_dtype_code(g_dtype), int(bool(g_logit)), _dtype_code(beta_dtype), int(bool(beta_logit)),
+             int(bool(qk_l2norm)))
+    if codes == (KDA_F32, 0, KDA_F32, 0, 0):
+        return None
+    return ctypes.pointer(Prologue(*codes))
 
 
 class KDAError(RuntimeError):
@@ -54,15 +74,16 @@ def load_library():
                           f"g.build()'` or `python gated_delta_rule_65_amd/_build.py`")
     L = ctypes.CDLL(_LIB_PATH)
     vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
-    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, vp, sz, vp]
+    pp = ctypes.POINTER(Prologue)
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, pp, vp, sz, vp]
     L.kda_chunk_fwd.restype = ci
-    L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, pp, vp, sz, vp]
     L.kda_varlen_fwd.restype = ci
     L.kda_chunk_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_chunk_workspace_bytes.restype = sz
     L.kda_varlen_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_varlen_workspace_bytes.restype = sz
-    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, vp]
+    L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, pp, vp]
     L.kda_decode_step.restype = ci
     L.kda_last_error.restype = ctypes.c_char_p
     L.kda_version.restype = ctypes.c_char_p
@@ -77,16 +98,16 @@ def _check(status: int):
 
 # ----------------------------------------------------------------- raw calls (ints in, status out)
 
-def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, workspace, workspace_bytes,
-                  stream) -> int:
-    return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, workspace,
-                                        workspace_bytes, stream)
+def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, prologue, workspace,
+                  workspace_bytes, stream) -> int:
+    return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, prologue,
+                                        workspace, workspace_bytes, stream)
 
 
-def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, workspace,
+def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, prologue, workspace,
                    workspace_bytes, stream) -> int:
     return load_library().kda_varlen_fwd(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype,
-                                         workspace, workspace_bytes, stream)
+                                         prologue, workspace, workspace_bytes, stream)
 
 
 def _dtype_code(dtype) -> int:
@@ -101,8 +122,8 @@ def varlen_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int, dtype=t
     return int(load_library().kda_varlen_workspace_bytes(N, total, H, Dk, Dv, _dtype_code(dtype)))
 
 
-def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream) -> int:
-    return load_library().kda_decode_step(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, stream)
+def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, prologue, stream) -> int:
+    return load_library().kda_decode_step(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, prologue, stream)
 
 
 # ----------------------------------------------------------------- torch front end
@@ -122,6 +143,15 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _gates(g, beta, g_shape, b_shape, g_logit, beta_logit, qk_l2norm):
+    """Check g and beta (float32 or bfloat16 each) and build the prologue for them."""
+    for t, name, shape in ((g, "g", g_shape), (beta, "beta", b_shape)):
+        if t.dtype not in DTYPE:
+            raise TypeError(f"{name} must be float32 or bfloat16 (got {t.dtype})")
+        _need(t, name, t.dtype, shape)
+    return prologue(g.dtype, g_logit, beta.dtype, beta_logit, qk_l2norm)
 
 
 def _stream(dev) -> int:
@@ -145,12 +175,15 @@ def _workspace(need: int, fused: bool, workspace: Optional[torch.Tensor], device
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               s0: Optional[torch.Tensor] = None, chunk: int = 64, output_final_state: bool = True,
-              fused: bool = False, workspace: Optional[torch.Tensor] = None
+              fused: bool = False, workspace: Optional[torch.Tensor] = None, g_logit: bool = False,
+              beta_logit: bool = False, qk_l2norm: bool = False
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill over equal-length sequences.
 
     q, k: [B, T, H, Dk]; v: [B, T, H, Dv] (bf16 or fp32, all the same);
-    g (log forget gate, fp32): [B, T, H, Dk]; beta (fp32): [B, T, H]; s0 (fp32): [B, H, Dk, Dv] or None.
+    g (log forget gate, or gate logits with ``g_logit``; fp32 or bf16): [B, T, H, Dk];
+    beta (fp32 or bf16; logits with ``beta_logit``): [B, T, H]; s0 (fp32): [B, H, Dk, Dv] or None.
+    ``qk_l2norm`` scales q and k to unit length per token and head inside the kernels.
     Returns o (fp32) [B, T, H, Dv] and the final state [B, H, Dk, Dv] (or None).
     By default the two-kernel path runs with a workspace (``workspace`` if given, else allocated);
     ``fused=True`` selects the single fused kernel, which needs none.
@@ -164,8 +197,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, Dk))
     _need(v, "v", q.dtype, (B, T, H, Dv))
-    _need(g, "g", torch.float32, (B, T, H, Dk))
-    _need(beta, "beta", torch.float32, (B, T, H))
+    pro = _gates(g, beta, (B, T, H, Dk), (B, T, H), g_logit, beta_logit, qk_l2norm)
     if s0 is not None:
         _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
     o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
@@ -173,19 +205,20 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     ws, ws_bytes = _workspace(chunk_workspace_bytes(B, T, H, Dk, Dv, q.dtype), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(chunk_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
-                             B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes, _stream(q.device)))
+                             B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], pro, _ptr(ws), ws_bytes, _stream(q.device)))
     return o, sf
 
 
 def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                cu_seqlens: torch.Tensor, s0: Optional[torch.Tensor] = None, chunk: int = 64,
-               output_final_state: bool = True, fused: bool = False, workspace: Optional[torch.Tensor] = None
+               output_final_state: bool = True, fused: bool = False, workspace: Optional[torch.Tensor] = None,
+               g_logit: bool = False, beta_logit: bool = False, qk_l2norm: bool = False
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Packed variable-length prefill.
 
     q, k, g: [total, H, Dk]; v: [total, H, Dv]; beta: [total, H]; cu_seqlens: int32 [N+1] on the GPU;
     s0: [N, H, Dk, Dv] or None.  Returns o [total, H, Dv] (fp32) and the final states [N, H, Dk, Dv].
-    ``fused`` and ``workspace`` as for :func:`chunk_fwd`.
+    ``fused``, ``workspace`` and the prologue options as for :func:`chunk_fwd`.
     """
     if q.dim() != 3:
         raise ValueError("q must be [total, H, Dk]")
@@ -196,8 +229,7 @@ def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (total, H, Dk))
     _need(v, "v", q.dtype, (total, H, Dv))
-    _need(g, "g", torch.float32, (total, H, Dk))
-    _need(beta, "beta", torch.float32, (total, H))
+    pro = _gates(g, beta, (total, H, Dk), (total, H), g_logit, beta_logit, qk_l2norm)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     N = cu_seqlens.numel() - 1
     if N < 0:
@@ -209,16 +241,17 @@ def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
     ws, ws_bytes = _workspace(varlen_workspace_bytes(N, total, H, Dk, Dv, q.dtype), fused, workspace, q.device)
     with torch.cuda.device(q.device):
         _check(varlen_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total,
-                              _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], _ptr(ws), ws_bytes,
-                              _stream(q.device)))
+                              _ptr(s0), _ptr(o), _ptr(sf), H, Dk, Dv, chunk, DTYPE[q.dtype], pro, _ptr(ws),
+                              ws_bytes, _stream(q.device)))
     return o, sf
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-                state: torch.Tensor, inplace: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+                state: torch.Tensor, inplace: bool = False, g_logit: bool = False, beta_logit: bool = False,
+                qk_l2norm: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """One token per sequence.  q, k, g: [B, H, Dk]; v: [B, H, Dv]; beta: [B, H];
     state (fp32): [B, H, Dk, Dv].  Returns o [B, H, Dv] (fp32) and the new state
-    (``state`` itself when ``inplace``)."""
+    (``state`` itself when ``inplace``).  Prologue options as for :func:`chunk_fwd`."""
     if q.dim() != 3:
         raise ValueError("q must be [B, H, Dk]")
     B, H, Dk = q.shape
@@ -228,12 +261,11 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, H, Dk))
     _need(v, "v", q.dtype, (B, H, Dv))
-    _need(g, "g", torch.float32, (B, H, Dk))
-    _need(beta, "beta", torch.float32, (B, H))
+    pro = _gates(g, beta, (B, H, Dk), (B, H), g_logit, beta_logit, qk_l2norm)
     _need(state, "state", torch.float32, (B, H, Dk, Dv))
     o = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
     out_state = state if inplace else torch.empty_like(state)
     with torch.cuda.device(q.device):
         _check(decode_step_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out_state),
-                               _ptr(o), B, H, Dk, Dv, DTYPE[q.dtype], _stream(q.device)))
+                               _ptr(o), B, H, Dk, Dv, DTYPE[q.dtype], pro, _stream(q.device)))
     return o, out_state

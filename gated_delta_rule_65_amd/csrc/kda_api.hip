@@ -56,6 +56,21 @@ kda_status check_ptrs(std::initializer_list<Ptr> ptrs) {
     return KDA_OK;
 }
 
+kda_status read_prologue(const kda_prologue* p, kda::Prologue& out) {
+    out = kda::Prologue{false, false, false, false, false};
+    if (!p) return KDA_OK;
+    if (p->g_dtype != KDA_F32 && p->g_dtype != KDA_BF16)
+        return fail(KDA_ERR_BAD_DTYPE, "prologue g_dtype must be KDA_F32 or KDA_BF16");
+    if (p->beta_dtype != KDA_F32 && p->beta_dtype != KDA_BF16)
+        return fail(KDA_ERR_BAD_DTYPE, "prologue beta_dtype must be KDA_F32 or KDA_BF16");
+    out.g_bf16 = p->g_dtype == KDA_BF16;
+    out.g_logit = p->g_logit != 0;
+    out.b_bf16 = p->beta_dtype == KDA_BF16;
+    out.b_logit = p->beta_logit != 0;
+    out.l2norm = p->qk_l2norm != 0;
+    return KDA_OK;
+}
+
 kda_status launched(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
     return ok();
@@ -82,11 +97,14 @@ kda_status run_chunked(const kda::ChunkArgs& a, void* workspace, size_t workspac
 
 extern "C" {
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk, int Dv,
-                         int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                         int chunk, kda_dtype dtype, const kda_prologue* prologue, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     kda_status st;
+    kda::Prologue pro;
     if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = read_prologue(prologue, pro)) != KDA_OK) return st;
     if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
     if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
     if (B < 0 || T < 0) return fail(KDA_ERR_BAD_SHAPE, "B and T must be >= 0");
@@ -97,16 +115,18 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                           {s_final, "s_final", false}, {workspace, "workspace", false}})) != KDA_OK)
         return st;
     if (B == 0 || (!tokens && !s_final)) return ok();
-    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, nullptr, T, B * T, B, H, Dk, Dv, dtype == KDA_F32};
+    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, nullptr, T, B * T, B, H, Dk, Dv, dtype == KDA_F32, pro};
     return run_chunked(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_chunk_fwd");
 }
 
-kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
-                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype,
+                          const kda_prologue* prologue, void* workspace, size_t workspace_bytes, void* stream) {
     kda_status st;
+    kda::Prologue pro;
     if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = read_prologue(prologue, pro)) != KDA_OK) return st;
     if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
     if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
     if (N < 0 || total < 0) return fail(KDA_ERR_BAD_SHAPE, "N and total must be >= 0");
@@ -118,15 +138,17 @@ kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const flo
                           {s_final, "s_final", false}, {workspace, "workspace", false}})) != KDA_OK)
         return st;
     if (N == 0 || (!tokens && !s_final)) return ok();
-    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, cu_seqlens, 0, total, N, H, Dk, Dv, dtype == KDA_F32};
+    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, cu_seqlens, 0, total, N, H, Dk, Dv, dtype == KDA_F32, pro};
     return run_chunked(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_varlen_fwd");
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                            const float* s_in, float* s_out, float* o, int64_t B, int H, int Dk, int Dv,
-                           kda_dtype dtype, void* stream) {
+                           kda_dtype dtype, const kda_prologue* prologue, void* stream) {
     kda_status st;
+    kda::Prologue pro;
     if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = read_prologue(prologue, pro)) != KDA_OK) return st;
     if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
     if (B < 0) return fail(KDA_ERR_BAD_SHAPE, "B must be >= 0");
     if (B * H > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "B*H exceeds the grid limit");
@@ -142,7 +164,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
             return fail(KDA_ERR_BAD_SHAPE, "s_in and s_out overlap without being the same buffer");
     }
     if (!any) return ok();
-    kda::DecodeArgs a{q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype == KDA_F32};
+    kda::DecodeArgs a{q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype == KDA_F32, pro};
     return launched(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda_decode_step");
 }
 
@@ -177,6 +199,6 @@ size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int D
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
-const char* kda_version(void) { return "kda-gfx950 0.2"; }
+const char* kda_version(void) { return "kda-gfx950 0.3"; }
 
 }  // extern "C"

@@ -39,7 +39,6 @@ namespace kda {
 
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int kSlice = 32;  // state columns per workgroup
-constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DK, bool F32>
 struct ChunkLds {
@@ -90,7 +89,7 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
                                             const float (*Ei)[8], const float* tPw, const char* pCol,
                                             const float* tD, const char* pS, const char* pRQ, const char* pRK,
                                             const float* sBeta, const float (*vD)[4], float* sA, char* pP,
-                                            char* pX, f32x4_t* accO, int m, int cg) {
+                                            char* pX, f32x4_t* accO, float rq, float rk, int m, int cg) {
     using Fr = Frag<F32>;
     constexpr int KS = DK / 32;
     constexpr int IMIN = (W == 3) ? 2 : 0;  // first own Gram block of this row block
@@ -107,6 +106,11 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
         float qf[8], kf[8], pw[8], x1[8], x2[8], x3[8];
         raw8_to_float<F32>(pq[s], qf);
         raw8_to_float<F32>(pk[s], kf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            qf[j] *= rq;
+            kf[j] *= rk;
+        }
         lds_read8(&tPw[W * DK + c0], pw);
         Fr fqE, fkE, fkd, fQt, fKt;
 #pragma unroll
@@ -204,12 +208,15 @@ __device__ __forceinline__ void gram_chain1(const Raw8<F32>* pq, const Raw8<F32>
     }
 }
 
-template <int DK, bool F32>
+template <int DK, bool F32, bool PRO>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv,
-    const float* __restrict__ g, const float* __restrict__ beta, const float* s0, float* __restrict__ o,
+    const void* __restrict__ gv, const void* __restrict__ bv, const float* s0, float* __restrict__ o,
     float* s_final, const int32_t* __restrict__ cu_seqlens, int64_t T_fixed, int64_t total, int64_t N, int H,
-    int Dv) {
+    int Dv, Prologue pro) {
+    // input prologue; PRO = false compiles the plain form (fp32 log alpha and beta, q and k as given)
+    const Prologue pf{PRO && pro.g_bf16, PRO && pro.g_logit, PRO && pro.b_bf16, PRO && pro.b_logit,
+                      PRO && pro.l2norm};
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChunkLds<DK, F32>;
@@ -300,16 +307,20 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
     const uint32_t rs_k = (uint32_t)H * DK, rs_v = (uint32_t)H * (uint32_t)Dv;
     const In* __restrict__ q_l = q + (int64_t)h * DK + 8 * cg;
     const In* __restrict__ k_l = k + (int64_t)h * DK + 8 * cg;
-    const float* __restrict__ g_l = g + (int64_t)h * DK + 8 * cg;
+    const int64_t g_l = (int64_t)h * DK + 8 * cg;  // element offset into g (fp32 or bf16)
     const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + m;
-    const float* __restrict__ b_l = beta + h;
+
     float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + m;
     auto prefetch_part = [&](int part, int64_t t0, int nt) {
         const int64_t cq = t0 * (int64_t)rs_k;
         const uint32_t rq = (uint32_t)min(r, nt - 1) * rs_k;
         if (part == 0) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) load_raw8(g_l + cq + rq + 32 * s, pg[s]);
+            for (int s = 0; s < KS; ++s) {
+                const int64_t e = g_l + cq + rq + 32 * s;
+                if (pf.g_bf16) pg[s].a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(gv) + e);
+                else load_raw8(static_cast<const float*>(gv) + e, pg[s]);
+            }
         } else if (part == 1) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) load_raw8(k_l + cq + rq + 32 * s, pk[s]);
@@ -324,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) pv[nb][jj] = v_l[cv + rv + 16 * nb];
             }
-            pb = b_l[t0 * H + (uint32_t)min(tid & 63, nt - 1) * (uint32_t)H];
+            pb = load1_gate(bv, t0 * H + h + (uint32_t)min(tid & 63, nt - 1) * (uint32_t)H, pf.b_bf16);
         }
     };
     auto prefetch = [&](int64_t t0, int nt) {
@@ -357,10 +368,16 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
         const int nt_next = more ? (int)min<int64_t>(kChunk, end - t0 - kChunk) : nt;
         float gl[KS][8];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            raw8_to_float<true>(pg[s], gl[s]);
+        for (int s = 0; s < KS; ++s) {  // clamped log alpha in log2 units; 0 past the end
+            if (pf.g_bf16) {
+                Raw8<false> t;
+                t.a = pg[s].a;
+                raw8_to_float<false>(t, gl[s]);
+            } else {
+                raw8_to_float<true>(pg[s], gl[s]);
+            }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) gl[s][j] = rv ? gl[s][j] : 0.f;
+            for (int j = 0; j < 8; ++j) gl[s][j] = rv ? gate_log2(gl[s][j], pf.g_logit) : 0.f;
         }
         float vD[2][4];
 #pragma unroll
@@ -372,16 +389,15 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
                 else x = bf16_bits_to_float(pv[nb][jj]);
                 vD[nb][jj] = (16 * w + 4 * cg + jj < nt) ? x : 0.f;
             }
-        const float bval = (tid < nt) ? pb : 0.f;
+        const float bval = (tid < nt) ? beta_value(pb, pf.b_logit) : 0.f;
         if (tid < kChunk) sBeta[tid] = bval;
         prefetch_part(3, t0_next, nt_next);  // v and beta of the next chunk
 
-        // clamp to [-5, 0], convert to log2 units, inclusive sums over each 16-token sub-block
+        // inclusive sums over each 16-token sub-block
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                gl[s][j] = row16_inclusive_scan(__builtin_amdgcn_fmed3f(gl[s][j], -5.f, 0.f) * kLog2e);
+            for (int j = 0; j < 8; ++j) gl[s][j] = row16_inclusive_scan(gl[s][j]);
         if (m == 15) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -419,6 +435,23 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
         // the diagonal and Kbar^T go to LDS.  Rows past the end of the sequence need no
         // masking beyond g = 0 and b = 0: their rows of A are zero, so their rows of
         // M^{-1} are unit rows and their pseudo-values U = b(V - Kt S) = 0.
+        float rq = 1.f, rk = 1.f;  // 1/||q_r||, 1/||k_r|| when q and k are scaled to unit length
+        if (pf.l2norm) {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                float qf[8], kf[8];
+                raw8_to_float<F32>(pq[s], qf);
+                raw8_to_float<F32>(pk[s], kf);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    sq = fmaf(qf[j], qf[j], sq);
+                    sk = fmaf(kf[j], kf[j], sk);
+                }
+            }
+            rq = rnorm_lanes4(sq);
+            rk = rnorm_lanes4(sk);
+        }
         float Ei[KS][8];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -427,6 +460,8 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
             lds_read8(&tAf[w * DK + c0], af);
             lds_read8(&tBt[w * DK + c0], bt);
             raw8_to_float<F32>(pk[s], kf);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kf[j] *= rk;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float E = __builtin_amdgcn_exp2f(gl[s][j]);   // e^{G_r - G_start(w)} in [e^-80, 1]
@@ -442,7 +477,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
                 raw8_to_float<F32>(pq[s], qf);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    xqe[j] = qf[j] * gl[s][j];
+                    xqe[j] = (qf[j] * rq) * gl[s][j];
                     xke[j] = kf[j] * gl[s][j];
                 }
                 lds_store8<F32, 16, DK>(smem + L::RQ, m, c0, xqe);
@@ -463,10 +498,10 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
         // accumulations interleave.
         f32x4_t accO[2];
         switch (w) {
-            case 0: gram_chain1<0, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            case 1: gram_chain1<1, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            case 2: gram_chain1<2, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
-            default: gram_chain1<3, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, m, cg); break;
+            case 0: gram_chain1<0, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, rq, rk, m, cg); break;
+            case 1: gram_chain1<1, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, rq, rk, m, cg); break;
+            case 2: gram_chain1<2, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, rq, rk, m, cg); break;
+            default: gram_chain1<3, DK, F32>(pq, pk, gl, Ei, tPw, pCol, tD, pS, smem + L::RQ, smem + L::RK, sBeta, vD, sA, pP, pX, accO, rq, rk, m, cg); break;
         }
 
         lds_barrier();  // (4)
@@ -628,8 +663,12 @@ int64_t chunk_grid_size(int64_t N, int H, int Dv) {
 template <int DK, bool F32>
 static hipError_t launch_dk(const ChunkArgs& a, hipStream_t st) {
     const int64_t grid = chunk_grid_size(a.N, a.H, a.Dv);
-    hipLaunchKernelGGL((chunk_fwd_kernel<DK, F32>), dim3((unsigned)grid), dim3(256), 0, st, a.q, a.k, a.v, a.g,
-                       a.beta, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv);
+    if (any_prologue(a.pro))
+        hipLaunchKernelGGL((chunk_fwd_kernel<DK, F32, true>), dim3((unsigned)grid), dim3(256), 0, st, a.q, a.k, a.v,
+                           a.g, a.beta, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, a.pro);
+    else
+        hipLaunchKernelGGL((chunk_fwd_kernel<DK, F32, false>), dim3((unsigned)grid), dim3(256), 0, st, a.q, a.k, a.v,
+                           a.g, a.beta, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, a.pro);
     return hipGetLastError();
 }
 

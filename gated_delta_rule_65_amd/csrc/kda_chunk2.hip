@@ -30,7 +30,6 @@ namespace {
 
 constexpr int kC = 64;  // tokens per chunk
 constexpr int kS = 32;  // state columns per chain workgroup
-constexpr float kL2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------- fragments in HBM
 // A fragment (eight values per lane, see Frag) is stored as two planes of
@@ -139,8 +138,8 @@ struct PrepLds {
     static constexpr int A0 = PM + 64 * 68 * 4;
     static constexpr int A = A0 > MKB::BYTES ? A0 : MKB::BYTES;  // fp32 b_r A_ri [64][68], then M^{-1} Diag(b)
     static constexpr int D = A + 64 * 68 * 4;             // fp32 diagonal inverses [4][16][17]
-    static constexpr int TAB = D + 4 * 16 * 17 * 4;       // fp32 tables [12][DK]
-    static constexpr int GT = TAB + 12 * DK * 4;          // fp32 sub-block sums (log2) [4][DK]
+    static constexpr int TAB = D + 4 * 16 * 17 * 4;       // fp32 tables [15][DK]
+    static constexpr int GT = TAB + 15 * DK * 4;          // fp32 sub-block sums (log2) [4][DK]
     static constexpr int BETA = GT + 4 * DK * 4;          // fp32 b [64]
     static constexpr int TOTAL = BETA + 64 * 4;
     static_assert(TOTAL <= 80 * 1024, "two prep workgroups per CU");
@@ -214,14 +213,18 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
     }
 }
 
-template <int DK, bool F32>
+template <int DK, bool F32, bool PRO>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
-                                                      const float* __restrict__ g, const float* __restrict__ beta,
+                                                      const void* __restrict__ gv, const void* __restrict__ bv,
                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
-                                                      int64_t total, int64_t N, int H, char* __restrict__ ws) {
+                                                      int64_t total, int64_t N, int H, Prologue pro,
+                                                      char* __restrict__ ws) {
     using In = typename std::conditional<F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = PrepLds<DK, F32>;
+    // input prologue; PRO = false compiles the plain form (fp32 log alpha and beta, q and k as given)
+    const Prologue pf{PRO && pro.g_bf16, PRO && pro.g_logit, PRO && pro.b_bf16, PRO && pro.b_logit,
+                      PRO && pro.l2norm};
     using R = Rec<DK, F32>;
     constexpr int KS = DK / 32;
     const In* __restrict__ q = static_cast<const In*>(qv);
@@ -233,10 +236,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     char* pKB = smem + L::KB;
     float* sA = reinterpret_cast<float*>(smem + L::A);
     float* sD = reinterpret_cast<float*>(smem + L::D);
-    float* tCum = reinterpret_cast<float*>(smem + L::TAB);  // sum_{J<w} Gt_J (log2)  [4][DK]
-    float* tBt = tCum + 4 * DK;                             // e^{Gt_w}               [4][DK]
+    float* tPw = reinterpret_cast<float*>(smem + L::TAB);   // e^{sum_{J<w} Gt_J}     [4][DK]
+    float* tBt = tPw + 4 * DK;                              // e^{Gt_w}               [4][DK]
     float* tD = tBt + 4 * DK;                               // e^{sum_{I<J<R} Gt_J}   [3][DK]
-    float* tGC = tD + 3 * DK;                               // G_C (log2)             [1][DK]
+    float* tAf = tD + 3 * DK;                               // e^{sum_{J>w} Gt_J}     [4][DK]
     float* sGt = reinterpret_cast<float*>(smem + L::GT);
     float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
 
@@ -276,14 +279,33 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     for (int s = 0; s < KS; ++s) {
         load8_as_float(q + base + 32 * s, qf[s]);
         load8_as_float(k + base + 32 * s, kf[s]);
-        load8_as_float(g + base + 32 * s, gl[s]);
+        load8_gate(gv, base + 32 * s, pf.g_bf16, gl[s]);
     }
-    if (tid < kC) sBeta[tid] = (tid < nt) ? beta[(t0 + tid) * H + h] : 0.f;
+    if (tid < kC)
+        sBeta[tid] = (tid < nt) ? beta_value(load1_gate(bv, (t0 + tid) * H + h, pf.b_bf16), pf.b_logit) : 0.f;
+    if (pf.l2norm) {  // unit q and k rows: each row lives in lanes m, m+16, m+32, m+48
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                sq = fmaf(qf[s][jj], qf[s][jj], sq);
+                sk = fmaf(kf[s][jj], kf[s][jj], sk);
+            }
+        const float rq = rnorm_lanes4(sq), rk = rnorm_lanes4(sk);
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                qf[s][jj] *= rq;
+                kf[s][jj] *= rk;
+            }
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-            gl[s][jj] = row16_inclusive_scan(rv ? __builtin_amdgcn_fmed3f(gl[s][jj], -5.f, 0.f) * kL2e : 0.f);
+            gl[s][jj] = row16_inclusive_scan(rv ? gate_log2(gl[s][jj], pf.g_logit) : 0.f);
     if (m == 15) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -298,10 +320,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     if (tid < DK) {
         const int c = tid;
         const float G0 = sGt[c], G1 = sGt[DK + c], G2 = sGt[2 * DK + c], G3 = sGt[3 * DK + c];
-        tCum[c] = 0.f;
-        tCum[DK + c] = G0;
-        tCum[2 * DK + c] = G0 + G1;
-        tCum[3 * DK + c] = G0 + G1 + G2;
+        tPw[c] = 1.f;
+        tPw[DK + c] = __builtin_amdgcn_exp2f(G0);
+        tPw[2 * DK + c] = __builtin_amdgcn_exp2f(G0 + G1);
+        tPw[3 * DK + c] = __builtin_amdgcn_exp2f(G0 + G1 + G2);
+        tAf[c] = __builtin_amdgcn_exp2f(G1 + G2 + G3);
+        tAf[DK + c] = __builtin_amdgcn_exp2f(G2 + G3);
+        tAf[2 * DK + c] = __builtin_amdgcn_exp2f(G3);
+        tAf[3 * DK + c] = 1.f;
         tBt[c] = __builtin_amdgcn_exp2f(G0);
         tBt[DK + c] = __builtin_amdgcn_exp2f(G1);
         tBt[2 * DK + c] = __builtin_amdgcn_exp2f(G2);
@@ -310,27 +336,27 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         tD[DK + c] = __builtin_amdgcn_exp2f(G2);
         tD[2 * DK + c] = __builtin_amdgcn_exp2f(G1 + G2);
         const float GC = ((G0 + G1) + G2) + G3;
-        tGC[c] = GC;
         reinterpret_cast<float*>(rec + R::GC)[c] = __builtin_amdgcn_exp2f(GC);
     }
     lds_barrier();  // (2)
 
     // ---- Qt, Kt to the record; Gram factors E = e^{Gloc}, Ei = e^{-Gloc}; column operands to LDS
+    // (two exponentials per element: the sub-block offsets come from the per-channel tables)
     float E[KS][8], Ei[KS][8];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int c0 = 32 * s + 8 * cg;
-        float cum[8], bt[8], xq[8], xk[8], xc[8];
-        lds_read8(&tCum[w * DK + c0], cum);
+        float pw[8], bt[8], xq[8], xk[8], xc[8];
+        lds_read8(&tPw[w * DK + c0], pw);
         lds_read8(&tBt[w * DK + c0], bt);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const float gam = __builtin_amdgcn_exp2f(cum[jj] + gl[s][jj]);  // e^{G_r}
-            xq[jj] = qf[s][jj] * gam;
-            xk[jj] = kf[s][jj] * gam;
             E[s][jj] = __builtin_amdgcn_exp2f(gl[s][jj]);
             Ei[s][jj] = __builtin_amdgcn_exp2f(-gl[s][jj]);
-            xc[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);
+            const float gam = pw[jj] * E[s][jj];  // e^{G_r}
+            xq[jj] = qf[s][jj] * gam;
+            xk[jj] = kf[s][jj] * gam;
+            xc[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);  // k e^{G_end(w) - G_r}
         }
         Fr fq, fk;
         fq.set(xq);
@@ -416,12 +442,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const int c0 = 32 * s + 8 * cg;
-        float cum[8], gcl[8];
-        lds_read8(&tCum[w * DK + c0], cum);
-        lds_read8(&tGC[c0], gcl);
+        float bt[8], af[8];
+        lds_read8(&tBt[w * DK + c0], bt);
+        lds_read8(&tAf[w * DK + c0], af);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-            const float kbar = kf[s][jj] * __builtin_amdgcn_exp2f(gcl[jj] - (cum[jj] + gl[s][jj]));
+            const float kbar = (kf[s][jj] * (bt[jj] * Ei[s][jj])) * af[jj];  // k e^{G_C - G_r}
             lds_store1<F32, DK, kC>(pKB, c0 + jj, r, kbar);
         }
     }
@@ -857,9 +883,12 @@ static int64_t chain_grid(int64_t items, int slices) { return ((items + 7) / 8) 
 template <int DK, bool F32>
 static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int64_t prep_grid = chunk_slots(a) * a.H;
-    if (prep_grid > 0)
-        hipLaunchKernelGGL((prep_kernel<DK, F32>), dim3((unsigned)prep_grid), dim3(256), 0, st, a.q, a.k, a.g, a.beta,
-                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, static_cast<char*>(ws));
+    if (prep_grid > 0 && any_prologue(a.pro))
+        hipLaunchKernelGGL((prep_kernel<DK, F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st, a.q, a.k, a.g,
+                           a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
+    else if (prep_grid > 0)
+        hipLaunchKernelGGL((prep_kernel<DK, F32, false>), dim3((unsigned)prep_grid), dim3(256), 0, st, a.q, a.k, a.g,
+                           a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int P = chunk_segments(a);

@@ -20,18 +20,21 @@
 
 namespace kda {
 
-template <int DK, int DV, bool F32>
+template <int DK, int DV, bool F32, bool PRO>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
-                                                     const void* __restrict__ vv, const float* __restrict__ g,
-                                                     const float* __restrict__ beta, const float* s_in,
-                                                     float* s_out, float* __restrict__ o) {
+                                                     const void* __restrict__ vv, const void* __restrict__ gv,
+                                                     const void* __restrict__ bv, const float* s_in,
+                                                     float* s_out, float* __restrict__ o, Prologue pro) {
     using In = typename std::conditional<F32, float, uint16_t>::type;
+    // input prologue; PRO = false compiles the plain form (fp32 log alpha and beta, q and k as given)
+    const Prologue pf{PRO && pro.g_bf16, PRO && pro.g_logit, PRO && pro.b_bf16, PRO && pro.b_logit,
+                      PRO && pro.l2norm};
     constexpr int C4 = DV / 4;     // threads across the columns
     constexpr int RG = 256 / C4;   // row groups
     constexpr int RPT = DK / RG;   // rows per thread
     static_assert(RPT * RG == DK, "row split");
 
-    __shared__ float sk[DK], sa[DK], sq[DK], su[DV];
+    __shared__ float sk[DK], sa[DK], sq[DK], su[DV], snk[2], snq[2];
     __shared__ float4 sred[RG][C4];
 
     const In* __restrict__ q = static_cast<const In*>(qv);
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
     // state loads; only threads tid < DK / tid < C4 use them)
     const int ti = tid % DK, tv = tid % C4;
     const In kr = k[bh * DK + ti], qr = q[bh * DK + ti];
-    const float gr = g[bh * DK + ti], b = beta[bh];
+    const float gr = load1_gate(gv, bh * DK + ti, pf.g_bf16), braw = load1_gate(bv, bh, pf.b_bf16);
     In vr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vr[j] = v[bh * DV + 4 * tv + j];
@@ -64,14 +67,34 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
     // compiler to sink the vector loads into
     sk[ti] = tof(kr);
     sq[ti] = tof(qr);
-    sa[ti] = __expf(fminf(fmaxf(gr, -5.f), 0.f));
+    sa[ti] = pf.g_logit ? __builtin_amdgcn_exp2f(gate_log2(gr, true)) : __expf(fminf(fmaxf(gr, -5.f), 0.f));
+    const float b = beta_value(braw, pf.b_logit);
+    if (pf.l2norm) {  // squared norms of k and q: waves 0 (and 1) hold every index once
+        float k2 = tof(kr) * tof(kr), q2 = tof(qr) * tof(qr);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            k2 += __shfl_xor(k2, off);
+            q2 += __shfl_xor(q2, off);
+        }
+        if ((tid & 63) == 0 && tid < DK) {
+            snk[tid >> 6] = k2;
+            snq[tid >> 6] = q2;
+        }
+    }
     __syncthreads();
+    float rk = 1.f, rq = 1.f;  // 1/||k||, 1/||q|| when both are scaled to unit length
+    if (pf.l2norm) {
+        const float k2 = DK == 128 ? snk[0] + snk[1] : snk[0];
+        const float q2 = DK == 128 ? snq[0] + snq[1] : snq[0];
+        rk = k2 > 0.f ? __builtin_amdgcn_rsqf(k2) : 0.f;
+        rq = q2 > 0.f ? __builtin_amdgcn_rsqf(q2) : 0.f;
+    }
 
     float4 wp = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int mm = 0; mm < RPT; ++mm) {
         const int i = rg + RG * mm;
-        const float ak = sa[i] * sk[i];
+        const float ak = sa[i] * (sk[i] * rk);
         wp.x = fmaf(ak, st[mm][0], wp.x);
         wp.y = fmaf(ak, st[mm][1], wp.y);
         wp.z = fmaf(ak, st[mm][2], wp.z);
@@ -97,7 +120,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
 #pragma unroll
     for (int mm = 0; mm < RPT; ++mm) {
         const int i = rg + RG * mm;
-        const float a = sa[i], kk = sk[i], qq = sq[i];
+        const float a = sa[i], kk = sk[i] * rk, qq = sq[i] * rq;
         f32x4_t x;
         x[0] = fmaf(a, st[mm][0], kk * u.x);
         x[1] = fmaf(a, st[mm][1], kk * u.y);
@@ -125,12 +148,19 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ qv
 template <int DK, int DV>
 static hipError_t launch_dv(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)(a.B * a.H));
-    if (a.f32)
-        hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta, a.s_in,
-                           a.s_out, a.o);
+    const bool pro = any_prologue(a.pro);
+    if (a.f32 && pro)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, true, true>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.s_in, a.s_out, a.o, a.pro);
+    else if (a.f32)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, true, false>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.s_in, a.s_out, a.o, a.pro);
+    else if (pro)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, false, true>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.s_in, a.s_out, a.o, a.pro);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.s_in, a.s_out, a.o);
+        hipLaunchKernelGGL((decode_kernel<DK, DV, false, false>), grid, dim3(256), 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.s_in, a.s_out, a.o, a.pro);
     return hipGetLastError();
 }
 

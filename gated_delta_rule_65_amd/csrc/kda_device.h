@@ -28,6 +28,42 @@ __device__ __forceinline__ void load8_as_float(const float* p, float x[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// Input prologue (the kda_prologue options): element type of the gate and beta
+// inputs, their logit forms, and unit-length q/k.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8_gate(const void* p, int64_t idx, bool bf, float x[8]) {
+    if (bf) load8_as_float(static_cast<const uint16_t*>(p) + idx, x);
+    else load8_as_float(static_cast<const float*>(p) + idx, x);
+}
+__device__ __forceinline__ float load1_gate(const void* p, int64_t idx, bool bf) {
+    return bf ? bf16_bits_to_float(static_cast<const uint16_t*>(p)[idx]) : static_cast<const float*>(p)[idx];
+}
+
+// Clamped log alpha in log2 units.  A log-alpha input x gives clamp(x, -5, 0) / ln 2.  A gate logit
+// x gives log alpha = -softplus(x), evaluated as -(max(x, 0) + ln(1 + e^{-|x|})) so that neither
+// exponential overflows, then the same clamp.
+__device__ __forceinline__ float gate_log2(float x, bool logit) {
+    constexpr float l2e = 1.4426950408889634f;
+    if (!logit) return __builtin_amdgcn_fmed3f(x, -5.f, 0.f) * l2e;
+    const float sp2 = fmaxf(x, 0.f) * l2e + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * l2e));
+    return __builtin_amdgcn_fmed3f(-sp2, -5.f * l2e, 0.f);
+}
+
+// beta from its input: the value itself, or the logistic function 1 / (1 + e^{-x}) of a logit.
+__device__ __forceinline__ float beta_value(float x, bool logit) {
+    constexpr float l2e = 1.4426950408889634f;
+    return logit ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * l2e)) : x;
+}
+
+// 1/||x|| of a vector whose squared entries are summed in `ss` over lanes l, l^16, l^32, l^48
+// (every lane of the group gets the same value); 0 for an all-zero vector.
+__device__ __forceinline__ float rnorm_lanes4(float ss) {
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    return ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // MFMA operand fragments.  For v_mfma_f32_16x16x32_bf16 a lane holds eight
 // consecutive reduction-index values of one row (A) or one column (B):
 // lane l -> row/column l%16, reduction indices 8*(l/16) .. 8*(l/16)+7 of the

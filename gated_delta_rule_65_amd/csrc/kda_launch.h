@@ -5,9 +5,18 @@
 
 namespace kda {
 
+// How the gate and beta inputs are read (kda_prologue of the C ABI): element type, and whether
+// they hold logits (log alpha = -softplus(x), beta = sigmoid(b)); l2norm scales q and k to unit
+// length per token and head.
+struct Prologue {
+    bool g_bf16, g_logit, b_bf16, b_logit, l2norm;
+};
+inline bool any_prologue(const Prologue& p) { return p.g_bf16 || p.g_logit || p.b_bf16 || p.b_logit || p.l2norm; }
+
 struct ChunkArgs {
     const void *q, *k, *v;
-    const float *g, *beta, *s0;
+    const void *g, *beta;
+    const float* s0;
     float *o, *s_final;
     const int32_t* cu_seqlens;  // device offsets, or nullptr for equal-length sequences
     int64_t T_fixed;            // tokens per sequence when cu_seqlens == nullptr
@@ -15,15 +24,18 @@ struct ChunkArgs {
     int64_t N;                  // sequences
     int H, Dk, Dv;
     bool f32;                   // q/k/v are float32 (else bf16)
+    Prologue pro;
 };
 
 struct DecodeArgs {
     const void *q, *k, *v;
-    const float *g, *beta, *s_in;
+    const void *g, *beta;
+    const float* s_in;
     float *s_out, *o;
     int64_t B;
     int H, Dk, Dv;
     bool f32;
+    Prologue pro;
 };
 
 int64_t chunk_grid_size(int64_t N, int H, int Dv);

@@ -23,10 +23,12 @@
  *  - All tensor pointers are DEVICE pointers, contiguous, row-major in the
  *    layouts given below, 16-byte aligned.  The caller owns every buffer; the
  *    library allocates nothing and keeps no pointer after a call returns.
- *  - q, k, v use `dtype` (KDA_BF16 or KDA_F32).  g (log alpha, clamped to
- *    [-5, 0] by the library), beta, the states and the output o are float32.
- *    o is float32 for both input types: rounding it to bf16 would by itself
- *    cost up to about 3% of the output RMS on realistic gate statistics.
+ *  - q, k, v use `dtype` (KDA_BF16 or KDA_F32).  By default g (log alpha,
+ *    clamped to [-5, 0] by the library) and beta are float32 and used as
+ *    given; a kda_prologue (below) can change that.  The states and the output
+ *    o are float32.  o is float32 for both input types: rounding it to bf16
+ *    would by itself cost up to about 3% of the output RMS on realistic gate
+ *    statistics.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *    asynchronous and stream-ordered; nothing here synchronises the device.
  *  - Arguments are validated on the host before any launch.  A non-zero
@@ -62,6 +64,32 @@ extern "C" {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/*
+ * Input prologue: transforms applied to the inputs as the kernels load them, so
+ * that raw projections can be fed in without separate passes over HBM, and
+ * bf16 gates halve their bytes.  The page cited above fixes only the roles of
+ * alpha (forgetting, kept inside [e^-5, 1] against bf16 underflow and overflow)
+ * and beta (write strength); the logit forms below are the customary
+ * parameterisations of such gates, not something the page states.  Pass NULL
+ * for the defaults (all fields zero / KDA_F32):
+ *   g_dtype     element type of g (KDA_F32 or KDA_BF16)
+ *   g_logit     0: g is log alpha.  Nonzero: g holds gate logits x and
+ *               log alpha = -softplus(x) = -ln(1 + e^x); the clamp to [-5, 0]
+ *               follows in both cases.
+ *   beta_dtype  element type of beta (KDA_F32 or KDA_BF16)
+ *   beta_logit  0: beta is used as given.  Nonzero: beta = 1 / (1 + e^-b).
+ *   qk_l2norm   nonzero: q and k are scaled to unit L2 norm per token and
+ *               head before use (an all-zero vector stays zero).
+ * The transforms are evaluated in float32.
+ */
+typedef struct {
+    kda_dtype g_dtype;
+    int g_logit;
+    kda_dtype beta_dtype;
+    int beta_logit;
+    int qk_l2norm;
+} kda_prologue;
+
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL_ARG = 1,   /* a required pointer is NULL */
@@ -74,18 +102,20 @@ typedef enum {
 /*
  * Chunked prefill over B sequences of equal length T.
  *   q, k : [B, T, H, Dk]  dtype          v : [B, T, H, Dv]  dtype
- *   g    : [B, T, H, Dk]  float32 (log alpha; clamped to [-5, 0] inside)
- *   beta : [B, T, H]      float32 (used as given, not clamped)
+ *   g    : [B, T, H, Dk]  log alpha, clamped to [-5, 0] inside (float32 unless
+ *                         the prologue says otherwise)
+ *   beta : [B, T, H]      used as given, not clamped (idem)
+ *   prologue : input transforms, or NULL (see kda_prologue)
  *   s0   : [B, H, Dk, Dv] float32 initial state, or NULL for zeros
  *   o    : [B, T, H, Dv]  float32 output (written)
  *   s_final : [B, H, Dk, Dv] float32 final state (written), or NULL
  * T = 0 is allowed: o is untouched and s_final receives s0 (or zeros).
  * s_final may alias s0 (each state is read before it is written).
  */
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
-                         int Dv, int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         int Dv, int chunk, kda_dtype dtype, const kda_prologue* prologue, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
@@ -98,6 +128,7 @@ size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kd
 /*
  * Packed variable-length prefill: N independent sequences stored back to back.
  *   q, k, g : [total, H, Dk]; v, o : [total, H, Dv]; beta : [total, H]
+ *   (element types and prologue as for kda_chunk_fwd)
  *   cu_seqlens : DEVICE int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
  *                cu_seqlens[N] = total; sequence n is tokens
  *                cu_seqlens[n] .. cu_seqlens[n+1]-1 and starts its own chunks.
@@ -106,10 +137,10 @@ size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kd
  * break the stated invariants give unspecified results for the affected
  * sequences but never access memory outside [0, total) tokens.
  */
-kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                           const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, float* o,
-                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          float* s_final, int H, int Dk, int Dv, int chunk, kda_dtype dtype,
+                          const kda_prologue* prologue, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes kda_varlen_fwd needs (0 if none or unsupported sizes): it
@@ -122,15 +153,16 @@ size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int D
 /*
  * One decoding step (one new token per sequence) on B sequences.
  *   q, k : [B, H, Dk] dtype;  v : [B, H, Dv] dtype
- *   g    : [B, H, Dk] float32 (log alpha);  beta : [B, H] float32
+ *   g    : [B, H, Dk] log alpha;  beta : [B, H]  (float32 unless the prologue
+ *          says otherwise; prologue as for kda_chunk_fwd, or NULL)
  *   s_in : [B, H, Dk, Dv] float32 state before the token
  *   s_out: [B, H, Dk, Dv] float32 state after the token; s_out == s_in is
  *          allowed (in-place update); partial overlap is not.
  *   o    : [B, H, Dv] float32 output of the token
  */
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                            const float* s_in, float* s_out, float* o, int64_t B, int H, int Dk, int Dv,
-                           kda_dtype dtype, void* stream);
+                           kda_dtype dtype, const kda_prologue* prologue, void* stream);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);

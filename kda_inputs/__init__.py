@@ -138,6 +138,10 @@ class Spec:
           a fraction ``bound_frac`` of entries forced to g=-5 or g=0, half
           each), 'longmem' (g = -U(0, 0.01)).
     s0_std: None for a zero initial state, else N(0, s0_std) entries.
+    Raw-input forms (what the method's input prologue takes):
+    g_logit: g holds the gate logits x ~ N(0, logit_std) themselves (gate 'softplus' only);
+    beta_logit: beta holds its logits ~ N(0, 1); qk_l2norm: q and k are left at their
+    N(0, 1) draws, not scaled to unit length; gate_dtype: 'f32' or 'bf16' storage of g and beta.
     """
     lengths: Sequence[int]
     H: int
@@ -150,6 +154,11 @@ class Spec:
     seed: int = 0
     packed: bool = False           # packed varlen layout with cu_seqlens
     name: str = ""
+    g_logit: bool = False
+    beta_logit: bool = False
+    qk_l2norm: bool = False
+    logit_std: float = 1.0
+    gate_dtype: str = "f32"
 
     @property
     def total(self) -> int:
@@ -166,14 +175,14 @@ class Inputs:
     q: np.ndarray            # [sumL, H, Dk]  uint16 bf16 bits or float32
     k: np.ndarray            # [sumL, H, Dk]
     v: np.ndarray            # [sumL, H, Dv]
-    g: np.ndarray            # [sumL, H, Dk]  float32 log-alpha (unclamped)
-    beta: np.ndarray         # [sumL, H]      float32
+    g: np.ndarray            # [sumL, H, Dk]  float32 (or bf16 bits) log-alpha (unclamped), or gate logits
+    beta: np.ndarray         # [sumL, H]      float32 (or bf16 bits), or logits
     s0: Optional[np.ndarray]  # [N, H, Dk, Dv] float32 or None
     cu_seqlens: np.ndarray   # [N+1] int32
     extra: dict = field(default_factory=dict)
 
     def as_f32(self, name: str) -> np.ndarray:
-        """q/k/v as float32 (exact upcast of the bf16 values)."""
+        """q/k/v/g/beta as float32 (exact upcast of the bf16 values)."""
         a = getattr(self, name)
         if a.dtype == np.uint16:
             return bf16_bits_to_f32(a)
@@ -190,16 +199,27 @@ def _softplus(x):
 
 def generate(spec: Spec) -> Inputs:
     L, H, Dk, Dv, s = spec.total, spec.H, spec.Dk, spec.Dv, spec.seed
-    q = unit_rows_f32(s, STREAM_Q, L * H, Dk).reshape(L, H, Dk)
-    k = unit_rows_f32(s, STREAM_K, L * H, Dk).reshape(L, H, Dk)
+    if spec.qk_l2norm:
+        q = normal_f32(s, STREAM_Q, L * H * Dk).reshape(L, H, Dk)
+        k = normal_f32(s, STREAM_K, L * H * Dk).reshape(L, H, Dk)
+    else:
+        q = unit_rows_f32(s, STREAM_Q, L * H, Dk).reshape(L, H, Dk)
+        k = unit_rows_f32(s, STREAM_K, L * H, Dk).reshape(L, H, Dk)
     v = normal_f32(s, STREAM_V, L * H * Dv).reshape(L, H, Dv)
     if spec.dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
     elif spec.dtype != "f32":
         raise ValueError(spec.dtype)
-    beta = _sigmoid(normal(s, STREAM_BETA, L * H)).astype(np.float32).reshape(L, H)
+    if spec.beta_logit:
+        beta = normal(s, STREAM_BETA, L * H).astype(np.float32).reshape(L, H)
+    else:
+        beta = _sigmoid(normal(s, STREAM_BETA, L * H)).astype(np.float32).reshape(L, H)
     n_g = L * H * Dk
-    if spec.gate in ("softplus", "softplus_bounds"):
+    if spec.g_logit:
+        if spec.gate != "softplus":
+            raise ValueError("gate logits are drawn for the 'softplus' gate only")
+        g = (spec.logit_std * normal(s, STREAM_G, n_g)).astype(np.float32)
+    elif spec.gate in ("softplus", "softplus_bounds"):
         g = (-_softplus(normal(s, STREAM_G, n_g))).astype(np.float32)
         if spec.gate == "softplus_bounds":
             u = uniform(s, STREAM_GSEL, n_g)
@@ -211,6 +231,10 @@ def generate(spec: Spec) -> Inputs:
     else:
         raise ValueError(spec.gate)
     g = g.reshape(L, H, Dk)
+    if spec.gate_dtype == "bf16":
+        g, beta = f32_to_bf16_bits(g), f32_to_bf16_bits(beta)
+    elif spec.gate_dtype != "f32":
+        raise ValueError(spec.gate_dtype)
     s0 = None
     if spec.s0_std is not None:
         s0 = normal_f32(s, STREAM_S0, spec.n_seq * H * Dk * Dv, scale=spec.s0_std).reshape(spec.n_seq, H, Dk, Dv)

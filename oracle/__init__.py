@@ -9,8 +9,18 @@ nothing from there.
 for the definition and the page it follows).  ``forward`` below only marshals
 numpy arrays into it.
 
+``prologue`` maps raw inputs to the recurrence's inputs in fp64: gate logits x
+to log alpha = -softplus(x), beta logits b to 1 / (1 + e^-b), and q, k to unit
+length per token and head.  The pages fix only the roles of alpha and beta and
+the clamp of alpha to [e^-5, 1] (worldcybernews page "Kimi K3 Open Model
+Surpasses Closed GPT and Anthropic Systems on Independent Benchmarks", second
+paragraph); these logit forms are the customary parameterisation of such gates
+and are written here from their definitions.
+
 Parity status: pinned by ``tests/test_oracle_pins.py`` (hand-worked example,
-exact rational arithmetic, dense brute force, closed forms, invariants).
+exact rational arithmetic, dense brute force, closed forms, invariants) and,
+for the prologue, by ``tests/test_oracle_prologue.py`` (closed-form values,
+symmetries, and end-to-end reductions to runs with known gates).
 """
 from __future__ import annotations
 
@@ -63,8 +73,8 @@ def max_threads() -> int:
     return int(lib().kda_oracle_max_threads())
 
 
-def _f32(a):
-    return np.ascontiguousarray(a, dtype=np.float32)
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
 
 
 def _p(a):
@@ -77,12 +87,12 @@ def forward(q, k, v, g, beta, cu_seqlens, s0=None, cols: Optional[Sequence[int]]
 
     q, k: [total, H, Dk]; v: [total, H, Dv]; g (log alpha, unclamped): [total, H, Dk];
     beta: [total, H]; cu_seqlens: [N+1]; s0: [N, H, Dk, Dv] or None.
-    Inputs are taken as float32 (bf16 values upcast exactly beforehand).
+    Inputs are taken as float64 (bf16 and fp32 values upcast exactly beforehand).
     cols: d_v columns to compute (default: all).
     Returns (o [total, H, ncols] float64, s_final [N, H, Dk, ncols] float64 or None).
     """
-    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(g)
-    beta = _f32(beta)
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    beta = _f64(beta)
     total, H, Dk = q.shape
     Dv = v.shape[2]
     if k.shape != (total, H, Dk) or g.shape != (total, H, Dk) or v.shape[:2] != (total, H) \
@@ -107,8 +117,44 @@ def forward(q, k, v, g, beta, cu_seqlens, s0=None, cols: Optional[Sequence[int]]
     return o, sf
 
 
+def softplus(x):
+    """ln(1 + e^x), evaluated as max(x, 0) + ln(1 + e^-|x|) so that no exponential overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), evaluated through e^-|x| so that no exponential overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def unit_rows(x):
+    """x / ||x|| along the last axis; an all-zero vector stays zero."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def prologue(q, k, g, beta, g_logit=False, beta_logit=False, qk_l2norm=False):
+    """The recurrence's inputs (fp64) from raw ones: log alpha = -softplus(g) for gate logits,
+    beta = sigmoid(beta) for beta logits, q and k scaled to unit length per token and head."""
+    q, k, g, beta = _f64(q), _f64(k), _f64(g), _f64(beta)
+    if g_logit:
+        g = -softplus(g)
+    if beta_logit:
+        beta = sigmoid(beta)
+    if qk_l2norm:
+        q, k = unit_rows(q), unit_rows(k)
+    return q, k, g, beta
+
+
 def forward_inputs(inp, cols=None, want_state=True, nthreads=0):
-    """Oracle on a ``kda_inputs.Inputs`` bundle."""
-    return forward(inp.as_f32("q"), inp.as_f32("k"), inp.as_f32("v"), inp.g, inp.beta, inp.cu_seqlens,
+    """Oracle on a ``kda_inputs.Inputs`` bundle (its prologue flags applied first)."""
+    sp = inp.spec
+    q, k, g, beta = prologue(inp.as_f32("q"), inp.as_f32("k"), inp.as_f32("g"), inp.as_f32("beta"),
+                             g_logit=sp.g_logit, beta_logit=sp.beta_logit, qk_l2norm=sp.qk_l2norm)
+    return forward(q, k, inp.as_f32("v"), g, beta, inp.cu_seqlens,
                    s0=None if inp.s0 is None else inp.s0.astype(np.float64), cols=cols,
                    want_state=want_state, nthreads=nthreads)

@@ -43,23 +43,23 @@
 #define ORACLE_COL_BLOCK 16
 
 /* alpha = exp(clamp(g, -5, 0)): the forget gate kept inside [e^-5, 1]. */
-static double forget_gate(float g) {
-    double x = (double)g;
+static double forget_gate(double g) {
+    double x = g;
     if (x < -5.0) x = -5.0;
     if (x > 0.0) x = 0.0;
     return exp(x);
 }
 
 /*
- * q, k: [total, H, Dk] float32; v: [total, H, Dv] float32;
- * g: [total, H, Dk] float32 (log alpha, clamped here); beta: [total, H] float32;
+ * q, k: [total, H, Dk] double; v: [total, H, Dv] double;
+ * g: [total, H, Dk] double (log alpha, clamped here); beta: [total, H] double;
  * s0: [N, H, Dk, Dv] double or NULL (zero state);
  * cu_seqlens: [N+1] int64, sequence n covers tokens cu[n] .. cu[n+1]-1;
  * cols: [ncols] d_v column indices to compute (each in [0, Dv));
  * o: [total, H, ncols] double; s_final: [N, H, Dk, ncols] double or NULL.
  * Returns 0, or -1 on a bad argument.
  */
-int kda_oracle_forward(const float* q, const float* k, const float* v, const float* g, const float* beta,
+int kda_oracle_forward(const double* q, const double* k, const double* v, const double* g, const double* beta,
                        const double* s0, const int64_t* cu_seqlens, int64_t N, int64_t H, int64_t Dk,
                        int64_t Dv, const int32_t* cols, int64_t ncols, double* o, double* s_final,
                        int nthreads) {
@@ -101,10 +101,10 @@ int kda_oracle_forward(const float* q, const float* k, const float* v, const flo
                 S[i * nc + j] = s0 ? s0[((n * H + h) * Dk + i) * Dv + cols[c0 + j]] : 0.0;
 
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
-            const float* qt = q + (t * H + h) * Dk;
-            const float* kt = k + (t * H + h) * Dk;
-            const float* vt = v + (t * H + h) * Dv;
-            const float* gt = g + (t * H + h) * Dk;
+            const double* qt = q + (t * H + h) * Dk;
+            const double* kt = k + (t * H + h) * Dk;
+            const double* vt = v + (t * H + h) * Dv;
+            const double* gt = g + (t * H + h) * Dk;
             double bt = (double)beta[t * H + h];
             for (int64_t i = 0; i < Dk; ++i) alpha[i] = forget_gate(gt[i]);
             /* forget: S <- Diag(alpha) S */

@@ -43,7 +43,7 @@ def last_error():
 
 def chunk(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, s_final=None, B=1, T=64, H=1, Dk=128,
-             Dv=128, chunk=64, dtype=1, workspace=None, workspace_bytes=0, stream=None)
+             Dv=128, chunk=64, dtype=1, prologue=None, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return kda.chunk_fwd_raw(*a.values())
 
@@ -71,7 +71,7 @@ def test_chunk_nothing_to_do_returns_ok():
 
 def varlen(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, N=2, total=100, s0=None, o=FAKE, s_final=None, H=2,
-             Dk=128, Dv=128, chunk=64, dtype=1, workspace=None, workspace_bytes=0, stream=None)
+             Dk=128, Dv=128, chunk=64, dtype=1, prologue=None, workspace=None, workspace_bytes=0, stream=None)
     a.update(kw)
     return kda.varlen_fwd_raw(*a.values())
 
@@ -148,7 +148,7 @@ def test_varlen_nothing_to_do():
 
 def decode(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s_in=FAKE, s_out=FAKE, o=FAKE, B=4, H=2, Dk=128, Dv=128,
-             dtype=1, stream=None)
+             dtype=1, prologue=None, stream=None)
     a.update(kw)
     return kda.decode_step_raw(*a.values())
 
@@ -181,3 +181,20 @@ def test_error_is_thread_local():
     t.start()
     t.join()
     assert seen == [""] and "Dk" in last_error()
+
+
+def test_prologue_validation():
+    import ctypes
+    bad = ctypes.pointer(kda.Prologue(5, 0, 0, 0, 0))
+    assert chunk(prologue=bad) == 3 and "g_dtype" in last_error()
+    bad = ctypes.pointer(kda.Prologue(0, 1, 9, 0, 0))
+    assert varlen(prologue=bad) == 3 and "beta_dtype" in last_error()
+    assert decode(prologue=bad) == 3 and "beta_dtype" in last_error()
+
+
+def test_prologue_struct_defaults_to_none():
+    import torch
+    assert kda.prologue() is None
+    p = kda.prologue(torch.bfloat16, True, torch.float32, False, True)
+    assert (p.contents.g_dtype, p.contents.g_logit, p.contents.beta_dtype, p.contents.beta_logit,
+            p.contents.qk_l2norm) == (1, 1, 0, 0, 1)

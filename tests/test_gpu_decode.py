@@ -20,7 +20,8 @@ def run_decode(inp, inplace=False):
     g = to_dev(inp.g, (B, H, sp.Dk))
     beta = to_dev(inp.beta, (B, H))
     st = to_dev(inp.s0)
-    o, s1 = kda.decode_step(q, k, v, g, beta, st, inplace=inplace)
+    o, s1 = kda.decode_step(q, k, v, g, beta, st, inplace=inplace, g_logit=sp.g_logit, beta_logit=sp.beta_logit,
+                            qk_l2norm=sp.qk_l2norm)
     torch.cuda.synchronize()
     return o.cpu().numpy(), s1.cpu().numpy(), st
 

@@ -21,13 +21,20 @@ pytestmark = pytest.mark.gpu
 PATHS = pytest.mark.parametrize("fused", [False, True], ids=["two_pass", "fused"])
 
 
+def prologue_flags(spec):
+    """The input prologue that the spec's raw input forms call for."""
+    return dict(g_logit=spec.g_logit, beta_logit=spec.beta_logit, qk_l2norm=spec.qk_l2norm)
+
+
 def run_chunk(inp, batched=True, fused=False, workspace=None):
     d = device_inputs(inp, batched)
+    fl = prologue_flags(inp.spec)
     if batched:
-        o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=fused, workspace=workspace)
+        o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=fused, workspace=workspace,
+                              **fl)
     else:
         o, sf = kda.varlen_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["s0"], fused=fused,
-                               workspace=workspace)
+                               workspace=workspace, **fl)
     torch.cuda.synchronize()
     sp = inp.spec
     return o.reshape(sp.total, sp.H, sp.Dv).cpu().numpy(), sf.cpu().numpy()
@@ -259,7 +266,7 @@ def test_s_final_may_alias_s0(fused):
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     rc = kda.chunk_fwd_raw(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["g"].data_ptr(),
                            d["beta"].data_ptr(), st.data_ptr(), o2.data_ptr(), st.data_ptr(), 2, 130, 2, 128, 128,
-                           64, kda.DTYPE[torch.bfloat16], None if fused else ws.data_ptr(), nws,
+                           64, kda.DTYPE[torch.bfloat16], None, None if fused else ws.data_ptr(), nws,
                            torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert rc == 0 and torch.equal(st, sf) and torch.equal(o2, o)
