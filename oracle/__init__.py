@@ -57,6 +57,8 @@ def load(path: str):
                                      ctypes.c_int]
     L.kda_oracle_forward.restype = ctypes.c_int
     L.kda_oracle_max_threads.restype = ctypes.c_int
+    L.kda_oracle_backward.argtypes = [vp] * 8 + [vp, i64, i64, i64, i64] + [vp] * 6 + [ctypes.c_int]
+    L.kda_oracle_backward.restype = ctypes.c_int
     return L
 
 
@@ -115,6 +117,30 @@ def forward(q, k, v, g, beta, cu_seqlens, s0=None, cols: Optional[Sequence[int]]
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed ({rc})")
     return o, sf
+
+
+def backward(q, k, v, g, beta, cu_seqlens, d_o, s0=None, d_sfinal=None, nthreads: int = 0, _lib=None):
+    """Gradients of L with dL/do = d_o and dL/dS_T = d_sfinal (None = 0), in fp64.
+
+    Shapes as for ``forward``; d_o: [total, H, Dv]; d_sfinal: [N, H, Dk, Dv] or None.
+    Returns dict(dq, dk, dv, dg, dbeta, ds0) (dg is with respect to g = log alpha before the clamp)."""
+    q, k, v, g, beta, d_o = _f64(q), _f64(k), _f64(v), _f64(g), _f64(beta), _f64(d_o)
+    total, H, Dk = q.shape
+    Dv = v.shape[2]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    if cu[0] != 0 or cu[-1] != total or d_o.shape != (total, H, Dv):
+        raise ValueError("shape mismatch")
+    s0 = None if s0 is None else _f64(s0)
+    d_sfinal = None if d_sfinal is None else _f64(d_sfinal)
+    out = dict(dq=np.zeros((total, H, Dk)), dk=np.zeros((total, H, Dk)), dv=np.zeros((total, H, Dv)),
+               dg=np.zeros((total, H, Dk)), dbeta=np.zeros((total, H)), ds0=np.zeros((N, H, Dk, Dv)))
+    rc = (_lib or lib()).kda_oracle_backward(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(s0), _p(d_o), _p(d_sfinal),
+                                             _p(cu), N, H, Dk, Dv, _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
+                                             _p(out["dg"]), _p(out["dbeta"]), _p(out["ds0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed ({rc})")
+    return out
 
 
 def softplus(x):
