@@ -97,7 +97,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
-    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m", "raw_gates"], default=None,
+    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m", "raw_gates", "backward"],
+                    default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
@@ -136,6 +137,9 @@ def main():
         return
     if args.only == "prefill_1m":
         print(json.dumps({"prefill_1m": measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)}))
+        return
+    if args.only == "backward":
+        print(json.dumps({"backward": measure_backward(args, torch, kda, kda_inputs, device_inputs)}))
         return
     if args.only == "raw_gates":
         print(json.dumps({"raw_gates": measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)}))
@@ -201,6 +205,7 @@ def main():
         line["varlen"] = measure_varlen(args, torch, kda, kda_inputs, device_inputs)
         line["prefill_1m"] = measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)
         line["raw_gates"] = measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)
+        line["backward"] = measure_backward(args, torch, kda, kda_inputs, device_inputs)
 
     if args.only is None and not args.no_cpu_baseline:
         import oracle
@@ -313,6 +318,30 @@ def measure_raw_gates(args, torch, kda, kda_inputs, device_inputs):
     return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg}
+
+
+def measure_backward(args, torch, kda, kda_inputs, device_inputs):
+    """Gradients of the B=4 H=16 T=8192 d=128 bf16 batch (seeded d_o, no final-state term)."""
+    name = "chunk_b4_h16_t8192_d128_bf16"
+    spec = kda_inputs.workload(name)
+    inp = kda_inputs.generate(spec)
+    d = device_inputs(inp, batched=True)
+    B, T, H, Dk, Dv = spec.n_seq, spec.lengths[0], spec.H, spec.Dk, spec.Dv
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    d_o = torch.randn((B, T, H, Dv), device="cuda", generator=gen)
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(B, T, H, Dk, Dv), dtype=torch.uint8, device="cuda")
+
+    def bstep():
+        kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d["s0"], None, workspace=ws)
+
+    _, k_ms, k_min = time_launches(bstep, max(5, args.steps // 5), min(args.warmup, 2), torch)
+    # reads q, k, v (bf16), g, beta, d_o (fp32); writes dq, dk, dv, dg, dbeta (fp32) and ds0
+    n_ht = B * T * H
+    alg = n_ht * ((2 * Dk + Dv) * 2 + 4 * Dk + 4 + 4 * Dv + 4 * (3 * Dk + Dv) + 4) + B * H * Dk * Dv * 4
+    return {"workload": name + "_backward", "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+            "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
+            "workspace_bytes": ws.numel(), "arith": "fp32"}
 
 
 if __name__ == "__main__":

@@ -26,7 +26,8 @@ import torch
 
 __all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
            "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "chunk_workspace_bytes",
-           "varlen_workspace_bytes", "DTYPE", "Prologue", "prologue"]
+           "varlen_workspace_bytes", "DTYPE", "Prologue", "prologue", "chunk_bwd", "varlen_bwd", "chunk_bwd_raw",
+           "varlen_bwd_raw", "chunk_bwd_workspace_bytes", "varlen_bwd_workspace_bytes", "ChunkKDA"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -85,6 +86,14 @@ def load_library():
     L.kda_varlen_workspace_bytes.restype = sz
     L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, ci, ci, ci, ci, pp, vp]
     L.kda_decode_step.restype = ci
+    L.kda_chunk_bwd.argtypes = [vp] * 14 + [i64, i64, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.kda_chunk_bwd.restype = ci
+    L.kda_varlen_bwd.argtypes = [vp] * 6 + [i64, i64] + [vp] * 9 + [ci, ci, ci, ci, ci, vp, sz, vp]
+    L.kda_varlen_bwd.restype = ci
+    L.kda_chunk_bwd_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
+    L.kda_chunk_bwd_workspace_bytes.restype = sz
+    L.kda_varlen_bwd_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
+    L.kda_varlen_bwd_workspace_bytes.restype = sz
     L.kda_last_error.restype = ctypes.c_char_p
     L.kda_version.restype = ctypes.c_char_p
     _lib = L
@@ -124,6 +133,26 @@ def varlen_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int, dtype=t
 
 def decode_step_raw(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, prologue, stream) -> int:
     return load_library().kda_decode_step(q, k, v, g, beta, s_in, s_out, o, B, H, Dk, Dv, dtype, prologue, stream)
+
+
+def chunk_bwd_raw(q, k, v, g, beta, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta, ds0, B, T, H, Dk, Dv, chunk, dtype,
+                  workspace, workspace_bytes, stream) -> int:
+    return load_library().kda_chunk_bwd(q, k, v, g, beta, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta, ds0, B, T, H, Dk,
+                                        Dv, chunk, dtype, workspace, workspace_bytes, stream)
+
+
+def varlen_bwd_raw(q, k, v, g, beta, cu, N, total, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta, ds0, H, Dk, Dv, chunk,
+                   dtype, workspace, workspace_bytes, stream) -> int:
+    return load_library().kda_varlen_bwd(q, k, v, g, beta, cu, N, total, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta,
+                                         ds0, H, Dk, Dv, chunk, dtype, workspace, workspace_bytes, stream)
+
+
+def chunk_bwd_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, dtype=torch.bfloat16) -> int:
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, _dtype_code(dtype)))
+
+
+def varlen_bwd_workspace_bytes(N: int, total: int, H: int, Dk: int, Dv: int, dtype=torch.bfloat16) -> int:
+    return int(load_library().kda_varlen_bwd_workspace_bytes(N, total, H, Dk, Dv, _dtype_code(dtype)))
 
 
 # ----------------------------------------------------------------- torch front end
@@ -269,3 +298,106 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
         _check(decode_step_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out_state),
                                _ptr(o), B, H, Dk, Dv, DTYPE[q.dtype], pro, _stream(q.device)))
     return o, out_state
+
+
+def _bwd_workspace(need: int, workspace: Optional[torch.Tensor], device) -> Tuple[Optional[torch.Tensor], int]:
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    else:
+        _need(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              d_o: torch.Tensor, s0: Optional[torch.Tensor] = None, d_sfinal: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """Gradients of :func:`chunk_fwd` (g = log alpha and beta as given, fp32) for dL/do = d_o and
+    dL/dS_T = d_sfinal (None = 0).  Returns dq, dk, dv, dg, dbeta, ds0 (all fp32); dg is with respect
+    to g before the clamp."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(g, "g", torch.float32, (B, T, H, Dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    _need(d_o, "d_o", torch.float32, (B, T, H, Dv))
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
+    if d_sfinal is not None:
+        _need(d_sfinal, "d_sfinal", torch.float32, (B, H, Dk, Dv))
+    f = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dg = (torch.empty((B, T, H, Dk), **f) for _ in range(3))
+    dv = torch.empty((B, T, H, Dv), **f)
+    dbeta = torch.empty((B, T, H), **f)
+    ds0 = torch.empty((B, H, Dk, Dv), **f)
+    ws, ws_bytes = _bwd_workspace(chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, q.dtype), workspace, q.device)
+    with torch.cuda.device(q.device):
+        _check(chunk_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(d_o), _ptr(d_sfinal),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0), B, T, H, Dk, Dv, 64,
+                             DTYPE[q.dtype], _ptr(ws), ws_bytes, _stream(q.device)))
+    return dq, dk, dv, dg, dbeta, ds0
+
+
+def varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+               cu_seqlens: torch.Tensor, d_o: torch.Tensor, s0: Optional[torch.Tensor] = None,
+               d_sfinal: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients of :func:`varlen_fwd`; layouts as there, results as for :func:`chunk_bwd`."""
+    if q.dim() != 3:
+        raise ValueError("q must be [total, H, Dk]")
+    total, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (total, H, Dk))
+    _need(v, "v", q.dtype, (total, H, Dv))
+    _need(g, "g", torch.float32, (total, H, Dk))
+    _need(beta, "beta", torch.float32, (total, H))
+    _need(d_o, "d_o", torch.float32, (total, H, Dv))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (N, H, Dk, Dv))
+    if d_sfinal is not None:
+        _need(d_sfinal, "d_sfinal", torch.float32, (N, H, Dk, Dv))
+    f = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dg = (torch.empty((total, H, Dk), **f) for _ in range(3))
+    dv = torch.empty((total, H, Dv), **f)
+    dbeta = torch.empty((total, H), **f)
+    ds0 = torch.empty((N, H, Dk, Dv), **f)
+    ws, ws_bytes = _bwd_workspace(varlen_bwd_workspace_bytes(N, total, H, Dk, Dv, q.dtype), workspace, q.device)
+    with torch.cuda.device(q.device):
+        _check(varlen_bwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, total, _ptr(s0),
+                              _ptr(d_o), _ptr(d_sfinal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                              _ptr(ds0), H, Dk, Dv, 64, DTYPE[q.dtype], _ptr(ws), ws_bytes, _stream(q.device)))
+    return dq, dk, dv, dg, dbeta, ds0
+
+
+class ChunkKDA(torch.autograd.Function):
+    """Autograd wrapper: ``o, s_final = ChunkKDA.apply(q, k, v, g, beta, s0)`` with the forward and
+    backward both in the library's kernels.  Gradients of q, k, v come back in fp32 and are cast
+    to the input type; s0 may be None."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, s0=None):
+        o, sf = chunk_fwd(q, k, v, g, beta, s0)
+        ctx.save_for_backward(q, k, v, g, beta, s0)
+        return o, sf
+
+    @staticmethod
+    def backward(ctx, d_o, d_sf):
+        q, k, v, g, beta, s0 = ctx.saved_tensors
+        d_o = torch.zeros_like(q[..., :1].float()).expand(*q.shape[:-1], v.shape[-1]).contiguous() \
+            if d_o is None else d_o.float().contiguous()
+        d_sf = None if d_sf is None else d_sf.float().contiguous()
+        dq, dk, dv, dg, dbeta, ds0 = chunk_bwd(q, k, v, g, beta, d_o, s0, d_sf)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dg, dbeta, (ds0 if s0 is not None else None)

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk2.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk2.hip", "kda_decode.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -168,6 +168,99 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     return launched(kda::launch_decode(a, static_cast<hipStream_t>(stream)), "kda_decode_step");
 }
 
+static kda_status run_bwd(const kda::BwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st,
+                          const char* what) {
+    if (a.N * (int64_t)a.H > 0x7fffffffLL / 4)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: %lld sequence-heads exceed the grid limit", what, (long long)(a.N * a.H));
+    if (kda::bwd_slots(a) * a.H > 0x7fffffffLL)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: %lld chunk-heads exceed the grid limit", what,
+                    (long long)(kda::bwd_slots(a) * a.H));
+    const int64_t need = kda::bwd_workspace_bytes(a);
+    if (need > 0 && !workspace) return fail(KDA_ERR_NULL_ARG, "%s: workspace is NULL (%lld bytes needed)", what,
+                                            (long long)need);
+    if ((uint64_t)need > (uint64_t)workspace_bytes)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: workspace holds %llu bytes, %lld needed", what,
+                    (unsigned long long)workspace_bytes, (long long)need);
+    return launched(kda::launch_bwd(a, workspace, st), what);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* s0, const float* d_o, const float* d_sfinal, float* dq, float* dk, float* dv,
+                         float* dg, float* dbeta, float* ds0, int64_t B, int64_t T, int H, int Dk, int Dv, int chunk,
+                         kda_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
+    if (B < 0 || T < 0) return fail(KDA_ERR_BAD_SHAPE, "B and T must be >= 0");
+    if (T > 0 && B > INT64_MAX / T) return fail(KDA_ERR_BAD_SHAPE, "B*T overflows");
+    const bool tokens = B > 0 && T > 0;
+    if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
+                          {beta, "beta", tokens}, {d_o, "d_o", tokens}, {dq, "dq", tokens}, {dk, "dk", tokens},
+                          {dv, "dv", tokens}, {dg, "dg", tokens}, {dbeta, "dbeta", tokens}, {s0, "s0", false},
+                          {d_sfinal, "d_sfinal", false}, {ds0, "ds0", false}, {workspace, "workspace", false}})) !=
+        KDA_OK)
+        return st;
+    if (B == 0 || (!tokens && !ds0)) return ok();
+    kda::BwdArgs a{q, k, v, g, beta, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta, ds0, nullptr, T, B * T, B, H, Dk, Dv,
+                   dtype == KDA_F32};
+    return run_bwd(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_chunk_bwd");
+}
+
+kda_status kda_varlen_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, const float* d_o,
+                          const float* d_sfinal, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* ds0,
+                          int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    kda_status st;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
+    if (N < 0 || total < 0) return fail(KDA_ERR_BAD_SHAPE, "N and total must be >= 0");
+    if (total > 0x7fffffffLL) return fail(KDA_ERR_BAD_SHAPE, "total exceeds the int32 range of cu_seqlens");
+    const bool tokens = total > 0;
+    if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL_ARG, "cu_seqlens is NULL");
+    if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
+                          {beta, "beta", tokens}, {d_o, "d_o", tokens}, {dq, "dq", tokens}, {dk, "dk", tokens},
+                          {dv, "dv", tokens}, {dg, "dg", tokens}, {dbeta, "dbeta", tokens}, {s0, "s0", false},
+                          {d_sfinal, "d_sfinal", false}, {ds0, "ds0", false}, {workspace, "workspace", false}})) !=
+        KDA_OK)
+        return st;
+    if (N == 0 || (!tokens && !ds0)) return ok();
+    kda::BwdArgs a{q, k, v, g, beta, s0, d_o, d_sfinal, dq, dk, dv, dg, dbeta, ds0, cu_seqlens, 0, total, N, H, Dk,
+                   Dv, dtype == KDA_F32};
+    return run_bwd(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), "kda_varlen_bwd");
+}
+
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype) {
+    if (B <= 0 || T < 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    kda::BwdArgs a{};
+    a.f32 = dtype == KDA_F32;
+    a.T_fixed = T;
+    a.N = B;
+    a.total = B * T;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    return (size_t)kda::bwd_workspace_bytes(a);
+}
+
+size_t kda_varlen_bwd_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv, kda_dtype dtype) {
+    if (N <= 0 || total < 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    kda::BwdArgs a{};
+    a.f32 = dtype == KDA_F32;
+    static const int32_t dummy = 0;
+    a.cu_seqlens = &dummy;  // only its presence matters for the size
+    a.N = N;
+    a.total = total;
+    a.H = H;
+    a.Dk = Dk;
+    a.Dv = Dv;
+    return (size_t)kda::bwd_workspace_bytes(a);
+}
+
 size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype) {
     if (B <= 0 || T <= 0 || H < 1 || (Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
@@ -199,6 +292,6 @@ size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int D
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
-const char* kda_version(void) { return "kda-gfx950 0.3"; }
+const char* kda_version(void) { return "kda-gfx950 0.4"; }
 
 }  // extern "C"

@@ -46,4 +46,18 @@ int64_t chunk_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
+// Backward pass (kda_bwd.hip): gradients of o and the final state.
+struct BwdArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *s0, *d_o, *d_sfinal;
+    float *dq, *dk, *dv, *dg, *dbeta, *ds0;
+    const int32_t* cu_seqlens;  // device offsets, or nullptr for equal-length sequences
+    int64_t T_fixed, total, N;
+    int H, Dk, Dv;
+    bool f32;
+};
+int64_t bwd_slots(const BwdArgs& a);
+int64_t bwd_workspace_bytes(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a, void* ws, hipStream_t st);
+
 }  // namespace kda

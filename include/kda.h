@@ -164,6 +164,44 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const float* s_in, float* s_out, float* o, int64_t B, int H, int Dk, int Dv,
                            kda_dtype dtype, const kda_prologue* prologue, void* stream);
 
+/*
+ * Gradients of kda_chunk_fwd (no prologue: g is log alpha and beta is used as given, both
+ * float32).  The pages describe only the forward recurrence; these are its exact derivatives,
+ * for a loss L with dL/do = d_o and dL/dS_T = d_sfinal:
+ *   d_o      : [B, T, H, Dv] float32;   d_sfinal : [B, H, Dk, Dv] float32, or NULL for zero
+ *   dq, dk   : [B, T, H, Dk] float32;   dv : [B, T, H, Dv] float32   (written)
+ *   dg       : [B, T, H, Dk] float32, gradient with respect to g before the clamp: zero where
+ *              g < -5 or g > 0 (the clamp passes the gradient on [-5, 0])   (written)
+ *   dbeta    : [B, T, H] float32 (written)
+ *   ds0      : [B, H, Dk, Dv] float32 gradient of the initial state (written), or NULL
+ * q, k, v, g, beta, s0 as for kda_chunk_fwd (s0 NULL = zero initial state).  The workspace is
+ * required (kda_chunk_bwd_workspace_bytes; no initial contents needed); a NULL or smaller one is
+ * rejected.  The computation runs in float32 throughout.  T = 0: only ds0 = d_sfinal (or 0).
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* s0, const float* d_o, const float* d_sfinal, float* dq, float* dk, float* dv,
+                         float* dg, float* dbeta, float* ds0, int64_t B, int64_t T, int H, int Dk, int Dv, int chunk,
+                         kda_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes kda_chunk_bwd needs: B * ceil(T/64) * H records of
+ * 4 * (386*Dk + 20544 + 2*Dk*Dv) bytes (401.25 KiB at Dk = Dv = 128).
+ */
+size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype);
+
+/*
+ * Gradients of kda_varlen_fwd: the packed layouts of kda_varlen_fwd, the outputs as for
+ * kda_chunk_bwd ([total, H, D] for the token tensors, [N, H, Dk, Dv] for d_sfinal and ds0).
+ */
+kda_status kda_varlen_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int64_t N, int64_t total, const float* s0, const float* d_o,
+                          const float* d_sfinal, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* ds0,
+                          int H, int Dk, int Dv, int chunk, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes kda_varlen_bwd needs: (floor(total/64) + N) * H records as above. */
+size_t kda_varlen_bwd_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv, kda_dtype dtype);
+
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 const char* kda_last_error(void);
 
