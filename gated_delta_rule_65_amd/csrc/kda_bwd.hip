@@ -20,9 +20,9 @@
 //   then through Abar, P, Qt, Kt, Kb and gamma to q, k and G, and from G to g by a reverse
 //   running sum inside the chunk (the clamp passes the gradient where -5 <= g <= 0).
 //
-// Five kernels, fp32 arithmetic throughout, 256 threads each:
-//   bwd_prep_kernel    per (chunk, head): Qt, Kt, Kb, P, Minv, Abar, gamma, b -> workspace records
-//   bwd_states_kernel  per (sequence, head, 32 state columns): the state at every chunk start
+// Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) and the state at every chunk start come from
+// the forward pass's prep kernel in its backward form and its chain kernel in mode 3, both with fp32
+// records (launch_chunk_states).  Then three kernels, fp32 arithmetic, 256 threads each:
 //   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS' of every chunk, ds0
 //   bwd_grad_a_kernel  per (chunk, head): dv and the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma)
 //   bwd_grad_b_kernel  per (chunk, head): through the inverse, the decayed Gram blocks and the gates
@@ -38,13 +38,8 @@ namespace {
 constexpr int kBC = 64;  // tokens per chunk
 constexpr int kBS = 32;  // state columns per chain workgroup
 
-// Per (chunk, head) record of bwd_prep (float offsets): row-major [64][DK] and [64][64] matrices.
 template <int DK>
-struct BRec {
-    static constexpr int QT = 0, KT = 64 * DK, KB = 128 * DK, PM = 192 * DK, MI = PM + 4096, AB = MI + 4096,
-                         GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
-    static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
-};
+using BRec = BwdRec<DK>;
 // Per (chunk, head) output of bwd_grad_a (float offsets).
 template <int DK>
 struct GRec {
@@ -117,185 +112,6 @@ __device__ __forceinline__ bool chain_item(int64_t items, int NS, int64_t& pr, i
 }
 
 }  // namespace
-
-// ============================================================================ per-chunk operands
-
-template <int DK, bool F32>
-__global__ __launch_bounds__(256, 1) void bwd_prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
-                                                          const float* __restrict__ g, const float* __restrict__ beta,
-                                                          const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                          int64_t total, int64_t N, int H, float* __restrict__ recs) {
-    using R = BRec<DK>;
-    constexpr int LD = DK + 1;
-    __shared__ float sq[64 * LD], sk[64 * LD], sG[64 * LD], sA[64 * 65], sMI[64 * 65], sB[64];
-    const int tid = threadIdx.x;
-    const int64_t slot = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
-    int64_t n, t0;
-    int nt;
-    if (!slot_chunk(cu, slot, T_fixed, total, N, n, t0, nt)) return;
-    float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
-
-    // rows past the end: q = k = 0, g = 0, b = 0
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        float x = 0.f, y = 0.f, z = 0.f;
-        if (r < nt) {
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
-            x = load_in<F32>(qv, idx);
-            y = load_in<F32>(kv, idx);
-            z = fminf(fmaxf(g[idx], -5.f), 0.f);
-        }
-        sq[r * LD + c] = x;
-        sk[r * LD + c] = y;
-        sG[r * LD + c] = z;
-    }
-    if (tid < 64) sB[tid] = tid < nt ? beta[(t0 + tid) * H + h] : 0.f;
-    __syncthreads();
-    if (tid < DK) {  // running sums down each key channel
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            acc += sG[r * LD + tid];
-            sG[r * LD + tid] = acc;
-        }
-    }
-    __syncthreads();
-
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        const float G = sG[r * LD + c], GC = sG[63 * LD + c];
-        const float gam = __expf(G);
-        rec[R::QT + e] = sq[r * LD + c] * gam;
-        rec[R::KT + e] = sk[r * LD + c] * gam;
-        rec[R::KB + e] = sk[r * LD + c] * __expf(GC - G);
-    }
-    if (tid < DK) rec[R::GM + tid] = __expf(sG[63 * LD + tid]);
-    if (tid < 64) rec[R::BT + tid] = sB[tid];
-
-    // decayed Gram blocks: Abar (strictly lower), P (lower with the diagonal)
-    for (int pi = tid; pi < 4096; pi += 256) {
-        const int r = pi >> 6, i = pi & 63;
-        float a = 0.f, p = 0.f;
-        if (i <= r) {
-            for (int c = 0; c < DK; ++c) {
-                const float ke = sk[i * LD + c] * __expf(sG[r * LD + c] - sG[i * LD + c]);
-                a = fmaf(sk[r * LD + c], ke, a);
-                p = fmaf(sq[r * LD + c], ke, p);
-            }
-        }
-        if (i == r) a = 0.f;
-        sA[r * 65 + i] = a;
-        rec[R::AB + pi] = a;
-        rec[R::PM + pi] = p;
-    }
-    __syncthreads();
-
-    // Minv = (I + Diag(b) Abar)^{-1} by forward substitution, one column per thread
-    if (tid < 64) {
-        const int i = tid;
-        for (int r = 0; r < 64; ++r) {
-            float x;
-            if (r < i) {
-                x = 0.f;
-            } else if (r == i) {
-                x = 1.f;
-            } else {
-                float s = 0.f;
-                for (int s2 = i; s2 < r; ++s2) s = fmaf(sA[r * 65 + s2], sMI[s2 * 65 + i], s);
-                x = -sB[r] * s;
-            }
-            sMI[r * 65 + i] = x;
-        }
-    }
-    __syncthreads();
-    for (int pi = tid; pi < 4096; pi += 256) rec[R::MI + pi] = sMI[(pi >> 6) * 65 + (pi & 63)];
-}
-
-// ============================================================================ states at chunk starts
-
-template <int DK, bool F32>
-__global__ __launch_bounds__(256, 1) void bwd_states_kernel(const void* __restrict__ vv, const float* __restrict__ s0,
-                                                            const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                            int64_t total, int64_t N, int H, int Dv,
-                                                            const float* __restrict__ recs, float* __restrict__ states) {
-    using R = BRec<DK>;
-    constexpr int LD = DK + 1;
-    constexpr int TPC = 256 / DK, CPT = kBS / TPC;  // threads per state row, columns per thread
-    __shared__ float sS[DK * kBS], sKt[64 * LD], sKb[64 * LD], sMI[64 * 65], sX[64 * kBS], sU[64 * kBS], sB[64],
-        sGm[DK];
-    const int tid = threadIdx.x;
-    int64_t pr;
-    int sl;
-    if (!chain_item(N * (int64_t)H, Dv / kBS, pr, sl)) return;
-    const int64_t n = pr / H;
-    const int h = (int)(pr % H);
-    const BSeq sr = bseq(cu, n, T_fixed, total);
-    const int64_t nch = (sr.end - sr.start + kBC - 1) / kBC;
-    const int col0 = sl * kBS;
-
-    for (int e = tid; e < DK * kBS; e += 256) {
-        const int c = e / kBS, jj = e % kBS;
-        sS[e] = s0 ? s0[((n * H + h) * DK + c) * (int64_t)Dv + col0 + jj] : 0.f;
-    }
-    __syncthreads();
-    const int xr = tid >> 2, xj = (tid & 3) * 8;               // X, U: row, 8 columns
-    const int sc = tid / TPC, sj = (tid % TPC) * CPT;          // S: row, CPT columns
-    for (int64_t jc = 0; jc < nch; ++jc) {
-        const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
-        const float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
-        float* st = states + (slot * H + h) * (int64_t)DK * Dv;
-        const int64_t t0 = sr.start + jc * kBC;
-        const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        for (int e = tid; e < DK * kBS; e += 256) st[(e / kBS) * (int64_t)Dv + col0 + e % kBS] = sS[e];
-        for (int e = tid; e < 64 * DK; e += 256) {
-            sKt[(e / DK) * LD + e % DK] = rec[R::KT + e];
-            sKb[(e / DK) * LD + e % DK] = rec[R::KB + e];
-        }
-        for (int e = tid; e < 4096; e += 256) sMI[(e >> 6) * 65 + (e & 63)] = rec[R::MI + e];
-        if (tid < 64) sB[tid] = rec[R::BT + tid];
-        if (tid < DK) sGm[tid] = rec[R::GM + tid];
-        for (int e = tid; e < 64 * kBS; e += 256) {
-            const int r = e / kBS;
-            sX[e] = r < nt ? load_in<F32>(vv, ((t0 + r) * H + h) * (int64_t)Dv + col0 + e % kBS) : 0.f;
-        }
-        __syncthreads();
-        {  // X = V - Kt S
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < DK; ++c) {
-                const float kt = sKt[xr * LD + c];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) acc[m] = fmaf(kt, sS[c * kBS + xj + m], acc[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) sX[xr * kBS + xj + m] -= acc[m];
-        }
-        __syncthreads();
-        {  // U = Minv Diag(b) X
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i <= xr; ++i) {
-                const float wgt = sMI[xr * 65 + i] * sB[i];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) acc[m] = fmaf(wgt, sX[i * kBS + xj + m], acc[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) sU[xr * kBS + xj + m] = acc[m];
-        }
-        __syncthreads();
-        {  // S = Diag(gamma) S + Kb^T U
-            float acc[CPT];
-#pragma unroll
-            for (int m = 0; m < CPT; ++m) acc[m] = sGm[sc] * sS[sc * kBS + sj + m];
-            for (int r = 0; r < 64; ++r) {
-                const float kb = sKb[r * LD + sc];
-#pragma unroll
-                for (int m = 0; m < CPT; ++m) acc[m] = fmaf(kb, sU[r * kBS + sj + m], acc[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < CPT; ++m) sS[sc * kBS + sj + m] = acc[m];
-        }
-        __syncthreads();
-    }
-}
 
 // ============================================================================ state gradients, in reverse
 
@@ -789,6 +605,7 @@ int64_t bwd_workspace_bytes(const BwdArgs& a) {
     return bwd_slots(a) * a.H * per * 4;
 }
 
+
 template <int DK, bool F32>
 static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     const int64_t ch = bwd_slots(a) * a.H;
@@ -800,10 +617,14 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     const int NS = a.Dv / kBS;
     const unsigned chain = (unsigned)(((items + 7) / 8) * 8 * NS);
     if (ch > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<DK, F32>), dim3((unsigned)ch), dim3(256), 0, st, a.q, a.k, a.g, a.beta,
-                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, recs);
-        hipLaunchKernelGGL((bwd_states_kernel<DK, F32>), dim3(chain), dim3(256), 0, st, a.v, a.s0, a.cu_seqlens,
-                           a.T_fixed, a.total, a.N, a.H, a.Dv, recs, states);
+        // the forward pass's preparation (fp32 records, plus the plain operands `recs`) and its
+        // state-only chain give the chunk-start states; the fragment records borrow the column-sum
+        // area, which bwd_grad_a writes only later
+        const ChunkArgs fa{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, nullptr, a.cu_seqlens, a.T_fixed, a.total,
+                           a.N, a.H, a.Dk, a.Dv, a.f32, Prologue{false, false, false, false, false}};
+        if ((int64_t)GRec<DK>::FLOATS * 4 < chunk_states_record_bytes(DK)) return hipErrorInvalidValue;
+        const hipError_t e = launch_chunk_states(fa, grads, recs, states, st);
+        if (e != hipSuccess) return e;
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
     hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(256), 0, st, a.d_o, a.d_sfinal, a.ds0,

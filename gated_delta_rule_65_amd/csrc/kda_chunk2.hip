@@ -148,10 +148,11 @@ struct PrepLds {
 // Gram row block W (rows 16W..16W+15), all column blocks I <= W: A (one pass) into sA,
 // scaled by b_r and strictly lower on the diagonal block; P (full precision) into sP,
 // lower with diagonal; blocks I > W of both are zero.
-template <int W, int DK, bool F32>
+// gAbar (backward form only): the unscaled strictly lower A, row-major [64][64].
+template <int W, int DK, bool F32, bool BWD>
 __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf)[8], const float (*E)[8],
                                           const float (*Ei)[8], const float* sCol, const float* tD,
-                                          const float* sBeta, float* sA, float* sP, int m, int cg) {
+                                          const float* sBeta, float* sA, float* sP, float* gAbar, int m, int cg) {
     using Fr = Frag<F32>;
     constexpr int KS = DK / 32;
     f32x4_t accA[W + 1], accP[W + 1];
@@ -209,17 +210,20 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
             }
             sA[gr * 68 + gi] = a * sBeta[gr];
             sP[gr * 68 + gi] = pv;
+            if constexpr (BWD) gAbar[gr * 64 + gi] = a;
         }
     }
 }
 
-template <int DK, bool F32, bool PRO>
+// F32: precision policy of the records (fp32 MFMA operands, else split bf16); IN_F32: q/k input type.
+// BWD: also write the backward pass's plain operands (BwdRec) to brecs.
+template <int DK, bool F32, bool PRO, bool IN_F32 = F32, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                       const void* __restrict__ gv, const void* __restrict__ bv,
                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                       int64_t total, int64_t N, int H, Prologue pro,
-                                                      char* __restrict__ ws) {
-    using In = typename std::conditional<F32, float, uint16_t>::type;
+                                                      char* __restrict__ ws, float* __restrict__ brecs = nullptr) {
+    using In = typename std::conditional<IN_F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = PrepLds<DK, F32>;
     // input prologue; PRO = false compiles the plain form (fp32 log alpha and beta, q and k as given)
@@ -269,6 +273,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     if (j < 0 || t0 >= sr.end) return;  // unused slot
     const int nt = (int)min<int64_t>(kC, sr.end - t0);
     char* rec = ws + (slot * H + h) * R::BYTES;
+    using BR = BwdRec<DK>;
+    float* brec = BWD ? brecs + (slot * H + h) * (int64_t)BR::FLOATS : nullptr;
 
     // ---- rows of sub-block w; running gate sums inside the sub-block (log2)
     const int r = 16 * w + m;
@@ -337,6 +343,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         tD[2 * DK + c] = __builtin_amdgcn_exp2f(G1 + G2);
         const float GC = ((G0 + G1) + G2) + G3;
         reinterpret_cast<float*>(rec + R::GC)[c] = __builtin_amdgcn_exp2f(GC);
+        if constexpr (BWD) brec[BR::GM + c] = __builtin_amdgcn_exp2f(GC);
     }
     lds_barrier();  // (2)
 
@@ -363,6 +370,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         fk.set_hi_only(xk);
         gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);
         gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane, fk);
+        if constexpr (BWD) {  // rows past the end as zeros
+            float* dq_ = brec + BR::QT + r * DK + c0;
+            float* dk_ = brec + BR::KT + r * DK + c0;
+            const float z = rv ? 1.f : 0.f;
+            *reinterpret_cast<float4*>(dq_) = make_float4(z * xq[0], z * xq[1], z * xq[2], z * xq[3]);
+            *reinterpret_cast<float4*>(dq_ + 4) = make_float4(z * xq[4], z * xq[5], z * xq[6], z * xq[7]);
+            *reinterpret_cast<float4*>(dk_) = make_float4(z * xk[0], z * xk[1], z * xk[2], z * xk[3]);
+            *reinterpret_cast<float4*>(dk_ + 4) = make_float4(z * xk[4], z * xk[5], z * xk[6], z * xk[7]);
+        }
         if (w < 3) {
             float* dst = sCol + r * (DK + 4) + c0;
             *reinterpret_cast<float4*>(dst) = make_float4(xc[0], xc[1], xc[2], xc[3]);
@@ -372,10 +388,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     lds_barrier();  // (3)
 
     switch (w) {
-        case 0: prep_gram<0, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
-        case 1: prep_gram<1, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
-        case 2: prep_gram<2, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
-        default: prep_gram<3, DK, F32>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, m, cg); break;
+        case 0: prep_gram<0, DK, F32, BWD>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, brec + BR::AB, m, cg); break;
+        case 1: prep_gram<1, DK, F32, BWD>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, brec + BR::AB, m, cg); break;
+        case 2: prep_gram<2, DK, F32, BWD>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, brec + BR::AB, m, cg); break;
+        default: prep_gram<3, DK, F32, BWD>(qf, kf, E, Ei, sCol, tD, sBeta, sA, sP, brec + BR::AB, m, cg); break;
     }
     lds_barrier();  // (4)
 
@@ -404,6 +420,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         Fr f;
         f.set(x);
         gfrag_store<F32>(rec + R::PM + pair_of(w, kb) * 2 * kPlane, lane, f);
+    }
+    if constexpr (BWD) {
+        for (int e = tid; e < 4096; e += 256) brec[BR::PM + e] = sP[(e >> 6) * 68 + (e & 63)];
+        if (tid < kC) brec[BR::BT + tid] = sBeta[tid];
     }
     lds_barrier();  // (5)
 
@@ -438,6 +458,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
             Nr[R_] = nv;
         }
     }
+    if constexpr (BWD) {  // column block w of M^{-1}
+#pragma unroll
+        for (int R_ = 0; R_ < 4; ++R_)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) brec[BR::MI + (16 * R_ + 4 * cg + jj) * 64 + 16 * w + m] = Nr[R_][jj];
+    }
     // ---- Kbar = e^{G_C - G} k staged transposed ([c][t]) over the Gram operands and P
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -449,6 +475,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         for (int jj = 0; jj < 8; ++jj) {
             const float kbar = (kf[s][jj] * (bt[jj] * Ei[s][jj])) * af[jj];  // k e^{G_C - G_r}
             lds_store1<F32, DK, kC>(pKB, c0 + jj, r, kbar);
+            if constexpr (BWD) brec[BR::KB + r * DK + c0 + jj] = rv ? kbar : 0.f;
         }
     }
     lds_barrier();  // (6)
@@ -496,12 +523,12 @@ struct ChainLds {
 };
 
 // Operands of one chunk for one wave of the chain kernel.
-template <int DK, bool F32>
+template <int DK, bool F32, bool IN_F32>
 struct ChainOps {
     static constexpr int KS = DK / 32, CBW = DK / 64;
     Frag<F32> fQ[KS], fK[KS], fN[2], fP[2], fKB[CBW][2];
     float4 gC[CBW];
-    uint4 vraw[F32 ? 2 : 1];  // this lane's 16-byte pieces of the wave's v rows
+    uint4 vraw[IN_F32 ? 2 : 1];  // this lane's 16-byte pieces of the wave's v rows
 };
 
 // Long sequences with few heads split the chunk range into P segments of L chunks (the one-GPU
@@ -512,6 +539,8 @@ struct ChainOps {
 //   mode 2 (outputs), items (n, h, p): segment p from its true initial state (s0 for p = 0,
 //     else sfold [n][h][p][Dk][Dv] from the fold kernel), o written, s_final from p = P - 1.
 //   mode 0: whole sequences (items (n, h)), s0 -> s_final.
+//   mode 3: as mode 0, and the state at the start of every chunk goes to sx [slot][h][Dk][Dv]
+//     (for the backward pass; compiled state-only, SO = true).
 struct ChainMode {
     int mode;      // 0, 1 or 2
     int P;         // segments per sequence (modes 1, 2)
@@ -520,18 +549,19 @@ struct ChainMode {
     const float* sfold;  // mode 2 input
 };
 
-// SO (state only, mode 1): the output products, their operands and the o traffic are compiled out.
-template <int DK, bool F32, bool SO>
+// SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
+// out.  F32: precision policy of the records; IN_F32: type of v.
+template <int DK, bool F32, bool SO, bool IN_F32 = F32>
 __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                        float* __restrict__ o, float* s_final,
                                                        const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                        int64_t total, int64_t N, int H, int Dv, ChainMode cm,
                                                        const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
-    using In = typename std::conditional<F32, float, uint16_t>::type;
+    using In = typename std::conditional<IN_F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChainLds<DK, F32>;
     using R = Rec<DK, F32>;
-    using Ops = ChainOps<DK, F32>;
+    using Ops = ChainOps<DK, F32, IN_F32>;
     constexpr int KS = DK / 32;
     constexpr int CBW = DK / 64;  // 16-channel blocks of S per wave
     constexpr int VPL = 16 / (int)sizeof(In);  // v values per 16-byte lane load
@@ -560,8 +590,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
     const int64_t start = sr.start, end = sr.end;
     const int64_t nall = (end - start + kC - 1) / kC;
-    const int64_t jbeg = cm.mode ? min<int64_t>(p * cm.L, nall) : 0;
-    const int64_t jend = cm.mode ? min<int64_t>((p + 1) * cm.L, nall) : nall;
+    const bool split = cm.mode == 1 || cm.mode == 2;
+    const int64_t jbeg = split ? min<int64_t>(p * cm.L, nall) : 0;
+    const int64_t jend = split ? min<int64_t>((p + 1) * cm.L, nall) : nall;
     const bool ident = sl >= NV;                           // identity columns (mode 1)
     const int col0 = ident ? 0 : sl * kS;                  // value columns read (v) by this slice
     const int colx = sl * kS;                              // column of this slice in sx rows (mode 1)
@@ -672,6 +703,17 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
         const int ntn = (int)min<int64_t>(kC, end - t0n);
         const char* recn = record(jn);
 
+        if (cm.mode == 3) {  // the state at the start of this chunk, for the backward pass
+            float* sj = cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0;
+#pragma unroll
+            for (int ci = 0; ci < CBW; ++ci)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        sj[(16 * (w * CBW + ci) + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accS[ci][nb][jj];
+        }
+
         // v rows of this chunk (loaded during the previous chunk) into LDS, for the D layout
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i)
@@ -699,7 +741,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             for (int jj = 0; jj < 4; ++jj) {
                 const In raw = sV[(16 * w + 4 * cg + jj) * kS + 16 * nb + m];
                 float vj;
-                if constexpr (F32) vj = raw;
+                if constexpr (IN_F32) vj = raw;
                 else vj = bf16_bits_to_float(raw);
                 xv[jj] = vscale * vj - accX[nb][jj];
             }
@@ -918,6 +960,35 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
                        a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, c2,
                        static_cast<const char*>(ws));
     return hipGetLastError();
+}
+
+// States at every chunk start (fp32 records and products for both input types), for the backward
+// pass: prep into `recs` (chunk_slots(a) * H records of chunk_record_bytes(Dk, true)) and the plain
+// backward operands into `brecs`, then the state-only chain in mode 3 writing `states` [slot][h][Dk][Dv].
+template <int DK, bool IN_F32>
+static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st) {
+    const int64_t prep_grid = chunk_slots(a) * a.H;
+    if (prep_grid > 0)
+        hipLaunchKernelGGL((prep_kernel<DK, true, false, IN_F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st,
+                           a.q, a.k, a.g, a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro,
+                           static_cast<char*>(recs), brecs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const ChainMode cm{3, 1, 0, states, nullptr};
+    hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
+                       dim3(256), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
+                       a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
+    return hipGetLastError();
+}
+
+int64_t chunk_states_record_bytes(int Dk) { return chunk_record_bytes(Dk, true); }
+
+hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st) {
+    if (a.Dk == 128)
+        return a.f32 ? launch_states<128, true>(a, recs, brecs, states, st)
+                     : launch_states<128, false>(a, recs, brecs, states, st);
+    return a.f32 ? launch_states<64, true>(a, recs, brecs, states, st)
+                 : launch_states<64, false>(a, recs, brecs, states, st);
 }
 
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st) {

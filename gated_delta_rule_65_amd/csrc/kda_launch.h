@@ -44,7 +44,22 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t st);
 int64_t chunk_slots(const ChunkArgs& a);
 int64_t chunk_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st);
+// The state at every chunk start, [slot][h][Dk][Dv] fp32 (fp32 products for either input type),
+// and the backward pass's operands: `recs` holds chunk_slots(a) * H records of
+// chunk_states_record_bytes(Dk) bytes, `brecs` as many BwdRec<Dk> records.
+int64_t chunk_states_record_bytes(int Dk);
+hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets): Qt, Kt, Kb
+// [64][DK]; P, Minv = (I + Diag(b) Abar)^{-1}, Abar [64][64]; gamma [DK]; b [64].  Written by the
+// forward preparation kernel in its backward form, read by the backward kernels.
+template <int DK>
+struct BwdRec {
+    static constexpr int QT = 0, KT = 64 * DK, KB = 128 * DK, PM = 192 * DK, MI = PM + 4096, AB = MI + 4096,
+                         GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
+    static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
+};
 
 // Backward pass (kda_bwd.hip): gradients of o and the final state.
 struct BwdArgs {
