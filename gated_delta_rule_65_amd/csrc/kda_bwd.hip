@@ -22,9 +22,10 @@
 //
 // Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) and the state at every chunk start come from
 // the forward pass's prep kernel in its backward form and its chain kernel in mode 3, both with fp32
-// records (launch_chunk_states).  Then three kernels, fp32 arithmetic, 256 threads each:
-//   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS' of every chunk, ds0
-//   bwd_grad_a_kernel  per (chunk, head): dv and the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma)
+// records (launch_chunk_states).  Then three kernels, fp32 arithmetic:
+//   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS', dU, dX of every
+//                      chunk, dv = dX, ds0
+//   bwd_colsum_kernel  per (chunk, head): the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma)
 //   bwd_grad_b_kernel  per (chunk, head): through the inverse, the decayed Gram blocks and the gates
 #include <type_traits>
 
@@ -40,7 +41,7 @@ constexpr int kBS = 32;  // state columns per chain workgroup
 
 template <int DK>
 using BRec = BwdRec<DK>;
-// Per (chunk, head) output of bwd_grad_a (float offsets).
+// Per (chunk, head) output of bwd_colsum (float offsets).
 template <int DK>
 struct GRec {
     static constexpr int DQT = 0, DKT = 64 * DK, DKB = 128 * DK, DP = 192 * DK, DN = DP + 4096, DGM = DN + 4096,
@@ -115,18 +116,26 @@ __device__ __forceinline__ bool chain_item(int64_t items, int NS, int64_t& pr, i
 
 // ============================================================================ state gradients, in reverse
 
+// One workgroup of 1024 threads per (sequence, head, 32 state columns) walks the chunks backwards:
+//   dU = P^T dO + Kb dS',  dX = Diag(b) Minv^T dU,  dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX.
+// dS' (the gradient at the chunk end) goes to dstates, dU and dX to dudx, dX to dv.  Operands are read
+// with 16-byte loads into registers one phase ahead of their use and then staged in LDS.
 template <int DK>
-__global__ __launch_bounds__(256, 1) void bwd_dstates_kernel(const float* __restrict__ d_o,
-                                                             const float* __restrict__ d_sfinal, float* ds0,
-                                                             const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                             int64_t total, int64_t N, int H, int Dv,
-                                                             const float* __restrict__ recs,
-                                                             float* __restrict__ dstates) {
+__global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __restrict__ d_o,
+                                                              const float* __restrict__ d_sfinal, float* ds0,
+                                                              const int32_t* __restrict__ cu, int64_t T_fixed,
+                                                              int64_t total, int64_t N, int H, int Dv,
+                                                              const float* __restrict__ recs,
+                                                              float* __restrict__ dstates, float* __restrict__ dudx,
+                                                              float* __restrict__ dv) {
     using R = BRec<DK>;
-    constexpr int LD = DK + 1;
-    constexpr int TPC = 256 / DK, CPT = kBS / TPC;
-    __shared__ float sD[DK * kBS], sO[64 * kBS], sDU[64 * kBS], sDX[64 * kBS], sM1[64 * LD], sM2[64 * LD],
-        sMI[64 * 65], sB[64], sGm[DK];
+    constexpr int NT = 1024;
+    constexpr int LK = DK + 4, LM = 68;       // padded rows of the [64][DK] and [64][64] operands
+    constexpr int KQ = 64 * DK / 4 / NT;      // 16-byte pieces per thread of a [64][DK] operand
+    constexpr int SPT = DK * kBS / NT;        // dS elements per thread
+    constexpr int TPR = kBS / SPT;            // threads per dS row
+    __shared__ __align__(16) float sD[DK * kBS], sO[64 * kBS], sDU[64 * kBS], sDX[64 * kBS], sA1[64 * LK],
+        sA2[64 * LK], sP[64 * LM], sMI[64 * LM], sB[64], sGm[DK];
     const int tid = threadIdx.x;
     int64_t pr;
     int sl;
@@ -137,253 +146,229 @@ __global__ __launch_bounds__(256, 1) void bwd_dstates_kernel(const float* __rest
     const int64_t nch = (sr.end - sr.start + kBC - 1) / kBC;
     const int col0 = sl * kBS;
 
-    for (int e = tid; e < DK * kBS; e += 256) {
+    for (int e = tid; e < DK * kBS; e += NT) {
         const int c = e / kBS, jj = e % kBS;
         sD[e] = d_sfinal ? d_sfinal[((n * H + h) * DK + c) * (int64_t)Dv + col0 + jj] : 0.f;
     }
-    __syncthreads();
-    const int xr = tid >> 2, xj = (tid & 3) * 8;
-    const int sc = tid / TPC, sj = (tid % TPC) * CPT;
-    for (int64_t jc = nch - 1; jc >= 0; --jc) {
-        const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
-        const float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
-        float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv;
+    const int ui = tid >> 4, uj = 2 * (tid & 15);           // dU, dX: row, 2 columns
+    const int sc = tid / TPR, sj = SPT * (tid % TPR);      // dS: row, SPT columns
+
+    float4 rKb[KQ], rQt[KQ], rKt[KQ], rP, rMI;
+    float2 rO;
+    float rB = 0.f, rG = 0.f;
+    auto rec_of = [&](int64_t jc) {
+        return recs + (bslot(cu, n, jc, T_fixed, sr.start) * H + h) * (int64_t)R::FLOATS;
+    };
+    auto load_a = [&](int64_t jc) {  // Kb, P, Minv, dO, b, gamma of chunk jc
+        const float* rec = rec_of(jc);
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) rKb[q] = reinterpret_cast<const float4*>(rec + R::KB)[tid + q * NT];
+        rP = reinterpret_cast<const float4*>(rec + R::PM)[tid];
+        rMI = reinterpret_cast<const float4*>(rec + R::MI)[tid];
         const int64_t t0 = sr.start + jc * kBC;
         const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        for (int e = tid; e < DK * kBS; e += 256) dst[(e / kBS) * (int64_t)Dv + col0 + e % kBS] = sD[e];
-        for (int e = tid; e < 64 * kBS; e += 256) {
-            const int r = e / kBS;
-            sO[e] = r < nt ? d_o[((t0 + r) * H + h) * (int64_t)Dv + col0 + e % kBS] : 0.f;
-        }
-        for (int e = tid; e < 64 * DK; e += 256) sM1[(e / DK) * LD + e % DK] = rec[R::KB + e];
-        for (int e = tid; e < 4096; e += 256) {
-            sM2[(e >> 6) * 65 + (e & 63)] = rec[R::PM + e];
-            sMI[(e >> 6) * 65 + (e & 63)] = rec[R::MI + e];
-        }
-        if (tid < 64) sB[tid] = rec[R::BT + tid];
-        if (tid < DK) sGm[tid] = rec[R::GM + tid];
-        __syncthreads();
-        {  // dU = P^T dO + Kb dS'
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int r = xr; r < 64; ++r) {
-                const float p = sM2[r * 65 + xr];
+        rO = ui < nt ? *reinterpret_cast<const float2*>(d_o + ((t0 + ui) * H + h) * (int64_t)Dv + col0 + uj)
+                     : make_float2(0.f, 0.f);
+        if (tid < 64) rB = rec[R::BT + tid];
+        if (tid < DK) rG = rec[R::GM + tid];
+    };
+    auto load_c = [&](int64_t jc) {  // Qt, Kt of chunk jc
+        const float* rec = rec_of(jc);
 #pragma unroll
-                for (int m = 0; m < 8; ++m) acc[m] = fmaf(p, sO[r * kBS + xj + m], acc[m]);
+        for (int q = 0; q < KQ; ++q) {
+            rQt[q] = reinterpret_cast<const float4*>(rec + R::QT)[tid + q * NT];
+            rKt[q] = reinterpret_cast<const float4*>(rec + R::KT)[tid + q * NT];
+        }
+    };
+    auto put4 = [&](float* base, int ld, int cols, int e4, float4 x) {  // piece e4 of a row-major [.][cols]
+        const int e = 4 * e4;
+        *reinterpret_cast<float4*>(base + (e / cols) * ld + e % cols) = x;
+    };
+
+    if (nch > 0) load_a(nch - 1);
+    __syncthreads();
+    for (int64_t jc = nch - 1; jc >= 0; --jc) {
+        const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
+        const int64_t t0 = sr.start + jc * kBC;
+        const int nt = (int)min<int64_t>(kBC, sr.end - t0);
+        float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv;
+        for (int e = tid; e < DK * kBS; e += NT) dst[(e / kBS) * (int64_t)Dv + col0 + e % kBS] = sD[e];
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) put4(sA1, LK, DK, tid + q * NT, rKb[q]);
+        put4(sP, LM, 64, tid, rP);
+        put4(sMI, LM, 64, tid, rMI);
+        *reinterpret_cast<float2*>(&sO[ui * kBS + uj]) = rO;
+        if (tid < 64) sB[tid] = rB;
+        if (tid < DK) sGm[tid] = rG;
+        load_c(jc);
+        __syncthreads();
+        if (jc > 0) load_a(jc - 1);
+        {  // dU = P^T dO + Kb dS'
+            float a0 = 0.f, a1 = 0.f;
+            for (int r = ui; r < 64; ++r) {
+                const float p = sP[r * LM + ui];
+                const float2 o = *reinterpret_cast<const float2*>(&sO[r * kBS + uj]);
+                a0 = fmaf(p, o.x, a0);
+                a1 = fmaf(p, o.y, a1);
             }
             for (int c = 0; c < DK; ++c) {
-                const float kb = sM1[xr * LD + c];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) acc[m] = fmaf(kb, sD[c * kBS + xj + m], acc[m]);
+                const float kb = sA1[ui * LK + c];
+                const float2 d = *reinterpret_cast<const float2*>(&sD[c * kBS + uj]);
+                a0 = fmaf(kb, d.x, a0);
+                a1 = fmaf(kb, d.y, a1);
             }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) sDU[xr * kBS + xj + m] = acc[m];
+            *reinterpret_cast<float2*>(&sDU[ui * kBS + uj]) = make_float2(a0, a1);
         }
         __syncthreads();
-        {  // dX = Diag(b) Minv^T dU
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int r = xr; r < 64; ++r) {
-                const float mi = sMI[r * 65 + xr];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) acc[m] = fmaf(mi, sDU[r * kBS + xj + m], acc[m]);
+        {  // dX = Diag(b) Minv^T dU; dU, dX of the chunk and dv = dX
+            float a0 = 0.f, a1 = 0.f;
+            for (int r = ui; r < 64; ++r) {
+                const float mi = sMI[r * LM + ui];
+                const float2 u = *reinterpret_cast<const float2*>(&sDU[r * kBS + uj]);
+                a0 = fmaf(mi, u.x, a0);
+                a1 = fmaf(mi, u.y, a1);
             }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) sDX[xr * kBS + xj + m] = sB[xr] * acc[m];
+            const float2 x = make_float2(sB[ui] * a0, sB[ui] * a1);
+            *reinterpret_cast<float2*>(&sDX[ui * kBS + uj]) = x;
+            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + uj;
+            *reinterpret_cast<float2*>(du_o + ui * (int64_t)Dv) = *reinterpret_cast<const float2*>(&sDU[ui * kBS + uj]);
+            *reinterpret_cast<float2*>(du_o + (64 + ui) * (int64_t)Dv) = x;
+            if (ui < nt) *reinterpret_cast<float2*>(dv + ((t0 + ui) * H + h) * (int64_t)Dv + col0 + uj) = x;
         }
-        for (int e = tid; e < 64 * DK; e += 256) {  // Kb and P were last read before the barrier above
-            sM1[(e / DK) * LD + e % DK] = rec[R::QT + e];
-            sM2[(e / DK) * LD + e % DK] = rec[R::KT + e];
+        __syncthreads();  // Kb is no longer read: Qt goes over it
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            put4(sA1, LK, DK, tid + q * NT, rQt[q]);
+            put4(sA2, LK, DK, tid + q * NT, rKt[q]);
         }
         __syncthreads();
         {  // dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX
-            float acc[CPT];
+            float acc[SPT];
 #pragma unroll
-            for (int m = 0; m < CPT; ++m) acc[m] = sGm[sc] * sD[sc * kBS + sj + m];
+            for (int m = 0; m < SPT; ++m) acc[m] = sGm[sc] * sD[sc * kBS + sj + m];
             for (int r = 0; r < 64; ++r) {
-                const float qt = sM1[r * LD + sc], kt = sM2[r * LD + sc];
+                const float qt = sA1[r * LK + sc], kt = sA2[r * LK + sc];
 #pragma unroll
-                for (int m = 0; m < CPT; ++m)
+                for (int m = 0; m < SPT; ++m)
                     acc[m] = fmaf(qt, sO[r * kBS + sj + m], fmaf(-kt, sDX[r * kBS + sj + m], acc[m]));
             }
 #pragma unroll
-            for (int m = 0; m < CPT; ++m) sD[sc * kBS + sj + m] = acc[m];
+            for (int m = 0; m < SPT; ++m) sD[sc * kBS + sj + m] = acc[m];
         }
         __syncthreads();
     }
     if (ds0)
-        for (int e = tid; e < DK * kBS; e += 256)
+        for (int e = tid; e < DK * kBS; e += NT)
             ds0[((n * H + h) * DK + e / kBS) * (int64_t)Dv + col0 + e % kBS] = sD[e];
 }
 
 // ============================================================================ sums over the value columns
 
-// Per (chunk, head): X, U, dU, dX per 16-column tile of the state, dv, and the products summed over
-// all value columns: dQt = dO S^T, dKt = -dX S^T, dKb = U dS'^T (64 x DK), dP = dO U^T,
-// dN = dU X^T (64 x 64), dgamma = rowsum(S o dS').  Tiles are stored column-major ([j][row]) so
-// that the accumulations read whole rows of them.
-template <int DK, bool F32>
-__global__ __launch_bounds__(256, 1) void bwd_grad_a_kernel(const void* __restrict__ vv, const float* __restrict__ d_o,
+// Eight consecutive fp32 values of a row-major matrix as a split-bf16 MFMA fragment: lane l takes row
+// row0 + l%16 and columns k0 + 8(l/16) .. +7.  The same fragment serves as the A operand of rows of
+// the matrix and as the B operand of its columns (both contract over the stored column index).
+__device__ __forceinline__ Frag<false> frag_rows(const float* base, int64_t ld, int row0, int k0, int m, int cg,
+                                                 float x[8]) {
+    load8_as_float(base + (row0 + m) * ld + k0 + 8 * cg, x);
+    Frag<false> f;
+    f.set(x);
+    return f;
+}
+
+// Per (chunk, head): the products summed over the value columns, all contracting over the stored
+// column index of row-major operands (so every fragment is read straight from memory):
+//   dQt = dO S^T, dKt = -dX S^T, dKb = U dS'^T (64 x DK);  dP = dO U^T, dN = dU X^T (64 x 64);
+//   dgamma = rowsum(S o dS').  Split-bf16 three-pass products; wave w owns rows 16w..16w+15.
+template <int DK>
+__global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restrict__ d_o,
                                                             const int32_t* __restrict__ cu, int64_t T_fixed,
                                                             int64_t total, int64_t N, int H, int Dv,
-                                                            const float* __restrict__ recs,
                                                             const float* __restrict__ states,
                                                             const float* __restrict__ dstates,
-                                                            float* __restrict__ grads, float* __restrict__ dv) {
-    using R = BRec<DK>;
+                                                            const float* __restrict__ xu,
+                                                            const float* __restrict__ dudx,
+                                                            float* __restrict__ grads) {
     using GR = GRec<DK>;
-    constexpr int LD = DK + 1;  // [64][DK] operands
-    constexpr int LT = DK + 4;  // [16][DK] state tiles
-    constexpr int LR = 68;      // [16][64] token tiles
-    constexpr int CPT = DK / 16;
-    __shared__ __align__(16) float sKt[64 * LD], sKb[64 * LD], sP[64 * 65], sMI[64 * 65], sB[64];
-    __shared__ __align__(16) float sST[16 * LT], sDST[16 * LT], sOT[16 * LR], sXT[16 * LR], sUT[16 * LR],
-        sDUT[16 * LR], sDXT[16 * LR];
-    const int tid = threadIdx.x;
+    constexpr int CB = DK / 16;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
     int64_t n, t0;
     int nt;
     if (!slot_chunk(cu, slot, T_fixed, total, N, n, t0, nt)) return;
-    const float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
-    const float* Sg = states + (slot * H + h) * (int64_t)DK * Dv;
-    const float* dSg = dstates + (slot * H + h) * (int64_t)DK * Dv;
-    float* out = grads + (slot * H + h) * (int64_t)GR::FLOATS;
+    const int64_t ch = slot * H + h;
+    const float* S = states + ch * DK * (int64_t)Dv;
+    const float* dS = dstates + ch * DK * (int64_t)Dv;
+    const float* X = xu + ch * 128 * (int64_t)Dv;
+    const float* U = X + 64 * (int64_t)Dv;
+    const float* dU = dudx + ch * 128 * (int64_t)Dv;
+    const float* dX = dU + 64 * (int64_t)Dv;
+    // dO rows of this wave: tokens past the end read the last token and count as zero
+    const int orow = 16 * w + m;
+    const float* dO = d_o + ((t0 + min(orow, nt - 1)) * H + h) * (int64_t)Dv;
+    const float omask = orow < nt ? 1.f : 0.f;
 
-    for (int e = tid; e < 64 * DK; e += 256) {
-        sKt[(e / DK) * LD + e % DK] = rec[R::KT + e];
-        sKb[(e / DK) * LD + e % DK] = rec[R::KB + e];
-    }
-    for (int e = tid; e < 4096; e += 256) {
-        sP[(e >> 6) * 65 + (e & 63)] = rec[R::PM + e];
-        sMI[(e >> 6) * 65 + (e & 63)] = rec[R::MI + e];
-    }
-    if (tid < 64) sB[tid] = rec[R::BT + tid];
+    f32x4_t aQ[CB], aK[CB], aB[CB], aP[4], aN[4];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) aQ[i] = aK[i] = aB[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aP[i] = aN[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float dgam[CB];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) dgam[i] = 0.f;
 
-    const int ar = 4 * (tid >> 4), ac = CPT * (tid & 15), ai = 4 * (tid & 15);  // accumulator block
-    const int xr = tid >> 2, xj = 4 * (tid & 3);                              // tile products: row, 4 columns
-    float aQ[4][CPT], aK[4][CPT], aB[4][CPT], aP[4][4], aN[4][4], aG = 0.f;
+    for (int k0 = 0; k0 < Dv; k0 += 32) {
+        float x[8], y[8];
+        load8_as_float(dO + k0 + 8 * cg, x);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+        for (int j = 0; j < 8; ++j) x[j] *= omask;
+        Frag<false> fO;
+        fO.set(x);
+        const Frag<false> fX = frag_rows(dX, Dv, 16 * w, k0, m, cg, x);
+        const Frag<false> fU = frag_rows(U, Dv, 16 * w, k0, m, cg, x);
+        const Frag<false> fdU = frag_rows(dU, Dv, 16 * w, k0, m, cg, x);
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) aQ[a][b] = aK[a][b] = aB[a][b] = 0.f;
+        for (int cb = 0; cb < CB; ++cb) {
+            const Frag<false> fS = frag_rows(S, Dv, 16 * cb, k0, m, cg, x);
+            const Frag<false> fdS = frag_rows(dS, Dv, 16 * cb, k0, m, cg, y);
+            aQ[cb] = mma_full(aQ[cb], fO, fS);
+            aK[cb] = mma_full(aK[cb], fX, fS);
+            aB[cb] = mma_full(aB[cb], fU, fdS);
+            if (w == 0)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) aP[a][b] = aN[a][b] = 0.f;
-    }
-
-    for (int j0 = 0; j0 < Dv; j0 += 16) {
-        for (int e = tid; e < DK * 16; e += 256) {
-            const int c = e >> 4, jj = e & 15;
-            sST[jj * LT + c] = Sg[c * (int64_t)Dv + j0 + jj];
-            sDST[jj * LT + c] = dSg[c * (int64_t)Dv + j0 + jj];
-        }
-        for (int e = tid; e < 64 * 16; e += 256) {
-            const int r = e >> 4, jj = e & 15;
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)Dv + j0 + jj;
-            sOT[jj * LR + r] = r < nt ? d_o[idx] : 0.f;
-            sXT[jj * LR + r] = r < nt ? load_in<F32>(vv, idx) : 0.f;
-        }
-        __syncthreads();
-        {  // X = V - Kt S
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < DK; ++c) {
-                const float kt = sKt[xr * LD + c];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = fmaf(kt, sST[(xj + m) * LT + c], acc[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) sXT[(xj + m) * LR + xr] -= acc[m];
-        }
-        __syncthreads();
-        {  // U = Minv Diag(b) X;  dU = P^T dO + Kb dS'
-            float u[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i <= xr; ++i) {
-                const float wgt = sMI[xr * 65 + i] * sB[i];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) u[m] = fmaf(wgt, sXT[(xj + m) * LR + i], u[m]);
-            }
-            for (int r = xr; r < 64; ++r) {
-                const float p = sP[r * 65 + xr];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) du[m] = fmaf(p, sOT[(xj + m) * LR + r], du[m]);
-            }
-            for (int c = 0; c < DK; ++c) {
-                const float kb = sKb[xr * LD + c];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) du[m] = fmaf(kb, sDST[(xj + m) * LT + c], du[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                sUT[(xj + m) * LR + xr] = u[m];
-                sDUT[(xj + m) * LR + xr] = du[m];
-            }
-        }
-        __syncthreads();
-        {  // dX = Diag(b) Minv^T dU = dV
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int r = xr; r < 64; ++r) {
-                const float mi = sMI[r * 65 + xr];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = fmaf(mi, sDUT[(xj + m) * LR + r], acc[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float x = sB[xr] * acc[m];
-                sDXT[(xj + m) * LR + xr] = x;
-                if (xr < nt) dv[((t0 + xr) * H + h) * (int64_t)Dv + j0 + xj + m] = x;
-            }
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int jj = 0; jj < 16; ++jj) {
-            float o4[4], x4[4], u4[4], du4[4], s[CPT], ds[CPT], uI[4], xI[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                o4[a] = sOT[jj * LR + ar + a];
-                x4[a] = sDXT[jj * LR + ar + a];
-                u4[a] = sUT[jj * LR + ar + a];
-                du4[a] = sDUT[jj * LR + ar + a];
-                uI[a] = sUT[jj * LR + ai + a];
-                xI[a] = sXT[jj * LR + ai + a];
-            }
-#pragma unroll
-            for (int b = 0; b < CPT; ++b) {
-                s[b] = sST[jj * LT + ac + b];
-                ds[b] = sDST[jj * LT + ac + b];
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-#pragma unroll
-                for (int b = 0; b < CPT; ++b) {
-                    aQ[a][b] = fmaf(o4[a], s[b], aQ[a][b]);
-                    aK[a][b] = fmaf(-x4[a], s[b], aK[a][b]);
-                    aB[a][b] = fmaf(u4[a], ds[b], aB[a][b]);
-                }
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    aP[a][b] = fmaf(o4[a], uI[b], aP[a][b]);
-                    aN[a][b] = fmaf(du4[a], xI[b], aN[a][b]);
-                }
-            }
-        }
-        if (tid < DK)
-            for (int jj = 0; jj < 16; ++jj) aG = fmaf(sST[jj * LT + tid], sDST[jj * LT + tid], aG);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            const int e = (ar + a) * DK + ac + b;
-            out[GR::DQT + e] = aQ[a][b];
-            out[GR::DKT + e] = aK[a][b];
-            out[GR::DKB + e] = aB[a][b];
+                for (int j = 0; j < 8; ++j) dgam[cb] = fmaf(x[j], y[j], dgam[cb]);
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            out[GR::DP + (ar + a) * 64 + ai + b] = aP[a][b];
-            out[GR::DN + (ar + a) * 64 + ai + b] = aN[a][b];
+        for (int ib = 0; ib < 4; ++ib) {
+            aP[ib] = mma_full(aP[ib], fO, frag_rows(U, Dv, 16 * ib, k0, m, cg, x));
+            aN[ib] = mma_full(aN[ib], fdU, frag_rows(X, Dv, 16 * ib, k0, m, cg, x));
         }
     }
-    if (tid < DK) out[GR::DGM + tid] = aG;
+    float* out = grads + ch * (int64_t)GR::FLOATS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * cg + i;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            out[GR::DQT + r * DK + 16 * cb + m] = aQ[cb][i];
+            out[GR::DKT + r * DK + 16 * cb + m] = -aK[cb][i];
+            out[GR::DKB + r * DK + 16 * cb + m] = aB[cb][i];
+        }
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+            out[GR::DP + r * 64 + 16 * ib + m] = aP[ib][i];
+            out[GR::DN + r * 64 + 16 * ib + m] = aN[ib][i];
+        }
+    }
+    if (w == 0) {  // rows 16cb + m: sum the four lane groups' column ranges
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            float v = dgam[cb];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (cg == 0) out[GR::DGM + 16 * cb + m] = v;
+        }
+    }
 }
 
 // ============================================================================ to dq, dk, dg, db
@@ -402,7 +387,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
     constexpr int LD = DK + 4;
     constexpr int CPT = DK / 16;
     __shared__ __align__(16) float sq[64 * LD], sk[64 * LD], sG[64 * LD], sM1[64 * 65], sM2[64 * 65],
-        sM3[64 * 65], sB[64], sDB[64];
+        sM3[64 * 65], sB[64], sDB[64], sGb[5 * DK], sFf[6 * DK], sDf[4 * DK];
     const int tid = threadIdx.x;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -490,73 +475,137 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
     }
     __syncthreads();
 
-    // ---- decayed Gram blocks: thread block rows ar..ar+3, channels ac..ac+CPT-1
-    const int ar = 4 * (tid >> 4), ac = CPT * (tid & 15);
-    float Gr[4][CPT], aq[4][CPT], ak1[4][CPT], ak2[4][CPT];
+    // ---- decay factors by 16-token sub-block (as in the forward pass): with Gs_R the running sum
+    // before block R and Ge_I the one at the end of block I, for token r in block R and i in I <= R
+    //   e^{G_r - G_i} = A1_r * F_RI * B1_i  (I < R),   A1_r * D_R * B1_i  (I = R),
+    // A1_r = e^{G_r - Gs_R} <= 1, B1_i = e^{Ge_I - G_i} <= 1, F_RI = e^{Gs_R - Ge_I} <= 1,
+    // D_R = e^{Gs_R - Ge_R} <= e^80: no exponential per term, none that overflows.
+    if (tid < DK) {
+        const int c = tid;
+        float gb[5];
+        gb[0] = 0.f;
+#pragma unroll
+        for (int b = 1; b < 5; ++b) gb[b] = sG[(16 * b - 1) * LD + c];
+#pragma unroll
+        for (int b = 0; b < 5; ++b) sGb[b * DK + c] = gb[b];
+#pragma unroll
+        for (int R_ = 0; R_ < 4; ++R_) {
+            sDf[R_ * DK + c] = __expf(gb[R_] - gb[R_ + 1]);
+#pragma unroll
+            for (int I = 0; I < R_; ++I) sFf[(R_ * (R_ - 1) / 2 + I) * DK + c] = __expf(gb[R_] - gb[I + 1]);
+        }
+    }
+    const int ar = 4 * (tid >> 4), ac = CPT * (tid & 15), blk = tid >> 6;  // rows ar..ar+3 lie in block blk
+    float Gr[4][CPT];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < CPT; ++b) Gr[a][b] = sG[(ar + a) * LD + ac + b];
+    __syncthreads();
+    // own elements -> tables: sq = q A1, sk = k A1, sG = k B1
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
-            Gr[a][b] = sG[(ar + a) * LD + ac + b];
-            aq[a][b] = ak1[a][b] = ak2[a][b] = 0.f;
+            const int e = (ar + a) * LD + ac + b;
+            const float a1 = __expf(Gr[a][b] - sGb[blk * DK + ac + b]);
+            const float b1 = __expf(sGb[(blk + 1) * DK + ac + b] - Gr[a][b]);
+            const float kx = sk[e];
+            sq[e] *= a1;
+            sk[e] = kx * a1;
+            sG[e] = kx * b1;
         }
-    // rows r of this thread against every column i <= r: dq (P), dk (Abar) of row r
-    for (int i = 0; i < 64; ++i) {
-        float ki[CPT], Gi[CPT];
+    __syncthreads();
+
+    // ---- rows r of this thread against columns i <= r: aq (from P, for dq), ak1 (from Abar, for dk)
+    float aq[4][CPT], ak1[4][CPT], ak2[4][CPT];
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            ki[b] = sk[i * LD + ac + b];
-            Gi[b] = sG[i * LD + ac + b];
-        }
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const float dp = sM2[(ar + a) * 65 + i], da = sM1[(ar + a) * 65 + i];  // zero unless i <= r
+        for (int b = 0; b < CPT; ++b) aq[a][b] = ak1[a][b] = ak2[a][b] = 0.f;
+    for (int I = 0; I <= blk; ++I) {
+        float pq[4][CPT], pk[4][CPT];
 #pragma unroll
-            for (int b = 0; b < CPT; ++b) {
-                const float ke = ki[b] * __expf(fminf(Gr[a][b] - Gi[b], 0.f));
-                aq[a][b] = fmaf(dp, ke, aq[a][b]);
-                ak1[a][b] = fmaf(da, ke, ak1[a][b]);
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) pq[a][b] = pk[a][b] = 0.f;
+        for (int i = 16 * I; i < 16 * I + 16; ++i) {
+            float kb[CPT];
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) kb[b] = sG[i * LD + ac + b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float dp = sM2[(ar + a) * 65 + i], da = sM1[(ar + a) * 65 + i];  // zero unless i <= r
+#pragma unroll
+                for (int b = 0; b < CPT; ++b) {
+                    pq[a][b] = fmaf(dp, kb[b], pq[a][b]);
+                    pk[a][b] = fmaf(da, kb[b], pk[a][b]);
+                }
             }
         }
-    }
-    // rows of this thread as the column index i against every row r >= i: dk of row i
-    for (int r = 0; r < 64; ++r) {
-        float kr[CPT], qr[CPT], Grr[CPT];
+        const float* f = I < blk ? &sFf[(blk * (blk - 1) / 2 + I) * DK + ac] : &sDf[blk * DK + ac];
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            kr[b] = sk[r * LD + ac + b];
-            qr[b] = sq[r * LD + ac + b];
-            Grr[b] = sG[r * LD + ac + b];
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const float dp = sM2[r * 65 + ar + a], da = sM1[r * 65 + ar + a];  // zero unless r >= i
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < CPT; ++b) {
-                const float e = __expf(fminf(Grr[b] - Gr[a][b], 0.f));
-                ak2[a][b] = fmaf(fmaf(da, kr[b], dp * qr[b]), e, ak2[a][b]);
+                aq[a][b] = fmaf(f[b], pq[a][b], aq[a][b]);
+                ak1[a][b] = fmaf(f[b], pk[a][b], ak1[a][b]);
+            }
+    }
+    // ---- rows of this thread as the column index i against rows r >= i: ak2 (for dk)
+    for (int R_ = blk; R_ < 4; ++R_) {
+        float pp[4][CPT];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) pp[a][b] = 0.f;
+        for (int r = 16 * R_; r < 16 * R_ + 16; ++r) {
+            float ka[CPT], qa[CPT];
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) {
+                ka[b] = sk[r * LD + ac + b];
+                qa[b] = sq[r * LD + ac + b];
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float da = sM1[r * 65 + ar + a], dp = sM2[r * 65 + ar + a];  // zero unless r >= i
+#pragma unroll
+                for (int b = 0; b < CPT; ++b) pp[a][b] = fmaf(da, ka[b], fmaf(dp, qa[b], pp[a][b]));
             }
         }
+        const float* f = R_ > blk ? &sFf[(R_ * (R_ - 1) / 2 + blk) * DK + ac] : &sDf[blk * DK + ac];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) ak2[a][b] = fmaf(f[b], pp[a][b], ak2[a][b]);
     }
-    // ---- own elements: dq, dk, and dG into LDS (after every thread has read q, k, G)
+    // ---- own elements: dq, dk, and dG into LDS (after every thread has read the tables)
     float dG[4][CPT], colp[CPT];
 #pragma unroll
     for (int b = 0; b < CPT; ++b) colp[b] = 0.f;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int r = ar + a;
+        float qx[CPT], kx[CPT];
+#pragma unroll
+        for (int b = 0; b < CPT; ++b) {
+            const int64_t idx = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + ac + b;
+            qx[b] = r < nt ? load_in<F32>(qv, idx) : 0.f;
+            kx[b] = r < nt ? load_in<F32>(kv, idx) : 0.f;
+        }
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
             const int c = ac + b;
-            const float Gc = sG[63 * LD + c];
-            const float gam = __expf(Gr[a][b]), gbar = __expf(Gc - Gr[a][b]);
-            const float qx = sq[r * LD + c], kx = sk[r * LD + c];
+            const float a1 = __expf(Gr[a][b] - sGb[blk * DK + c]);
+            const float b1 = __expf(sGb[(blk + 1) * DK + c] - Gr[a][b]);
+            const float q_ = a1 * aq[a][b], k1 = a1 * ak1[a][b], k2 = b1 * ak2[a][b];
+            const float gam = __expf(Gr[a][b]), gbar = __expf(sGb[4 * DK + c] - Gr[a][b]);
             const float dQt = gin[GR::DQT + r * DK + c], dKt = gin[GR::DKT + r * DK + c];
             const float dKb = gin[GR::DKB + r * DK + c];
-            const float dqv = fmaf(gam, dQt, aq[a][b]);
-            const float dkv = fmaf(gam, dKt, fmaf(gbar, dKb, ak1[a][b] + ak2[a][b]));
-            dG[a][b] = qx * (gam * dQt + aq[a][b]) + kx * (gam * dKt - gbar * dKb + ak1[a][b] - ak2[a][b]);
-            colp[b] = fmaf(kx * gbar, dKb, colp[b]);
+            const float dqv = fmaf(gam, dQt, q_);
+            const float dkv = fmaf(gam, dKt, fmaf(gbar, dKb, k1 + k2));
+            dG[a][b] = qx[b] * (gam * dQt + q_) + kx[b] * (gam * dKt - gbar * dKb + k1 - k2);
+            colp[b] = fmaf(kx[b] * gbar, dKb, colp[b]);
             if (r < nt) {
                 const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
                 dq[idx] = dqv;
@@ -570,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
 #pragma unroll
         for (int b = 0; b < CPT; ++b) sq[(ar + a) * LD + ac + b] = dG[a][b];
 #pragma unroll
-    for (int b = 0; b < CPT; ++b) sM3[(tid >> 4) * DK + ac + b] = colp[b];  // [16 row blocks][DK]
+    for (int b = 0; b < CPT; ++b) sM3[(tid >> 4) * DK + ac + b] = colp[b];  // [16 row groups][DK]
     __syncthreads();
     // ---- G to g: reverse running sum plus the chunk-end term; the clamp's mask
     if (tid < DK) {
@@ -599,9 +648,9 @@ int64_t bwd_slots(const BwdArgs& a) {
 static int64_t bwd_rec_floats(int Dk) { return Dk == 128 ? BRec<128>::FLOATS : BRec<64>::FLOATS; }
 static int64_t bwd_grad_floats(int Dk) { return Dk == 128 ? GRec<128>::FLOATS : GRec<64>::FLOATS; }
 
-// [records][states][state gradients][column sums], each per (slot, head)
+// [records][states][state gradients][column sums][X, U][dU, dX], each per (slot, head)
 int64_t bwd_workspace_bytes(const BwdArgs& a) {
-    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_grad_floats(a.Dk);
+    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_grad_floats(a.Dk) + 4 * 64 * (int64_t)a.Dv;
     return bwd_slots(a) * a.H * per * 4;
 }
 
@@ -613,25 +662,27 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     float* states = recs + ch * (int64_t)BRec<DK>::FLOATS;
     float* dstates = states + ch * (int64_t)DK * a.Dv;
     float* grads = dstates + ch * (int64_t)DK * a.Dv;
+    float* xu = grads + ch * (int64_t)GRec<DK>::FLOATS;
+    float* dudx = xu + ch * 128 * (int64_t)a.Dv;
     const int64_t items = a.N * (int64_t)a.H;
     const int NS = a.Dv / kBS;
     const unsigned chain = (unsigned)(((items + 7) / 8) * 8 * NS);
     if (ch > 0) {
         // the forward pass's preparation (fp32 records, plus the plain operands `recs`) and its
-        // state-only chain give the chunk-start states; the fragment records borrow the column-sum
-        // area, which bwd_grad_a writes only later
+        // state-only chain give the chunk-start states and X, U; the fragment records borrow the
+        // column-sum area, which bwd_colsum writes only later
         const ChunkArgs fa{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, nullptr, a.cu_seqlens, a.T_fixed, a.total,
                            a.N, a.H, a.Dk, a.Dv, a.f32, Prologue{false, false, false, false, false}};
         if ((int64_t)GRec<DK>::FLOATS * 4 < chunk_states_record_bytes(DK)) return hipErrorInvalidValue;
-        const hipError_t e = launch_chunk_states(fa, grads, recs, states, st);
+        const hipError_t e = launch_chunk_states(fa, grads, recs, states, xu, st);
         if (e != hipSuccess) return e;
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(256), 0, st, a.d_o, a.d_sfinal, a.ds0,
-                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates);
+    hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
+                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, dudx, a.dv);
     if (ch > 0) {
-        hipLaunchKernelGGL((bwd_grad_a_kernel<DK, F32>), dim3((unsigned)ch), dim3(256), 0, st, a.v, a.d_o,
-                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, states, dstates, grads, a.dv);
+        hipLaunchKernelGGL((bwd_colsum_kernel<DK>), dim3((unsigned)ch), dim3(256), 0, st, a.d_o, a.cu_seqlens,
+                           a.T_fixed, a.total, a.N, a.H, a.Dv, states, dstates, xu, dudx, grads);
         hipLaunchKernelGGL((bwd_grad_b_kernel<DK, F32>), dim3((unsigned)ch), dim3(256), 0, st, a.q, a.k, a.g,
                            a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, recs, grads, a.dq, a.dk, a.dg, a.dbeta);
     }

@@ -542,11 +542,12 @@ struct ChainOps {
 //   mode 3: as mode 0, and the state at the start of every chunk goes to sx [slot][h][Dk][Dv]
 //     (for the backward pass; compiled state-only, SO = true).
 struct ChainMode {
-    int mode;      // 0, 1 or 2
+    int mode;      // 0, 1, 2 or 3
     int P;         // segments per sequence (modes 1, 2)
     int64_t L;     // chunks per segment (modes 1, 2)
-    float* sx;     // mode 1 output
+    float* sx;     // mode 1 output; mode 3: chunk-start states
     const float* sfold;  // mode 2 input
+    float* xu = nullptr;  // mode 3: X and U of every chunk, [slot][h][2][64][Dv] (rows past the end zero)
 };
 
 // SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
@@ -746,6 +747,14 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
                 xv[jj] = vscale * vj - accX[nb][jj];
             }
             lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
+            if (cm.mode == 3 && cm.xu) {
+                float* xo = cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = 16 * w + 4 * cg + jj;
+                    xo[row * (int64_t)Dv + 16 * nb + m] = row < nt ? xv[jj] : 0.f;
+                }
+            }
         }
         lds_barrier();  // (1)
 
@@ -764,6 +773,15 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             load_nv(nxt, recn, t0n, ntn);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
+            if (cm.mode == 3 && cm.xu) {
+                float* uo = cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) * (int64_t)Dv +
+                            col0;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        uo[(16 * w + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accU[nb][jj];
+            }
         }
         lds_barrier();  // (2)
 
@@ -964,9 +982,11 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
 
 // States at every chunk start (fp32 records and products for both input types), for the backward
 // pass: prep into `recs` (chunk_slots(a) * H records of chunk_record_bytes(Dk, true)) and the plain
-// backward operands into `brecs`, then the state-only chain in mode 3 writing `states` [slot][h][Dk][Dv].
+// backward operands into `brecs`, then the state-only chain in mode 3 writing `states` [slot][h][Dk][Dv]
+// and X, U of every chunk to `xu` [slot][h][2][64][Dv].
 template <int DK, bool IN_F32>
-static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st) {
+static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, float* states, float* xu,
+                                hipStream_t st) {
     const int64_t prep_grid = chunk_slots(a) * a.H;
     if (prep_grid > 0)
         hipLaunchKernelGGL((prep_kernel<DK, true, false, IN_F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st,
@@ -974,7 +994,7 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
                            static_cast<char*>(recs), brecs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const ChainMode cm{3, 1, 0, states, nullptr};
+    const ChainMode cm{3, 1, 0, states, nullptr, xu};
     hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
                        dim3(256), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
                        a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
@@ -983,12 +1003,13 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
 
 int64_t chunk_states_record_bytes(int Dk) { return chunk_record_bytes(Dk, true); }
 
-hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st) {
+hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, float* xu,
+                               hipStream_t st) {
     if (a.Dk == 128)
-        return a.f32 ? launch_states<128, true>(a, recs, brecs, states, st)
-                     : launch_states<128, false>(a, recs, brecs, states, st);
-    return a.f32 ? launch_states<64, true>(a, recs, brecs, states, st)
-                 : launch_states<64, false>(a, recs, brecs, states, st);
+        return a.f32 ? launch_states<128, true>(a, recs, brecs, states, xu, st)
+                     : launch_states<128, false>(a, recs, brecs, states, xu, st);
+    return a.f32 ? launch_states<64, true>(a, recs, brecs, states, xu, st)
+                 : launch_states<64, false>(a, recs, brecs, states, xu, st);
 }
 
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st) {

@@ -45,10 +45,12 @@ int64_t chunk_slots(const ChunkArgs& a);
 int64_t chunk_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st);
 // The state at every chunk start, [slot][h][Dk][Dv] fp32 (fp32 products for either input type),
-// and the backward pass's operands: `recs` holds chunk_slots(a) * H records of
-// chunk_states_record_bytes(Dk) bytes, `brecs` as many BwdRec<Dk> records.
+// X = V - Kt S and U of every chunk, [slot][h][2][64][Dv], and the backward pass's operands: `recs`
+// holds chunk_slots(a) * H records of chunk_states_record_bytes(Dk) bytes, `brecs` as many
+// BwdRec<Dk> records.
 int64_t chunk_states_record_bytes(int Dk);
-hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, hipStream_t st);
+hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, float* xu,
+                               hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
 // Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets): Qt, Kt, Kb

@@ -185,7 +185,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
 
 /*
  * Workspace bytes kda_chunk_bwd needs: B * ceil(T/64) * H records of
- * 4 * (386*Dk + 20544 + 2*Dk*Dv) bytes (401.25 KiB at Dk = Dv = 128).
+ * 4 * (386*Dk + 20544 + 2*Dk*Dv + 256*Dv) bytes (529.25 KiB at Dk = Dv = 128).
  */
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype);
 
