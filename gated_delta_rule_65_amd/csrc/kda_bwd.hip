@@ -373,21 +373,27 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
 
 // ============================================================================ to dq, dk, dg, db
 
+// Per (chunk, head), 1024 threads: through N = Minv Diag(b) and Minv = (I + Diag(b) Abar)^{-1} to db and
+// dAbar, then through the decayed Gram blocks Abar and P, Qt, Kt, Kb and gamma to dq, dk and dG, and
+// from G to dg.  Thread t owns row t/16 and channels (t%16)*DK/16 .. of the token-by-channel tensors.
 template <int DK, bool F32>
-__global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
-                                                            const float* __restrict__ g,
-                                                            const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                            int64_t total, int64_t N, int H,
-                                                            const float* __restrict__ recs,
-                                                            const float* __restrict__ grads, float* __restrict__ dq,
-                                                            float* __restrict__ dk, float* __restrict__ dg,
-                                                            float* __restrict__ dbeta) {
+__global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restrict__ qv,
+                                                             const void* __restrict__ kv,
+                                                             const float* __restrict__ g,
+                                                             const int32_t* __restrict__ cu, int64_t T_fixed,
+                                                             int64_t total, int64_t N, int H,
+                                                             const float* __restrict__ recs,
+                                                             const float* __restrict__ grads,
+                                                             float* __restrict__ dq, float* __restrict__ dk,
+                                                             float* __restrict__ dg, float* __restrict__ dbeta) {
     using R = BRec<DK>;
     using GR = GRec<DK>;
+    constexpr int NT = 1024;
     constexpr int LD = DK + 4;
     constexpr int CPT = DK / 16;
     __shared__ __align__(16) float sq[64 * LD], sk[64 * LD], sG[64 * LD], sM1[64 * 65], sM2[64 * 65],
         sM3[64 * 65], sB[64], sDB[64], sGb[5 * DK], sFf[6 * DK], sDf[4 * DK];
+    __shared__ uint32_t sMk[64 * DK / 32];  // bit set: g outside [-5, 0] (its gradient is zero)
     const int tid = threadIdx.x;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -398,47 +404,47 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
     const float* gin = grads + (slot * H + h) * (int64_t)GR::FLOATS;
 
     // ---- through N = Minv Diag(b) and Minv = M^{-1}
-    for (int e = tid; e < 4096; e += 256) {
+    for (int e = tid; e < 4096; e += NT) {
         const int r = e >> 6, i = e & 63;
         sM1[r * 65 + i] = i <= r ? gin[GR::DN + e] : 0.f;  // dN (N is lower triangular)
         sM2[r * 65 + i] = rec[R::MI + e];                   // Minv
     }
     if (tid < 64) sB[tid] = rec[R::BT + tid];
+    for (int e = tid; e < 64 * DK / 32; e += NT) sMk[e] = 0u;
     __syncthreads();
     float dbn = 0.f;
     if (tid < 64)
         for (int r = tid; r < 64; ++r) dbn = fmaf(sM1[r * 65 + tid], sM2[r * 65 + tid], dbn);
     __syncthreads();
-    for (int e = tid; e < 4096; e += 256) sM1[(e >> 6) * 65 + (e & 63)] *= sB[e & 63];  // dMinv = dN Diag(b)
+    for (int e = tid; e < 4096; e += NT) sM1[(e >> 6) * 65 + (e & 63)] *= sB[e & 63];  // dMinv = dN Diag(b)
     __syncthreads();
-    const int xr = tid >> 2, xs = 16 * (tid & 3);
+    const int xr = tid >> 4, xs = 4 * (tid & 15);
     {  // T1 = dMinv Minv^T
-        float acc[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
         for (int i = 0; i < 64; ++i) {
             const float d = sM1[xr * 65 + i];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc[m] = fmaf(d, sM2[(xs + m) * 65 + i], acc[m]);
+            for (int m = 0; m < 4; ++m) acc[m] = fmaf(d, sM2[(xs + m) * 65 + i], acc[m]);
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) sM3[xr * 65 + xs + m] = acc[m];
+        for (int m = 0; m < 4; ++m) sM3[xr * 65 + xs + m] = acc[m];
     }
     __syncthreads();
     {  // dM = -Minv^T T1
-        float acc[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = 0.f;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
         for (int r = 0; r < 64; ++r) {
             const float mi = sM2[r * 65 + xr];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc[m] = fmaf(mi, sM3[r * 65 + xs + m], acc[m]);
+            for (int m = 0; m < 4; ++m) acc[m] = fmaf(mi, sM3[r * 65 + xs + m], acc[m]);
         }
+        __syncthreads();  // every thread has read dMinv
 #pragma unroll
-        for (int m = 0; m < 16; ++m) sM1[xr * 65 + xs + m] = -acc[m];
+        for (int m = 0; m < 4; ++m) sM1[xr * 65 + xs + m] = -acc[m];
     }
     __syncthreads();
-    for (int e = tid; e < 4096; e += 256) {
+    for (int e = tid; e < 4096; e += NT) {
         const int r = e >> 6, i = e & 63;
         sM3[r * 65 + i] = rec[R::AB + e];                   // Abar
         sM2[r * 65 + i] = i <= r ? gin[GR::DP + e] : 0.f;   // dP (P is lower triangular with the diagonal)
@@ -451,19 +457,30 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
         sDB[r] = dbn + dbm;
         for (int i = 0; i < 64; ++i) sM1[r * 65 + i] = i < r ? sB[r] * sM1[r * 65 + i] : 0.f;
     }
-    // ---- q, k and the running gate sums
-    for (int e = tid; e < 64 * DK; e += 256) {
-        const int r = e / DK, c = e % DK;
-        float x = 0.f, y = 0.f, z = 0.f;
-        if (r < nt) {
-            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
-            x = load_in<F32>(qv, idx);
-            y = load_in<F32>(kv, idx);
-            z = fminf(fmaxf(g[idx], -5.f), 0.f);
+    // ---- q, k and the running gate sums (eight consecutive channels per piece)
+#pragma unroll 1
+    for (int e8 = tid; e8 < 8 * DK; e8 += NT) {
+        const int r = (8 * e8) / DK, c = (8 * e8) % DK;
+        float x[8], y[8], z[8];
+        const int64_t idx = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + c;
+        if constexpr (F32) {
+            load8_as_float(static_cast<const float*>(qv) + idx, x);
+            load8_as_float(static_cast<const float*>(kv) + idx, y);
+        } else {
+            load8_as_float(static_cast<const uint16_t*>(qv) + idx, x);
+            load8_as_float(static_cast<const uint16_t*>(kv) + idx, y);
         }
-        sq[r * LD + c] = x;
-        sk[r * LD + c] = y;
-        sG[r * LD + c] = z;
+        load8_as_float(g + idx, z);
+        const float msk = r < nt ? 1.f : 0.f;
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            sq[r * LD + c + jj] = msk * x[jj];
+            sk[r * LD + c + jj] = msk * y[jj];
+            sG[r * LD + c + jj] = msk * fminf(fmaxf(z[jj], -5.f), 0.f);
+            bits |= (z[jj] < -5.f || z[jj] > 0.f) ? (1u << jj) : 0u;
+        }
+        atomicOr(&sMk[r * (DK / 32) + c / 32], bits << (c % 32));
     }
     __syncthreads();
     if (tid < DK) {
@@ -495,117 +512,91 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
             for (int I = 0; I < R_; ++I) sFf[(R_ * (R_ - 1) / 2 + I) * DK + c] = __expf(gb[R_] - gb[I + 1]);
         }
     }
-    const int ar = 4 * (tid >> 4), ac = CPT * (tid & 15), blk = tid >> 6;  // rows ar..ar+3 lie in block blk
-    float Gr[4][CPT];
+    const int ar = tid >> 4, ac = CPT * (tid & 15), blk = ar >> 4;  // one row; a wave's rows share a block
+    float Gr[CPT];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < CPT; ++b) Gr[a][b] = sG[(ar + a) * LD + ac + b];
+    for (int b = 0; b < CPT; ++b) Gr[b] = sG[ar * LD + ac + b];
     __syncthreads();
     // own elements -> tables: sq = q A1, sk = k A1, sG = k B1
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            const int e = (ar + a) * LD + ac + b;
-            const float a1 = __expf(Gr[a][b] - sGb[blk * DK + ac + b]);
-            const float b1 = __expf(sGb[(blk + 1) * DK + ac + b] - Gr[a][b]);
-            const float kx = sk[e];
-            sq[e] *= a1;
-            sk[e] = kx * a1;
-            sG[e] = kx * b1;
-        }
+    for (int b = 0; b < CPT; ++b) {
+        const int e = ar * LD + ac + b;
+        const float a1 = __expf(Gr[b] - sGb[blk * DK + ac + b]);
+        const float b1 = __expf(sGb[(blk + 1) * DK + ac + b] - Gr[b]);
+        const float kx = sk[e];
+        sq[e] *= a1;
+        sk[e] = kx * a1;
+        sG[e] = kx * b1;
+    }
     __syncthreads();
 
-    // ---- rows r of this thread against columns i <= r: aq (from P, for dq), ak1 (from Abar, for dk)
-    float aq[4][CPT], ak1[4][CPT], ak2[4][CPT];
+    // ---- row ar against columns i <= ar: aq (from P, for dq), ak1 (from Abar, for dk)
+    float aq[CPT], ak1[CPT], ak2[CPT];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < CPT; ++b) aq[a][b] = ak1[a][b] = ak2[a][b] = 0.f;
+    for (int b = 0; b < CPT; ++b) aq[b] = ak1[b] = ak2[b] = 0.f;
+#pragma unroll 1
     for (int I = 0; I <= blk; ++I) {
-        float pq[4][CPT], pk[4][CPT];
+        float pq[CPT], pk[CPT];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < CPT; ++b) pq[a][b] = pk[a][b] = 0.f;
+        for (int b = 0; b < CPT; ++b) pq[b] = pk[b] = 0.f;
+#pragma unroll 4
         for (int i = 16 * I; i < 16 * I + 16; ++i) {
-            float kb[CPT];
+            const float dp = sM2[ar * 65 + i], da = sM1[ar * 65 + i];  // zero unless i <= ar
 #pragma unroll
-            for (int b = 0; b < CPT; ++b) kb[b] = sG[i * LD + ac + b];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const float dp = sM2[(ar + a) * 65 + i], da = sM1[(ar + a) * 65 + i];  // zero unless i <= r
-#pragma unroll
-                for (int b = 0; b < CPT; ++b) {
-                    pq[a][b] = fmaf(dp, kb[b], pq[a][b]);
-                    pk[a][b] = fmaf(da, kb[b], pk[a][b]);
-                }
+            for (int b = 0; b < CPT; ++b) {
+                const float kb = sG[i * LD + ac + b];
+                pq[b] = fmaf(dp, kb, pq[b]);
+                pk[b] = fmaf(da, kb, pk[b]);
             }
         }
         const float* f = I < blk ? &sFf[(blk * (blk - 1) / 2 + I) * DK + ac] : &sDf[blk * DK + ac];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < CPT; ++b) {
-                aq[a][b] = fmaf(f[b], pq[a][b], aq[a][b]);
-                ak1[a][b] = fmaf(f[b], pk[a][b], ak1[a][b]);
-            }
+        for (int b = 0; b < CPT; ++b) {
+            aq[b] = fmaf(f[b], pq[b], aq[b]);
+            ak1[b] = fmaf(f[b], pk[b], ak1[b]);
+        }
     }
-    // ---- rows of this thread as the column index i against rows r >= i: ak2 (for dk)
+    // ---- row ar as the column index i against rows r >= i: ak2 (for dk)
+#pragma unroll 1
     for (int R_ = blk; R_ < 4; ++R_) {
-        float pp[4][CPT];
+        float pp[CPT];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < CPT; ++b) pp[a][b] = 0.f;
+        for (int b = 0; b < CPT; ++b) pp[b] = 0.f;
+#pragma unroll 4
         for (int r = 16 * R_; r < 16 * R_ + 16; ++r) {
-            float ka[CPT], qa[CPT];
+            const float da = sM1[r * 65 + ar], dp = sM2[r * 65 + ar];  // zero unless r >= ar
 #pragma unroll
-            for (int b = 0; b < CPT; ++b) {
-                ka[b] = sk[r * LD + ac + b];
-                qa[b] = sq[r * LD + ac + b];
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const float da = sM1[r * 65 + ar + a], dp = sM2[r * 65 + ar + a];  // zero unless r >= i
-#pragma unroll
-                for (int b = 0; b < CPT; ++b) pp[a][b] = fmaf(da, ka[b], fmaf(dp, qa[b], pp[a][b]));
-            }
+            for (int b = 0; b < CPT; ++b)
+                pp[b] = fmaf(da, sk[r * LD + ac + b], fmaf(dp, sq[r * LD + ac + b], pp[b]));
         }
         const float* f = R_ > blk ? &sFf[(R_ * (R_ - 1) / 2 + blk) * DK + ac] : &sDf[blk * DK + ac];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < CPT; ++b) ak2[a][b] = fmaf(f[b], pp[a][b], ak2[a][b]);
+        for (int b = 0; b < CPT; ++b) ak2[b] = fmaf(f[b], pp[b], ak2[b]);
     }
-    // ---- own elements: dq, dk, and dG into LDS (after every thread has read the tables)
-    float dG[4][CPT], colp[CPT];
-#pragma unroll
-    for (int b = 0; b < CPT; ++b) colp[b] = 0.f;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int r = ar + a;
+    // ---- own elements: dq, dk, and dG (after every thread has read the tables)
+    float dG[CPT], colp[CPT];
+    {
+        const int r = ar;
         float qx[CPT], kx[CPT];
+        const int64_t idx0 = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + ac;
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
-            const int64_t idx = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + ac + b;
-            qx[b] = r < nt ? load_in<F32>(qv, idx) : 0.f;
-            kx[b] = r < nt ? load_in<F32>(kv, idx) : 0.f;
+            qx[b] = r < nt ? load_in<F32>(qv, idx0 + b) : 0.f;
+            kx[b] = r < nt ? load_in<F32>(kv, idx0 + b) : 0.f;
         }
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
             const int c = ac + b;
-            const float a1 = __expf(Gr[a][b] - sGb[blk * DK + c]);
-            const float b1 = __expf(sGb[(blk + 1) * DK + c] - Gr[a][b]);
-            const float q_ = a1 * aq[a][b], k1 = a1 * ak1[a][b], k2 = b1 * ak2[a][b];
-            const float gam = __expf(Gr[a][b]), gbar = __expf(sGb[4 * DK + c] - Gr[a][b]);
+            const float a1 = __expf(Gr[b] - sGb[blk * DK + c]);
+            const float b1 = __expf(sGb[(blk + 1) * DK + c] - Gr[b]);
+            const float q_ = a1 * aq[b], k1 = a1 * ak1[b], k2 = b1 * ak2[b];
+            const float gam = __expf(Gr[b]), gbar = __expf(sGb[4 * DK + c] - Gr[b]);
             const float dQt = gin[GR::DQT + r * DK + c], dKt = gin[GR::DKT + r * DK + c];
             const float dKb = gin[GR::DKB + r * DK + c];
             const float dqv = fmaf(gam, dQt, q_);
             const float dkv = fmaf(gam, dKt, fmaf(gbar, dKb, k1 + k2));
-            dG[a][b] = qx[b] * (gam * dQt + q_) + kx[b] * (gam * dKt - gbar * dKb + k1 - k2);
-            colp[b] = fmaf(kx[b] * gbar, dKb, colp[b]);
+            dG[b] = qx[b] * (gam * dQt + q_) + kx[b] * (gam * dKt - gbar * dKb + k1 - k2);
+            colp[b] = kx[b] * gbar * dKb;
             if (r < nt) {
                 const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
                 dq[idx] = dqv;
@@ -613,25 +604,29 @@ __global__ __launch_bounds__(256, 1) void bwd_grad_b_kernel(const void* __restri
             }
         }
     }
+    // the four rows of a wave summed for the chunk-end column term
+#pragma unroll
+    for (int b = 0; b < CPT; ++b) {
+        colp[b] += __shfl_xor(colp[b], 16);
+        colp[b] += __shfl_xor(colp[b], 32);
+    }
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < CPT; ++b) sq[ar * LD + ac + b] = dG[b];
+    if ((tid & 63) < 16)
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) sq[(ar + a) * LD + ac + b] = dG[a][b];
-#pragma unroll
-    for (int b = 0; b < CPT; ++b) sM3[(tid >> 4) * DK + ac + b] = colp[b];  // [16 row groups][DK]
+        for (int b = 0; b < CPT; ++b) sM3[(tid >> 6) * DK + ac + b] = colp[b];  // [16 waves][DK]
     __syncthreads();
     // ---- G to g: reverse running sum plus the chunk-end term; the clamp's mask
     if (tid < DK) {
         const int c = tid;
         float acc = rec[R::GM + c] * gin[GR::DGM + c];  // gamma dgamma
-        for (int rb = 0; rb < 16; ++rb) acc += sM3[rb * DK + c];
+        for (int wv = 0; wv < 16; ++wv) acc += sM3[wv * DK + c];
         for (int r = 63; r >= 0; --r) {
             acc += sq[r * LD + c];
             if (r < nt) {
-                const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
-                const float gr = g[idx];
-                dg[idx] = (gr >= -5.f && gr <= 0.f) ? acc : 0.f;
+                const bool outside = (sMk[r * (DK / 32) + c / 32] >> (c % 32)) & 1u;
+                dg[((t0 + r) * H + h) * (int64_t)DK + c] = outside ? 0.f : acc;
             }
         }
     }
@@ -683,7 +678,7 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     if (ch > 0) {
         hipLaunchKernelGGL((bwd_colsum_kernel<DK>), dim3((unsigned)ch), dim3(256), 0, st, a.d_o, a.cu_seqlens,
                            a.T_fixed, a.total, a.N, a.H, a.Dv, states, dstates, xu, dudx, grads);
-        hipLaunchKernelGGL((bwd_grad_b_kernel<DK, F32>), dim3((unsigned)ch), dim3(256), 0, st, a.q, a.k, a.g,
+        hipLaunchKernelGGL((bwd_grad_b_kernel<DK, F32>), dim3((unsigned)ch), dim3(1024), 0, st, a.q, a.k, a.g,
                            a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, recs, grads, a.dq, a.dk, a.dg, a.dbeta);
     }
     return hipGetLastError();
