@@ -540,7 +540,7 @@ struct ChainOps {
 //     else sfold [n][h][p][Dk][Dv] from the fold kernel), o written, s_final from p = P - 1.
 //   mode 0: whole sequences (items (n, h)), s0 -> s_final.
 //   mode 3: as mode 0, and the state at the start of every chunk goes to sx [slot][h][Dk][Dv]
-//     (for the backward pass; compiled state-only, SO = true).
+//     (for the backward pass; compiled state-only with the stores, SO = ST = true).
 struct ChainMode {
     int mode;      // 0, 1, 2 or 3
     int P;         // segments per sequence (modes 1, 2)
@@ -551,8 +551,8 @@ struct ChainMode {
 };
 
 // SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
-// out.  F32: precision policy of the records; IN_F32: type of v.
-template <int DK, bool F32, bool SO, bool IN_F32 = F32>
+// out.  F32: precision policy of the records; IN_F32: type of v; ST: mode 3's stores are compiled in.
+template <int DK, bool F32, bool SO, bool IN_F32 = F32, bool ST = false>
 __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                        float* __restrict__ o, float* s_final,
                                                        const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
         const int ntn = (int)min<int64_t>(kC, end - t0n);
         const char* recn = record(jn);
 
-        if (cm.mode == 3) {  // the state at the start of this chunk, for the backward pass
+        if constexpr (ST) {  // the state at the start of this chunk, for the backward pass
             float* sj = cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0;
 #pragma unroll
             for (int ci = 0; ci < CBW; ++ci)
@@ -747,7 +747,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
                 xv[jj] = vscale * vj - accX[nb][jj];
             }
             lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
-            if (cm.mode == 3 && cm.xu) {
+            if constexpr (ST) {
                 float* xo = cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
             load_nv(nxt, recn, t0n, ntn);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
-            if (cm.mode == 3 && cm.xu) {
+            if constexpr (ST) {
                 float* uo = cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) * (int64_t)Dv +
                             col0;
 #pragma unroll
@@ -995,7 +995,7 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const ChainMode cm{3, 1, 0, states, nullptr, xu};
-    hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
+    hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32, true>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
                        dim3(256), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
                        a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
     return hipGetLastError();
