@@ -116,11 +116,15 @@ __device__ __forceinline__ bool chain_item(int64_t items, int NS, int64_t& pr, i
 
 // ============================================================================ state gradients, in reverse
 
-// One workgroup of 1024 threads per (sequence, head, 32 state columns) walks the chunks backwards:
+// One workgroup of 1024 threads (16 waves) per (sequence, head, 32 state columns) walks the chunks
+// backwards on MFMA (F32: fp32 products, else split bf16):
 //   dU = P^T dO + Kb dS',  dX = Diag(b) Minv^T dU,  dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX.
-// dS' (the gradient at the chunk end) goes to dstates, dU and dX to dudx, dX to dv.  Operands are read
-// with 16-byte loads into registers one phase ahead of their use and then staged in LDS.
-template <int DK>
+// Waves 0-7 own one 16x16 tile of dU and dX each; every wave (Dk = 128) or waves 0-7 (Dk = 64) own
+// one 16x16 tile of dS, which stays in their registers from chunk to chunk.  dS' (the gradient at
+// the chunk end) goes to dstates, dU and dX to dudx, dX to dv.  The operands are read with 16-byte
+// loads into registers one phase ahead of their use and staged in LDS in operand order (rows, then
+// the contracted index), so that each MFMA fragment is one row read.
+template <int DK, bool F32>
 __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __restrict__ d_o,
                                                               const float* __restrict__ d_sfinal, float* ds0,
                                                               const int32_t* __restrict__ cu, int64_t T_fixed,
@@ -129,14 +133,32 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
                                                               float* __restrict__ dstates, float* __restrict__ dudx,
                                                               float* __restrict__ dv) {
     using R = BRec<DK>;
+    using Fr = Frag<F32>;
+    using MTT = LMat<F32, 64, 64>;   // P^T, Minv^T  [i][r]
+    using MKB = LMat<F32, 64, DK>;   // Kb           [i][c]
+    using MQT = LMat<F32, DK, 64>;   // Qt^T, -Kt^T  [c][r]
+    using MOT = LMat<F32, kBS, 64>;  // dO^T, dU^T, dX^T [j][r]
+    using MDS = LMat<F32, kBS, DK>;  // dS'^T [j][c]
     constexpr int NT = 1024;
-    constexpr int LK = DK + 4, LM = 68;       // padded rows of the [64][DK] and [64][64] operands
-    constexpr int KQ = 64 * DK / 4 / NT;      // 16-byte pieces per thread of a [64][DK] operand
-    constexpr int SPT = DK * kBS / NT;        // dS elements per thread
-    constexpr int TPR = kBS / SPT;            // threads per dS row
-    __shared__ __align__(16) float sD[DK * kBS], sO[64 * kBS], sDU[64 * kBS], sDX[64 * kBS], sA1[64 * LK],
-        sA2[64 * LK], sP[64 * LM], sMI[64 * LM], sB[64], sGm[DK];
-    const int tid = threadIdx.x;
+    constexpr int AB1 = MTT::BYTES + MKB::BYTES, AB2 = 2 * MQT::BYTES;
+    constexpr int A_BYTES = AB1 > AB2 ? AB1 : AB2;  // P^T + Kb (for dU), then Qt^T + -Kt^T (for dS)
+    constexpr int O_MT = A_BYTES, O_OT = O_MT + MTT::BYTES, O_DS = O_OT + MOT::BYTES, O_DU = O_DS + MDS::BYTES,
+                  O_DX = O_DU + MOT::BYTES, O_B = O_DX + MOT::BYTES, O_G = O_B + 256, TOTAL = O_G + DK * 4;
+    constexpr int KQ = 64 * DK / 4 / NT;  // 16-byte pieces per thread of a [64][DK] operand
+    __shared__ __align__(16) char smem[TOTAL];
+    char* pPT = smem;
+    char* pKB = smem + MTT::BYTES;
+    char* pQT = smem;
+    char* pKT = smem + MQT::BYTES;
+    char* pMT = smem + O_MT;
+    char* pOT = smem + O_OT;
+    char* pDS = smem + O_DS;
+    char* pDU = smem + O_DU;
+    char* pDX = smem + O_DX;
+    float* sB = reinterpret_cast<float*>(smem + O_B);
+    float* sG = reinterpret_cast<float*>(smem + O_G);
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     int64_t pr;
     int sl;
     if (!chain_item(N * (int64_t)H, Dv / kBS, pr, sl)) return;
@@ -146,120 +168,132 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
     const int64_t nch = (sr.end - sr.start + kBC - 1) / kBC;
     const int col0 = sl * kBS;
 
-    for (int e = tid; e < DK * kBS; e += NT) {
-        const int c = e / kBS, jj = e % kBS;
-        sD[e] = d_sfinal ? d_sfinal[((n * H + h) * DK + c) * (int64_t)Dv + col0 + jj] : 0.f;
-    }
-    const int ui = tid >> 4, uj = 2 * (tid & 15);           // dU, dX: row, 2 columns
-    const int sc = tid / TPR, sj = SPT * (tid % TPR);      // dS: row, SPT columns
+    const bool uwave = w < 8;                         // owns a tile of dU and dX
+    const int rb = (w >> 1) & 3, nb = w & 1;          // that tile: rows 16rb.., columns 16nb..
+    const int s0u = rb >= 2 ? 1 : 0;                  // P^T, Minv^T rows 16rb.. vanish below column 32 s0u
+    const bool swave = w < DK / 8;                    // owns a tile of dS
+    const int cb = w >> 1;                            // that tile: rows 16cb.., columns 16nb..
 
-    float4 rKb[KQ], rQt[KQ], rKt[KQ], rP, rMI;
+    // dS' in the owners' registers (D layout: rows 16cb + 4cg + jj, column 16nb + m) and in LDS
+    f32x4_t dS = {0.f, 0.f, 0.f, 0.f};
+    if (swave) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            dS[jj] = d_sfinal ? d_sfinal[((n * H + h) * DK + 16 * cb + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nb + m]
+                              : 0.f;
+        lds_store4<F32, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, dS);
+    }
+
+    float4 rPT, rMT, rKB[KQ], rQT[KQ], rKT[KQ];
     float2 rO;
     float rB = 0.f, rG = 0.f;
+    const int orow = tid >> 4, ocol = 2 * (tid & 15);  // this thread's two dO values
     auto rec_of = [&](int64_t jc) {
         return recs + (bslot(cu, n, jc, T_fixed, sr.start) * H + h) * (int64_t)R::FLOATS;
     };
-    auto load_a = [&](int64_t jc) {  // Kb, P, Minv, dO, b, gamma of chunk jc
+    auto load_a = [&](int64_t jc) {  // P^T, Minv^T, Kb, dO, b, gamma of chunk jc
         const float* rec = rec_of(jc);
+        rPT = reinterpret_cast<const float4*>(rec + R::PMT)[tid];
+        rMT = reinterpret_cast<const float4*>(rec + R::MIT)[tid];
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) rKb[q] = reinterpret_cast<const float4*>(rec + R::KB)[tid + q * NT];
-        rP = reinterpret_cast<const float4*>(rec + R::PM)[tid];
-        rMI = reinterpret_cast<const float4*>(rec + R::MI)[tid];
+        for (int q = 0; q < KQ; ++q) rKB[q] = reinterpret_cast<const float4*>(rec + R::KB)[tid + q * NT];
         const int64_t t0 = sr.start + jc * kBC;
         const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        rO = ui < nt ? *reinterpret_cast<const float2*>(d_o + ((t0 + ui) * H + h) * (int64_t)Dv + col0 + uj)
-                     : make_float2(0.f, 0.f);
+        rO = orow < nt ? *reinterpret_cast<const float2*>(d_o + ((t0 + orow) * H + h) * (int64_t)Dv + col0 + ocol)
+                       : make_float2(0.f, 0.f);
         if (tid < 64) rB = rec[R::BT + tid];
         if (tid < DK) rG = rec[R::GM + tid];
     };
-    auto load_c = [&](int64_t jc) {  // Qt, Kt of chunk jc
+    auto load_c = [&](int64_t jc) {  // Qt^T, Kt^T of chunk jc
         const float* rec = rec_of(jc);
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
-            rQt[q] = reinterpret_cast<const float4*>(rec + R::QT)[tid + q * NT];
-            rKt[q] = reinterpret_cast<const float4*>(rec + R::KT)[tid + q * NT];
+            rQT[q] = reinterpret_cast<const float4*>(rec + R::QTT)[tid + q * NT];
+            rKT[q] = reinterpret_cast<const float4*>(rec + R::KTT)[tid + q * NT];
         }
     };
-    auto put4 = [&](float* base, int ld, int cols, int e4, float4 x) {  // piece e4 of a row-major [.][cols]
-        const int e = 4 * e4;
-        *reinterpret_cast<float4*>(base + (e / cols) * ld + e % cols) = x;
-    };
+    auto f4 = [](float4 x, float sgn) { return f32x4_t{sgn * x.x, sgn * x.y, sgn * x.z, sgn * x.w}; };
 
     if (nch > 0) load_a(nch - 1);
-    __syncthreads();
     for (int64_t jc = nch - 1; jc >= 0; --jc) {
         const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
         const int64_t t0 = sr.start + jc * kBC;
         const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv;
-        for (int e = tid; e < DK * kBS; e += NT) dst[(e / kBS) * (int64_t)Dv + col0 + e % kBS] = sD[e];
+        if (swave) {  // dS' of this chunk
+            float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv + col0 + 16 * nb + m;
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) put4(sA1, LK, DK, tid + q * NT, rKb[q]);
-        put4(sP, LM, 64, tid, rP);
-        put4(sMI, LM, 64, tid, rMI);
-        *reinterpret_cast<float2*>(&sO[ui * kBS + uj]) = rO;
+            for (int jj = 0; jj < 4; ++jj) dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv] = dS[jj];
+        }
+        // stage P^T, Minv^T, Kb, dO^T, b, gamma (the previous chunk's dS phase has finished: barrier)
+        lds_store4<F32, 64, 64>(pPT, (4 * tid) >> 6, (4 * tid) & 63, f4(rPT, 1.f));
+        lds_store4<F32, 64, 64>(pMT, (4 * tid) >> 6, (4 * tid) & 63, f4(rMT, 1.f));
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            const int e = 4 * (tid + q * NT);
+            lds_store4<F32, 64, DK>(pKB, e / DK, e % DK, f4(rKB[q], 1.f));
+        }
+        lds_store1<F32, kBS, 64>(pOT, ocol, orow, rO.x);
+        lds_store1<F32, kBS, 64>(pOT, ocol + 1, orow, rO.y);
         if (tid < 64) sB[tid] = rB;
-        if (tid < DK) sGm[tid] = rG;
+        if (tid < DK) sG[tid] = rG;
         load_c(jc);
         __syncthreads();
         if (jc > 0) load_a(jc - 1);
-        {  // dU = P^T dO + Kb dS'
-            float a0 = 0.f, a1 = 0.f;
-            for (int r = ui; r < 64; ++r) {
-                const float p = sP[r * LM + ui];
-                const float2 o = *reinterpret_cast<const float2*>(&sO[r * kBS + uj]);
-                a0 = fmaf(p, o.x, a0);
-                a1 = fmaf(p, o.y, a1);
-            }
-            for (int c = 0; c < DK; ++c) {
-                const float kb = sA1[ui * LK + c];
-                const float2 d = *reinterpret_cast<const float2*>(&sD[c * kBS + uj]);
-                a0 = fmaf(kb, d.x, a0);
-                a1 = fmaf(kb, d.y, a1);
-            }
-            *reinterpret_cast<float2*>(&sDU[ui * kBS + uj]) = make_float2(a0, a1);
+
+        f32x4_t accU = {0.f, 0.f, 0.f, 0.f};
+        if (uwave) {  // dU = P^T dO + Kb dS'
+            for (int s = s0u; s < 2; ++s)
+                accU = mma_full(accU, lds_frag<F32, 64, 64>(pPT, 16 * rb + m, 32 * s + 8 * cg),
+                                lds_frag<F32, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s)
+                accU = mma_full(accU, lds_frag<F32, 64, DK>(pKB, 16 * rb + m, 32 * s + 8 * cg),
+                                lds_frag<F32, kBS, DK>(pDS, 16 * nb + m, 32 * s + 8 * cg));
+            lds_store4<F32, kBS, 64>(pDU, 16 * nb + m, 16 * rb + 4 * cg, accU);
         }
         __syncthreads();
-        {  // dX = Diag(b) Minv^T dU; dU, dX of the chunk and dv = dX
-            float a0 = 0.f, a1 = 0.f;
-            for (int r = ui; r < 64; ++r) {
-                const float mi = sMI[r * LM + ui];
-                const float2 u = *reinterpret_cast<const float2*>(&sDU[r * kBS + uj]);
-                a0 = fmaf(mi, u.x, a0);
-                a1 = fmaf(mi, u.y, a1);
+        if (uwave) {  // dX = Diag(b) Minv^T dU; dU, dX of the chunk and dv = dX
+            f32x4_t accX = {0.f, 0.f, 0.f, 0.f};
+            for (int s = s0u; s < 2; ++s)
+                accX = mma_full(accX, lds_frag<F32, 64, 64>(pMT, 16 * rb + m, 32 * s + 8 * cg),
+                                lds_frag<F32, kBS, 64>(pDU, 16 * nb + m, 32 * s + 8 * cg));
+            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + 16 * nb + m;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * rb + 4 * cg + jj;
+                accX[jj] *= sB[i];
+                du_o[i * (int64_t)Dv] = accU[jj];
+                du_o[(64 + i) * (int64_t)Dv] = accX[jj];
+                if (i < nt) dv[((t0 + i) * H + h) * (int64_t)Dv + col0 + 16 * nb + m] = accX[jj];
             }
-            const float2 x = make_float2(sB[ui] * a0, sB[ui] * a1);
-            *reinterpret_cast<float2*>(&sDX[ui * kBS + uj]) = x;
-            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + uj;
-            *reinterpret_cast<float2*>(du_o + ui * (int64_t)Dv) = *reinterpret_cast<const float2*>(&sDU[ui * kBS + uj]);
-            *reinterpret_cast<float2*>(du_o + (64 + ui) * (int64_t)Dv) = x;
-            if (ui < nt) *reinterpret_cast<float2*>(dv + ((t0 + ui) * H + h) * (int64_t)Dv + col0 + uj) = x;
+            lds_store4<F32, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, accX);
         }
-        __syncthreads();  // Kb is no longer read: Qt goes over it
+        __syncthreads();  // P^T and Kb are no longer read: Qt^T and -Kt^T go over them
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
-            put4(sA1, LK, DK, tid + q * NT, rQt[q]);
-            put4(sA2, LK, DK, tid + q * NT, rKt[q]);
+            const int e = 4 * (tid + q * NT);
+            lds_store4<F32, DK, 64>(pQT, e / 64, e % 64, f4(rQT[q], 1.f));
+            lds_store4<F32, DK, 64>(pKT, e / 64, e % 64, f4(rKT[q], -1.f));
         }
         __syncthreads();
-        {  // dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX
-            float acc[SPT];
+        if (swave) {  // dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX
 #pragma unroll
-            for (int m = 0; m < SPT; ++m) acc[m] = sGm[sc] * sD[sc * kBS + sj + m];
-            for (int r = 0; r < 64; ++r) {
-                const float qt = sA1[r * LK + sc], kt = sA2[r * LK + sc];
+            for (int jj = 0; jj < 4; ++jj) dS[jj] *= sG[16 * cb + 4 * cg + jj];
 #pragma unroll
-                for (int m = 0; m < SPT; ++m)
-                    acc[m] = fmaf(qt, sO[r * kBS + sj + m], fmaf(-kt, sDX[r * kBS + sj + m], acc[m]));
+            for (int s = 0; s < 2; ++s) {
+                dS = mma_full(dS, lds_frag<F32, DK, 64>(pQT, 16 * cb + m, 32 * s + 8 * cg),
+                              lds_frag<F32, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
+                dS = mma_full(dS, lds_frag<F32, DK, 64>(pKT, 16 * cb + m, 32 * s + 8 * cg),
+                              lds_frag<F32, kBS, 64>(pDX, 16 * nb + m, 32 * s + 8 * cg));
             }
-#pragma unroll
-            for (int m = 0; m < SPT; ++m) sD[sc * kBS + sj + m] = acc[m];
+            lds_store4<F32, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, dS);
         }
         __syncthreads();
     }
-    if (ds0)
-        for (int e = tid; e < DK * kBS; e += NT)
-            ds0[((n * H + h) * DK + e / kBS) * (int64_t)Dv + col0 + e % kBS] = sD[e];
+    if (ds0 && swave)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            ds0[((n * H + h) * DK + 16 * cb + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nb + m] = dS[jj];
 }
 
 // ============================================================================ sums over the value columns
@@ -407,7 +441,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     for (int e = tid; e < 4096; e += NT) {
         const int r = e >> 6, i = e & 63;
         sM1[r * 65 + i] = i <= r ? gin[GR::DN + e] : 0.f;  // dN (N is lower triangular)
-        sM2[r * 65 + i] = rec[R::MI + e];                   // Minv
+        sM2[i * 65 + r] = rec[R::MIT + e];                  // Minv (from its transpose)
     }
     if (tid < 64) sB[tid] = rec[R::BT + tid];
     for (int e = tid; e < 64 * DK / 32; e += NT) sMk[e] = 0u;
@@ -673,7 +707,7 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
+    hipLaunchKernelGGL((bwd_dstates_kernel<DK, true>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
                        a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, dudx, a.dv);
     if (ch > 0) {
         hipLaunchKernelGGL((bwd_colsum_kernel<DK>), dim3((unsigned)ch), dim3(256), 0, st, a.d_o, a.cu_seqlens,

@@ -370,14 +370,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         fk.set_hi_only(xk);
         gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);
         gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane, fk);
-        if constexpr (BWD) {  // rows past the end as zeros
-            float* dq_ = brec + BR::QT + r * DK + c0;
-            float* dk_ = brec + BR::KT + r * DK + c0;
+        if constexpr (BWD) {  // Qt^T, Kt^T [c][r]; rows past the end as zeros
             const float z = rv ? 1.f : 0.f;
-            *reinterpret_cast<float4*>(dq_) = make_float4(z * xq[0], z * xq[1], z * xq[2], z * xq[3]);
-            *reinterpret_cast<float4*>(dq_ + 4) = make_float4(z * xq[4], z * xq[5], z * xq[6], z * xq[7]);
-            *reinterpret_cast<float4*>(dk_) = make_float4(z * xk[0], z * xk[1], z * xk[2], z * xk[3]);
-            *reinterpret_cast<float4*>(dk_ + 4) = make_float4(z * xk[4], z * xk[5], z * xk[6], z * xk[7]);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                brec[BR::QTT + (c0 + jj) * 64 + r] = z * xq[jj];
+                brec[BR::KTT + (c0 + jj) * 64 + r] = z * xk[jj];
+            }
         }
         if (w < 3) {
             float* dst = sCol + r * (DK + 4) + c0;
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         gfrag_store<F32>(rec + R::PM + pair_of(w, kb) * 2 * kPlane, lane, f);
     }
     if constexpr (BWD) {
-        for (int e = tid; e < 4096; e += 256) brec[BR::PM + e] = sP[(e >> 6) * 68 + (e & 63)];
+        for (int e = tid; e < 4096; e += 256) brec[BR::PMT + e] = sP[(e & 63) * 68 + (e >> 6)];  // P^T
         if (tid < kC) brec[BR::BT + tid] = sBeta[tid];
     }
     lds_barrier();  // (5)
@@ -458,11 +457,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
             Nr[R_] = nv;
         }
     }
-    if constexpr (BWD) {  // column block w of M^{-1}
+    if constexpr (BWD) {  // column block w of M^{-1}, as rows of (M^{-1})^T
 #pragma unroll
         for (int R_ = 0; R_ < 4; ++R_)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) brec[BR::MI + (16 * R_ + 4 * cg + jj) * 64 + 16 * w + m] = Nr[R_][jj];
+            *reinterpret_cast<float4*>(brec + BR::MIT + (16 * w + m) * 64 + 16 * R_ + 4 * cg) =
+                make_float4(Nr[R_][0], Nr[R_][1], Nr[R_][2], Nr[R_][3]);
     }
     // ---- Kbar = e^{G_C - G} k staged transposed ([c][t]) over the Gram operands and P
 #pragma unroll

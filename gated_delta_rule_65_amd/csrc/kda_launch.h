@@ -53,13 +53,14 @@ hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, flo
                                hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
-// Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets): Qt, Kt, Kb
-// [64][DK]; P, Minv = (I + Diag(b) Abar)^{-1}, Abar [64][64]; gamma [DK]; b [64].  Written by the
-// forward preparation kernel in its backward form, read by the backward kernels.
+// Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets):
+// Qt^T, Kt^T [DK][64]; Kb [64][DK]; P^T, Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1};
+// Abar [64][64]; gamma [DK]; b [64].  Transposed where the backward products contract over tokens.
+// Written by the forward preparation kernel in its backward form, read by the backward kernels.
 template <int DK>
 struct BwdRec {
-    static constexpr int QT = 0, KT = 64 * DK, KB = 128 * DK, PM = 192 * DK, MI = PM + 4096, AB = MI + 4096,
-                         GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
+    static constexpr int QTT = 0, KTT = 64 * DK, KB = 128 * DK, PMT = 192 * DK, MIT = PMT + 4096,
+                         AB = MIT + 4096, GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
     static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
 };
 
