@@ -446,9 +446,17 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     if (tid < 64) sB[tid] = rec[R::BT + tid];
     for (int e = tid; e < 64 * DK / 32; e += NT) sMk[e] = 0u;
     __syncthreads();
+    {  // db from N: column sums of dN o Minv, 16 partial sums of 4 rows per column
+        const int i = tid & 63, r0 = 4 * (tid >> 6);
+        float p = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) p = fmaf(sM1[(r0 + a) * 65 + i], sM2[(r0 + a) * 65 + i], p);
+        sM3[(tid >> 6) * 64 + i] = p;
+    }
+    __syncthreads();
     float dbn = 0.f;
     if (tid < 64)
-        for (int r = tid; r < 64; ++r) dbn = fmaf(sM1[r * 65 + tid], sM2[r * 65 + tid], dbn);
+        for (int rg = 0; rg < 16; ++rg) dbn += sM3[rg * 64 + tid];
     __syncthreads();
     for (int e = tid; e < 4096; e += NT) sM1[(e >> 6) * 65 + (e & 63)] *= sB[e & 63];  // dMinv = dN Diag(b)
     __syncthreads();
@@ -484,12 +492,23 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
         sM2[r * 65 + i] = i <= r ? gin[GR::DP + e] : 0.f;   // dP (P is lower triangular with the diagonal)
     }
     __syncthreads();
-    if (tid < 64) {  // db from M = I + Diag(b) Abar, then dAbar = strict_tril(Diag(b) dM)
-        const int r = tid;
-        float dbm = 0.f;
-        for (int i = 0; i < r; ++i) dbm = fmaf(sM1[r * 65 + i], sM3[r * 65 + i], dbm);
-        sDB[r] = dbn + dbm;
-        for (int i = 0; i < 64; ++i) sM1[r * 65 + i] = i < r ? sB[r] * sM1[r * 65 + i] : 0.f;
+    if (tid < 64) sDB[tid] = dbn;
+    {  // db from M = I + Diag(b) Abar (row sums over 16 lanes), then dAbar = strict_tril(Diag(b) dM)
+        const int r = tid >> 4, i0 = 4 * (tid & 15);
+        float p = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int i = i0 + a;
+            const float dm = sM1[r * 65 + i];
+            if (i < r) p = fmaf(dm, sM3[r * 65 + i], p);
+            sM1[r * 65 + i] = i < r ? sB[r] * dm : 0.f;
+        }
+        p += __shfl_xor(p, 1);
+        p += __shfl_xor(p, 2);
+        p += __shfl_xor(p, 4);
+        p += __shfl_xor(p, 8);
+        __syncthreads();  // sDB holds the column part
+        if ((tid & 15) == 0) sDB[r] += p;
     }
     // ---- q, k and the running gate sums (eight consecutive channels per piece)
 #pragma unroll 1
@@ -517,12 +536,24 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
         atomicOr(&sMk[r * (DK / 32) + c / 32], bits << (c % 32));
     }
     __syncthreads();
-    if (tid < DK) {
+    // running sums down each channel: segments of SEG rows per thread, then the segment offsets
+    constexpr int NSEG = NT / DK, SEG = 64 / NSEG;
+    const int sc_ = tid % DK, sg_ = tid / DK;
+    {
         float acc = 0.f;
-        for (int r = 0; r < 64; ++r) {
-            acc += sG[r * LD + tid];
-            sG[r * LD + tid] = acc;
+#pragma unroll
+        for (int r = SEG * sg_; r < SEG * sg_ + SEG; ++r) {
+            acc += sG[r * LD + sc_];
+            sG[r * LD + sc_] = acc;
         }
+    }
+    __syncthreads();
+    {
+        float off = 0.f;
+        for (int s2 = 0; s2 < sg_; ++s2) off += sG[(SEG * s2 + SEG - 1) * LD + sc_];
+        __syncthreads();  // every offset read before any is changed
+#pragma unroll
+        for (int r = SEG * sg_; r < SEG * sg_ + SEG; ++r) sG[r * LD + sc_] += off;
     }
     __syncthreads();
 
@@ -651,16 +682,27 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
 #pragma unroll
         for (int b = 0; b < CPT; ++b) sM3[(tid >> 6) * DK + ac + b] = colp[b];  // [16 waves][DK]
     __syncthreads();
-    // ---- G to g: reverse running sum plus the chunk-end term; the clamp's mask
-    if (tid < DK) {
-        const int c = tid;
-        float acc = rec[R::GM + c] * gin[GR::DGM + c];  // gamma dgamma
-        for (int wv = 0; wv < 16; ++wv) acc += sM3[wv * DK + c];
-        for (int r = 63; r >= 0; --r) {
+    // ---- G to g: reverse running sum (segments as above) plus the chunk-end term; the clamp's mask
+    {
+        const int c = sc_;
+        float acc = 0.f;
+#pragma unroll
+        for (int r = SEG * sg_ + SEG - 1; r >= SEG * sg_; --r) {
             acc += sq[r * LD + c];
+            sq[r * LD + c] = acc;
+        }
+    }
+    __syncthreads();
+    {
+        const int c = sc_;
+        float off = rec[R::GM + c] * gin[GR::DGM + c];  // gamma dgamma
+        for (int wv = 0; wv < 16; ++wv) off += sM3[wv * DK + c];
+        for (int s2 = sg_ + 1; s2 < NSEG; ++s2) off += sq[(SEG * s2) * LD + c];
+#pragma unroll
+        for (int r = SEG * sg_; r < SEG * sg_ + SEG; ++r) {
             if (r < nt) {
                 const bool outside = (sMk[r * (DK / 32) + c / 32] >> (c % 32)) & 1u;
-                dg[((t0 + r) * H + h) * (int64_t)DK + c] = outside ? 0.f : acc;
+                dg[((t0 + r) * H + h) * (int64_t)DK + c] = outside ? 0.f : sq[r * LD + c] + off;
             }
         }
     }
