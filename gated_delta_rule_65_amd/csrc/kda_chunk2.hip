@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kC = 64;  // tokens per chunk
 constexpr int kS = 32;  // state columns per chain workgroup
+constexpr int kChainThreads = 512;  // chain workgroup: eight waves
 
 // ---------------------------------------------------------------------------- fragments in HBM
 // A fragment (eight values per lane, see Frag) is stored as two planes of
@@ -521,13 +522,19 @@ struct ChainLds {
     static constexpr int TOTAL = V + 64 * kS * 4;
 };
 
-// Operands of one chunk for one wave of the chain kernel.
+// Operands of one chunk for one wave of the chain kernel.  A state wave (row block rb) holds the rows
+// of rb of Kt and M^{-1} Diag(b) and its v rows; an output wave (row block rb) the rows of rb of Qt and
+// P; both hold the Kbar^T rows and gamma_C entries of their S tiles' channel block.
 template <int DK, bool F32, bool IN_F32>
-struct ChainOps {
-    static constexpr int KS = DK / 32, CBW = DK / 64;
-    Frag<F32> fQ[KS], fK[KS], fN[2], fP[2], fKB[CBW][2];
-    float4 gC[CBW];
+struct ChainStateOps {
+    Frag<F32> fK[DK / 32], fN[2], fKB[2];
+    float4 gC;
     uint4 vraw[IN_F32 ? 2 : 1];  // this lane's 16-byte pieces of the wave's v rows
+};
+template <int DK, bool F32>
+struct ChainOutOps {
+    Frag<F32> fQ[DK / 32], fP[2], fKB[2];
+    float4 gC;
 };
 
 // Long sequences with few heads split the chunk range into P segments of L chunks (the one-GPU
@@ -551,20 +558,28 @@ struct ChainMode {
 
 // SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
 // out.  F32: precision policy of the records; IN_F32: type of v; ST: mode 3's stores are compiled in.
+//
+// Eight waves, two per SIMD, so that one wave's LDS and MFMA latencies overlap the other's work.
+// State waves 0-3 (row block rb = w) compute X = V - Kt S and U = M^{-1} Diag(b) X for the 16 rows
+// of rb and all 32 columns; output waves 4-7 (rb = w - 4) compute O = Qt S + P U for the same rows,
+// Qt S spread over the first two phases.  Every wave also updates DK / 64 of the (16-channel block,
+// 16-column half) tiles of S in the third phase.  Both kinds of wave pass the same three barriers
+// per chunk.
 template <int DK, bool F32, bool SO, bool IN_F32 = F32, bool ST = false>
-__global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
-                                                       float* __restrict__ o, float* s_final,
-                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
-                                                       int64_t total, int64_t N, int H, int Dv, ChainMode cm,
-                                                       const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
+__global__ __launch_bounds__(kChainThreads, SO && !F32 ? 4 : 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
+                                                                 float* __restrict__ o, float* s_final,
+                                                                 const int32_t* __restrict__ cu_seqlens,
+                                                                 int64_t T_fixed, int64_t total, int64_t N, int H,
+                                                                 int Dv, ChainMode cm,
+                                                                 const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
     using In = typename std::conditional<IN_F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChainLds<DK, F32>;
     using R = Rec<DK, F32>;
-    using Ops = ChainOps<DK, F32, IN_F32>;
     constexpr int KS = DK / 32;
-    constexpr int CBW = DK / 64;  // 16-channel blocks of S per wave
-    constexpr int VPL = 16 / (int)sizeof(In);  // v values per 16-byte lane load
+    constexpr int KH = KS / 2;                      // Qt S steps in the first phase (the rest in the second)
+    constexpr int TPW = DK / 64;                    // S tiles per wave (all in one channel block)
+    constexpr int VPL = 16 / (int)sizeof(In);       // v values per 16-byte lane load
     const In* __restrict__ v = static_cast<const In*>(vv);
 
     __shared__ __align__(16) char smem[L::TOTAL];
@@ -575,6 +590,9 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     In* sV = reinterpret_cast<In*>(smem + L::V);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
+    const int rb = w & 3;
+    const int cbw = (w * TPW) >> 1;                            // channel block of this wave's S tiles
+    auto nbt = [&](int i) { return (w * TPW + i) & 1; };      // column half of S tile i
     const int NV = Dv / kS;                                // value-column slices
     const int NS = cm.mode == 1 ? NV + DK / kS : NV;       // + identity-column slices in mode 1
     const int segs = cm.mode == 1 ? cm.P - 1 : (cm.mode == 2 ? cm.P : 1);
@@ -597,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     const int col0 = ident ? 0 : sl * kS;                  // value columns read (v) by this slice
     const int colx = sl * kS;                              // column of this slice in sx rows (mode 1)
     const float vscale = ident ? 0.f : 1.f;                // V = 0 for the identity columns
-    const int nk = steps_of(w);
+    const int nk = steps_of(rb);
 
     // state of this slice at the segment start / its destination
     auto state_in = [&](int c, int col) -> float {
@@ -612,242 +630,284 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(const void* __restrict__ 
     const int ld_dst = cm.mode == 1 ? Dv + DK : Dv;
     const int col_dst = cm.mode == 1 ? colx : col0;
 
-    // initial state (wave w: channel blocks w*CBW.., both 16-column halves)
-    f32x4_t accS[CBW][2];
+    // initial state of this wave's tiles
+    f32x4_t accS[TPW];
 #pragma unroll
-    for (int ci = 0; ci < CBW; ++ci) {
-        const int cb = w * CBW + ci;
+    for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int c = 16 * cb + 4 * cg + jj;
-                accS[ci][nb][jj] = state_in(c, col0 + 16 * nb + m);
-            }
-            lds_store4<F32, kS, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
-        }
+        for (int jj = 0; jj < 4; ++jj) accS[i][jj] = state_in(16 * cbw + 4 * cg + jj, col0 + 16 * nbt(i) + m);
+        lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
     }
-
-    // global row traffic of this wave (rows 16w..16w+15 of a chunk): v and o move as whole
-    // row slices of the workgroup's 32 columns, one 16-byte piece per lane and load
-    const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
-    constexpr int VLPR = kS / VPL;        // lanes per v row slice (bf16: 4, fp32: 8)
-    constexpr int VROWS = 64 / VLPR;      // v rows per load (bf16: 16, fp32: 8)
-    constexpr int VLOADS = 16 / VROWS;    // loads per lane (bf16: 1, fp32: 2)
-    const int vrow = 16 * w + lane / VLPR, vpiece = lane % VLPR;
-    const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * VPL;
-    float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + (lane & 7) * 4;
 
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
     };
-    // loads of one chunk's operands, in the three groups they are consumed in
-    auto load_qk = [&](Ops& d, const char* rec, int s) {
-        if constexpr (!SO) d.fQ[s] = gfrag_load<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane);
-        d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane);
-    };
-    auto load_nv = [&](Ops& d, const char* rec, int64_t t0, int nt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)  // rows of waves 0, 1 stop at token 31: their second step repeats the first
-            d.fN[kb] = gfrag_load<F32>(rec + R::NM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const uint32_t rvo = (uint32_t)min(vrow + i * VROWS, nt - 1) * rs_v;
-            d.vraw[i] = *reinterpret_cast<const uint4*>(v_l + t0 * (int64_t)rs_v + rvo);
-        }
-    };
-    auto load_pkb = [&](Ops& d, const char* rec, int ci) {
-        const int cb = w * CBW + ci;
-        if (!SO && ci == 0) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                d.fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(w, min(kb, nk - 1)) * 2 * kPlane, lane);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) d.fKB[ci][kb] = gfrag_load<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane);
-        d.gC[ci] = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cb + 4 * cg) * 4);
-    };
-    auto load_all = [&](Ops& d, int64_t jc) {
-        const char* rec = record(jc);
-        const int64_t t0 = start + jc * kC;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) load_qk(d, rec, s);
-        load_nv(d, rec, t0, (int)min<int64_t>(kC, end - t0));
-#pragma unroll
-        for (int ci = 0; ci < CBW; ++ci) load_pkb(d, rec, ci);
-    };
+    auto chunk_start = [&](int64_t jc) { return start + jc * kC; };
+    auto chunk_len = [&](int64_t jc) { return (int)min<int64_t>(kC, end - chunk_start(jc)); };
+    // the chunk after jc, or jc again after the last one
+    auto next_chunk = [&](int64_t jc) { return jc + 1 < jend ? jc + 1 : jc; };
 
-    // o rows of a finished chunk: D-layout registers -> LDS -> whole row slices
-    f32x4_t oPrev[2];
-    auto stage_o = [&]() {
+    // third phase, both kinds of wave: S = gamma_C S + Kbar^T U on this wave's tiles
+    auto update_state = [&](const Fr (&uf)[2][2], const Fr (&fKB)[2], float4 gC) {
+        const float gcv[4] = {gC.x, gC.y, gC.z, gC.w};
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sO[(16 * w + 4 * cg + jj) * (kS + 4) + 16 * nb + m] = oPrev[nb][jj];
-    };
-    auto store_o = [&](int64_t tc, int ntc) {  // this wave's 16 rows; staged by this wave only
+            for (int jj = 0; jj < 4; ++jj) accS[i][jj] *= gcv[jj];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int rr = 16 * w + 8 * half + (lane >> 3);
-            const float4 x = *reinterpret_cast<const float4*>(&sO[rr * (kS + 4) + (lane & 7) * 4]);
-            if (rr < ntc) *reinterpret_cast<float4*>(o_l + (tc + rr) * (int64_t)rs_v) = x;
-        }
-    };
-
-    // one chunk with operands `cur`, loading the next chunk's operands into `nxt` on the way
-    auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
-        const int64_t t0 = start + jc * kC;
-        const int nt = (int)min<int64_t>(kC, end - t0);
-        const int64_t jn = jc + 1 < jend ? jc + 1 : jc;  // the current chunk again after the last one
-        const int64_t t0n = start + jn * kC;
-        const int ntn = (int)min<int64_t>(kC, end - t0n);
-        const char* recn = record(jn);
-
-        if constexpr (ST) {  // the state at the start of this chunk, for the backward pass
-            float* sj = cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0;
-#pragma unroll
-            for (int ci = 0; ci < CBW; ++ci)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        sj[(16 * (w * CBW + ci) + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accS[ci][nb][jj];
-        }
-
-        // v rows of this chunk (loaded during the previous chunk) into LDS, for the D layout
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i)
-            *reinterpret_cast<uint4*>(&sV[(vrow + i * VROWS) * kS + vpiece * VPL]) = cur.vraw[i];
-
-        // ---- chain 1:  X = V - Kt S (one pass), O1 = Qt S (full)
-        f32x4_t accO[2], accX[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) accX[nb] = accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const Fr sf = lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg);
-                accX[nb] = mma_fast(accX[nb], cur.fK[s], sf);
-                if constexpr (!SO) accO[nb] = mma_full(accO[nb], cur.fQ[s], sf);
-            }
-            load_qk(nxt, recn, s);
-        }
-        if (!SO && jc > jbeg) store_o(t0 - kC, kC);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x4_t xv;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const In raw = sV[(16 * w + 4 * cg + jj) * kS + 16 * nb + m];
-                float vj;
-                if constexpr (IN_F32) vj = raw;
-                else vj = bf16_bits_to_float(raw);
-                xv[jj] = vscale * vj - accX[nb][jj];
-            }
-            lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * w + 4 * cg, xv);
-            if constexpr (ST) {
-                float* xo = cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int row = 16 * w + 4 * cg + jj;
-                    xo[row * (int64_t)Dv + 16 * nb + m] = row < nt ? xv[jj] : 0.f;
+            for (int kb = 0; kb < 2; ++kb) {
+                if constexpr (TPW == 2) {  // tile i is column half i
+                    accS[i] = mma_full(accS[i], fKB[kb], uf[i][kb]);
+                } else {
+                    const Fr u = lds_frag<F32, kS, kC>(pU, 16 * nbt(i) + m, 32 * kb + 8 * cg);
+                    accS[i] = mma_full(accS[i], fKB[kb], u);
                 }
             }
         }
-        lds_barrier();  // (1)
+    };
+    auto store_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
+    };
+    auto read_u = [&](Fr (&uf)[2][2]) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) uf[hb][kb] = lds_frag<F32, kS, kC>(pU, 16 * hb + m, 32 * kb + 8 * cg);
+    };
+    auto load_kb = [&](Fr (&fKB)[2], float4& gC, const char* rec) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) fKB[kb] = gfrag_load<F32>(rec + R::KB + (cbw * 2 + kb) * 2 * kPlane, lane);
+        gC = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cbw + 4 * cg) * 4);
+    };
+    auto store_start_state = [&](int64_t jc) {  // mode 3: the state at the start of chunk jc
+        if constexpr (ST) {
+            float* sj = cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0;
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    sj[(16 * cbw + 4 * cg + jj) * (int64_t)Dv + 16 * nbt(i) + m] = accS[i][jj];
+        }
+    };
 
-        // ---- chain 2:  U = M^{-1} Diag(b) X  (rows of sub-block w)
-        {
+    if (w < 4) {
+        // ======================= state waves: X and U of row block rb
+        using Ops = ChainStateOps<DK, F32, IN_F32>;
+        constexpr int VLPR = kS / VPL;        // lanes per v row slice (bf16: 4, fp32: 8)
+        constexpr int VROWS = 64 / VLPR;      // v rows per load (bf16: 16, fp32: 8)
+        constexpr int VLOADS = 16 / VROWS;    // loads per lane (bf16: 1, fp32: 2)
+        const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
+        const int vrow = 16 * rb + lane / VLPR, vpiece = lane % VLPR;
+        const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * VPL;
+
+        auto load_k = [&](Ops& d, const char* rec, int s) {
+            d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (rb * KS + s) * R::KT_PLANES * kPlane, lane);
+        };
+        auto load_nv = [&](Ops& d, const char* rec, int64_t jc) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)  // blocks 0, 1 stop at token 31: their second step repeats the first
+                d.fN[kb] = gfrag_load<F32>(rec + R::NM + pair_of(rb, min(kb, nk - 1)) * 2 * kPlane, lane);
+            const int64_t t0 = chunk_start(jc);
+            const int nt = chunk_len(jc);
+#pragma unroll
+            for (int i = 0; i < VLOADS; ++i) {
+                const uint32_t rvo = (uint32_t)min(vrow + i * VROWS, nt - 1) * rs_v;
+                d.vraw[i] = *reinterpret_cast<const uint4*>(v_l + t0 * (int64_t)rs_v + rvo);
+            }
+        };
+        auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
+            const int nt = chunk_len(jc);
+            const int64_t jn = next_chunk(jc);
+            const char* recn = record(jn);
+            store_start_state(jc);
+#pragma unroll
+            for (int i = 0; i < VLOADS; ++i)
+                *reinterpret_cast<uint4*>(&sV[(vrow + i * VROWS) * kS + vpiece * VPL]) = cur.vraw[i];
+
+            // ---- phase 1:  X = V - Kt S (one pass)
+            f32x4_t accX[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    accX[nb] = mma_fast(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
+                load_k(nxt, recn, s);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                f32x4_t xv;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const In raw = sV[(16 * rb + 4 * cg + jj) * kS + 16 * nb + m];
+                    float vj;
+                    if constexpr (IN_F32) vj = raw;
+                    else vj = bf16_bits_to_float(raw);
+                    xv[jj] = vscale * vj - accX[nb][jj];
+                }
+                lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * rb + 4 * cg, xv);
+                if constexpr (ST) {
+                    float* xo = cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int row = 16 * rb + 4 * cg + jj;
+                        xo[row * (int64_t)Dv + 16 * nb + m] = row < nt ? xv[jj] : 0.f;
+                    }
+                }
+            }
+            lds_barrier();  // (1)
+
+            // ---- phase 2:  U = M^{-1} Diag(b) X
             f32x4_t accU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb >= nk) continue;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const Fr xf = lds_frag<F32, kS, kC>(pX, 16 * nb + m, 32 * kb + 8 * cg);
-                    accU[nb] = mma_full(accU[nb], cur.fN[kb], xf);
+                for (int nb = 0; nb < 2; ++nb)
+                    accU[nb] = mma_full(accU[nb], cur.fN[kb], lds_frag<F32, kS, kC>(pX, 16 * nb + m, 32 * kb + 8 * cg));
+            }
+            load_nv(nxt, recn, jn);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * rb + 4 * cg, accU[nb]);
+                if constexpr (ST) {
+                    float* uo = cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) *
+                                            (int64_t)Dv + col0;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) uo[(16 * rb + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accU[nb][jj];
                 }
             }
-            load_nv(nxt, recn, t0n, ntn);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * w + 4 * cg, accU[nb]);
-            if constexpr (ST) {
-                float* uo = cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) * (int64_t)Dv +
-                            col0;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        uo[(16 * w + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accU[nb][jj];
-            }
-        }
-        lds_barrier();  // (2)
+            lds_barrier();  // (2)
 
-        // ---- chain 3:  O = O1 + P U,  S = gamma_C S + Kbar^T U
-        {
+            // ---- phase 3:  S tiles
             Fr uf[2][2];
+            read_u(uf);
+            update_state(uf, cur.fKB, cur.gC);
+            load_kb(nxt.fKB, nxt.gC, recn);
+            store_state();
+            lds_barrier();  // (3)
+        };
+        Ops opsA, opsB;
+        if (jbeg < jend) {
+            const char* rec = record(jbeg);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) uf[nb][kb] = lds_frag<F32, kS, kC>(pU, 16 * nb + m, 32 * kb + 8 * cg);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (SO || kb >= nk) continue;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
-            }
-#pragma unroll
-            for (int ci = 0; ci < CBW; ++ci) {
-                const float gcv[4] = {cur.gC[ci].x, cur.gC[ci].y, cur.gC[ci].z, cur.gC[ci].w};
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) accS[ci][nb][jj] *= gcv[jj];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) accS[ci][nb] = mma_full(accS[ci][nb], cur.fKB[ci][kb], uf[nb][kb]);
-                load_pkb(nxt, recn, ci);
-            }
-#pragma unroll
-            for (int ci = 0; ci < CBW; ++ci) {
-                const int cb = w * CBW + ci;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) lds_store4<F32, kS, DK>(pS, 16 * nb + m, 16 * cb + 4 * cg, accS[ci][nb]);
-            }
+            for (int s = 0; s < KS; ++s) load_k(opsA, rec, s);
+            load_nv(opsA, rec, jbeg);
+            load_kb(opsA.fKB, opsA.gC, rec);
+        }
+        lds_barrier();
+        // two chunks per iteration, so that the operand sets alternate without copies
+        int64_t jc = jbeg;
+        for (; jc + 1 < jend; jc += 2) {
+            step(opsA, opsB, jc);
+            step(opsB, opsA, jc + 1);
+        }
+        if (jc < jend) step(opsA, opsB, jc);
+    } else {
+        // ======================= output waves: O of row block rb (and S tiles)
+        using Ops = ChainOutOps<DK, F32>;
+        const uint32_t rs_o = (uint32_t)H * (uint32_t)Dv;
+        float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + (lane & 7) * 4;
+
+        auto load_q = [&](Ops& d, const char* rec, int s) {
+            if constexpr (!SO) d.fQ[s] = gfrag_load<F32>(rec + R::QT + (rb * KS + s) * 2 * kPlane, lane);
+        };
+        auto load_p = [&](Ops& d, const char* rec) {
             if constexpr (!SO) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) oPrev[nb] = accO[nb];
-                stage_o();
+                for (int kb = 0; kb < 2; ++kb)
+                    d.fP[kb] = gfrag_load<F32>(rec + R::PM + pair_of(rb, min(kb, nk - 1)) * 2 * kPlane, lane);
             }
-        }
-        lds_barrier();  // (3)
-    };
-
-    Ops opsA, opsB;
-    if (jbeg < jend) load_all(opsA, jbeg);
-    lds_barrier();
-    for (int64_t jc = jbeg; jc < jend; jc += 2) {
-        step(opsA, opsB, jc);
-        if (jc + 1 < jend) step(opsB, opsA, jc + 1);
-    }
-    if (!SO && jbeg < jend) {
-        const int64_t t_last = start + (jend - 1) * kC;
-        store_o(t_last, (int)min<int64_t>(kC, end - t_last));
-    }
-    if (sdst) {
-#pragma unroll
-        for (int ci = 0; ci < CBW; ++ci) {
-            const int cb = w * CBW + ci;
+        };
+        // o rows of a finished chunk: D-layout registers -> LDS -> whole row slices (this wave's rows only)
+        auto stage_o = [&](const f32x4_t (&accO)[2]) {
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int c = 16 * cb + 4 * cg + jj;
-                    sdst[c * (int64_t)ld_dst + col_dst + 16 * nb + m] = accS[ci][nb][jj];
+                for (int jj = 0; jj < 4; ++jj) sO[(16 * rb + 4 * cg + jj) * (kS + 4) + 16 * nb + m] = accO[nb][jj];
+        };
+        auto store_o = [&](int64_t tc, int ntc) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int rr = 16 * rb + 8 * half + (lane >> 3);
+                const float4 x = *reinterpret_cast<const float4*>(&sO[rr * (kS + 4) + (lane & 7) * 4]);
+                if (rr < ntc) *reinterpret_cast<float4*>(o_l + (tc + rr) * (int64_t)rs_o) = x;
+            }
+        };
+        auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
+            const int64_t jn = next_chunk(jc);
+            const char* recn = record(jn);
+            store_start_state(jc);
+
+            // ---- phase 1:  O = Qt S, first half of the channels
+            f32x4_t accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            if constexpr (!SO) {
+#pragma unroll
+                for (int s = 0; s < KH; ++s) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        accO[nb] = mma_full(accO[nb], cur.fQ[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
+                    load_q(nxt, recn, s);
                 }
+                if (jc > jbeg) store_o(chunk_start(jc) - kC, kC);
+            }
+            lds_barrier();  // (1)
+
+            // ---- phase 2:  second half of the channels (S is rewritten only in phase 3)
+            if constexpr (!SO) {
+#pragma unroll
+                for (int s = KH; s < KS; ++s) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        accO[nb] = mma_full(accO[nb], cur.fQ[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
+                    load_q(nxt, recn, s);
+                }
+            }
+            lds_barrier();  // (2)
+
+            // ---- phase 3:  O += P U, S tiles
+            Fr uf[2][2];
+            read_u(uf);
+            if constexpr (!SO) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (kb >= nk) continue;
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
+                }
+                load_p(nxt, recn);
+            }
+            update_state(uf, cur.fKB, cur.gC);
+            load_kb(nxt.fKB, nxt.gC, recn);
+            store_state();
+            if constexpr (!SO) stage_o(accO);
+            lds_barrier();  // (3)
+        };
+        Ops opsA, opsB;
+        if (jbeg < jend) {
+            const char* rec = record(jbeg);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load_q(opsA, rec, s);
+            load_p(opsA, rec);
+            load_kb(opsA.fKB, opsA.gC, rec);
         }
+        lds_barrier();
+        // two chunks per iteration, so that the operand sets alternate without copies
+        int64_t jc = jbeg;
+        for (; jc + 1 < jend; jc += 2) {
+            step(opsA, opsB, jc);
+            step(opsB, opsA, jc + 1);
+        }
+        if (jc < jend) step(opsA, opsB, jc);
+        if (!SO && jbeg < jend) store_o(chunk_start(jend - 1), chunk_len(jend - 1));
+    }
+
+    if (sdst) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sdst[(16 * cbw + 4 * cg + jj) * (int64_t)ld_dst + col_dst + 16 * nbt(i) + m] = accS[i][jj];
     }
 }
 
@@ -954,7 +1014,7 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int NV = a.Dv / kS;
     if (P < 2) {
         const ChainMode cm{0, 1, 0, nullptr, nullptr};
-        hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(256), 0, st,
+        hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(kChainThreads), 0, st,
                            a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, cm,
                            static_cast<const char*>(ws));
         return hipGetLastError();
@@ -966,14 +1026,14 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     float* sfold = sx + a.N * a.H * (int64_t)(P - 1) * a.Dk * (a.Dv + a.Dk);
     const ChainMode c1{1, P, L, sx, nullptr};
     hipLaunchKernelGGL((chain_kernel<DK, F32, true>), dim3((unsigned)chain_grid(a.N * a.H * (P - 1), NV + DK / kS)),
-                       dim3(256), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H,
+                       dim3(kChainThreads), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H,
                        a.Dv, c1, static_cast<const char*>(ws));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((fold_kernel<DK>), dim3((unsigned)(a.N * a.H * NV)), dim3(256), 0, st, a.s0, sx, sfold, a.H,
                        a.Dv, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const ChainMode c2{2, P, L, nullptr, sfold};
-    hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(256), 0, st,
+    hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(kChainThreads), 0, st,
                        a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, c2,
                        static_cast<const char*>(ws));
     return hipGetLastError();
@@ -995,7 +1055,7 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
     if (e != hipSuccess) return e;
     const ChainMode cm{3, 1, 0, states, nullptr, xu};
     hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32, true>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
-                       dim3(256), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
+                       dim3(kChainThreads), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
                        a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
     return hipGetLastError();
 }
