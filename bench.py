@@ -188,7 +188,7 @@ def main():
                    "qkv": "bf16", "gates": "fp32", "state": "fp32", "output": "fp32", "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prep_kernel<128,false,false,false,false> + chain_kernel<128,false,false,false>", "kernel_ms": k_ms,
+                     "kernel": "prep_kernel<128,false,false,false,false> + chain_kernel<128,false,false,false,false>", "kernel_ms": k_ms,
                      "kernel_ms_min": k_min, "alg_bytes_per_launch": alg_bytes,
                      "workspace_bytes": ws.numel()},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
