@@ -437,11 +437,43 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     const float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
     const float* gin = grads + (slot * H + h) * (int64_t)GR::FLOATS;
 
+    // ---- every global operand of the chunk is requested up front (the phases below are short and
+    // would otherwise each wait out a full memory latency): four elements of each 64x64 block per
+    // thread, and one piece of eight q, k, g channels per thread (8 DK <= 1024 pieces)
+    static_assert(4096 % NT == 0 && 8 * DK <= NT, "one piece per thread");
+    constexpr int EPT = 4096 / NT;
+    float vN[EPT], vM[EPT], vA[EPT], vP[EPT];
+#pragma unroll
+    for (int a = 0; a < EPT; ++a) {
+        const int e = tid + a * NT;
+        vN[a] = gin[GR::DN + e];
+        vM[a] = rec[R::MIT + e];
+        vA[a] = rec[R::AB + e];
+        vP[a] = gin[GR::DP + e];
+    }
+    const bool has8 = tid < 8 * DK;
+    const int r8 = (8 * tid) / DK, c8 = (8 * tid) % DK;
+    Raw8<F32> xq8, xk8;
+    float4 zg[2];
+    if (has8) {
+        const int64_t idx = ((t0 + min(r8, nt - 1)) * H + h) * (int64_t)DK + c8;
+        if constexpr (F32) {
+            load_raw8(static_cast<const float*>(qv) + idx, xq8);
+            load_raw8(static_cast<const float*>(kv) + idx, xk8);
+        } else {
+            load_raw8(static_cast<const uint16_t*>(qv) + idx, xq8);
+            load_raw8(static_cast<const uint16_t*>(kv) + idx, xk8);
+        }
+        zg[0] = *reinterpret_cast<const float4*>(g + idx);
+        zg[1] = *reinterpret_cast<const float4*>(g + idx + 4);
+    }
+
     // ---- through N = Minv Diag(b) and Minv = M^{-1}
-    for (int e = tid; e < 4096; e += NT) {
-        const int r = e >> 6, i = e & 63;
-        sM1[r * 65 + i] = i <= r ? gin[GR::DN + e] : 0.f;  // dN (N is lower triangular)
-        sM2[i * 65 + r] = rec[R::MIT + e];                  // Minv (from its transpose)
+#pragma unroll
+    for (int a = 0; a < EPT; ++a) {
+        const int e = tid + a * NT, r = e >> 6, i = e & 63;
+        sM1[r * 65 + i] = i <= r ? vN[a] : 0.f;  // dN (N is lower triangular)
+        sM2[i * 65 + r] = vM[a];                 // Minv (from its transpose)
     }
     if (tid < 64) sB[tid] = rec[R::BT + tid];
     for (int e = tid; e < 64 * DK / 32; e += NT) sMk[e] = 0u;
@@ -460,36 +492,37 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     __syncthreads();
     for (int e = tid; e < 4096; e += NT) sM1[(e >> 6) * 65 + (e & 63)] *= sB[e & 63];  // dMinv = dN Diag(b)
     __syncthreads();
-    const int xr = tid >> 4, xs = 4 * (tid & 15);
-    {  // T1 = dMinv Minv^T
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int i = 0; i < 64; ++i) {
-            const float d = sM1[xr * 65 + i];
+    // T1 = dMinv Minv^T, then dM = -Minv^T T1, on fp32 MFMA: wave wv computes the 16x16 tile
+    // (row block wv / 4, column block wv % 4) of each; MFMA number kk takes reduction index
+    // 4 kk + lane / 16 in both operands
+    {
+        const int wv = tid >> 6, mm = tid & 15, cq = (tid >> 4) & 3, X = wv >> 2, S = wv & 3;
+        f32x4_t t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = fmaf(d, sM2[(xs + m) * 65 + i], acc[m]);
+        for (int kk = 0; kk < 16; ++kk) {
+            const int i = 4 * kk + cq;
+            t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sM1[(16 * X + mm) * 65 + i], sM2[(16 * S + mm) * 65 + i], t1,
+                                                      0, 0, 0);
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sM3[xr * 65 + xs + m] = acc[m];
-    }
-    __syncthreads();
-    {  // dM = -Minv^T T1
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int r = 0; r < 64; ++r) {
-            const float mi = sM2[r * 65 + xr];
+        for (int jj = 0; jj < 4; ++jj) sM3[(16 * X + 4 * cq + jj) * 65 + 16 * S + mm] = t1[jj];
+        __syncthreads();
+        f32x4_t dm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = fmaf(mi, sM3[r * 65 + xs + m], acc[m]);
+        for (int kk = 0; kk < 16; ++kk) {
+            const int r = 4 * kk + cq;
+            dm = __builtin_amdgcn_mfma_f32_16x16x4f32(sM2[r * 65 + 16 * X + mm], sM3[r * 65 + 16 * S + mm], dm, 0, 0,
+                                                      0);
         }
-        __syncthreads();  // every thread has read dMinv
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sM1[xr * 65 + xs + m] = -acc[m];
+        for (int jj = 0; jj < 4; ++jj) sM1[(16 * X + 4 * cq + jj) * 65 + 16 * S + mm] = -dm[jj];
     }
     __syncthreads();
-    for (int e = tid; e < 4096; e += NT) {
-        const int r = e >> 6, i = e & 63;
-        sM3[r * 65 + i] = rec[R::AB + e];                   // Abar
-        sM2[r * 65 + i] = i <= r ? gin[GR::DP + e] : 0.f;   // dP (P is lower triangular with the diagonal)
+#pragma unroll
+    for (int a = 0; a < EPT; ++a) {
+        const int e = tid + a * NT, r = e >> 6, i = e & 63;
+        sM3[r * 65 + i] = vA[a];                 // Abar
+        sM2[r * 65 + i] = i <= r ? vP[a] : 0.f;  // dP (P is lower triangular with the diagonal)
     }
     __syncthreads();
     if (tid < 64) sDB[tid] = dbn;
@@ -510,20 +543,17 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
         __syncthreads();  // sDB holds the column part
         if ((tid & 15) == 0) sDB[r] += p;
     }
-    // ---- q, k and the running gate sums (eight consecutive channels per piece)
-#pragma unroll 1
-    for (int e8 = tid; e8 < 8 * DK; e8 += NT) {
-        const int r = (8 * e8) / DK, c = (8 * e8) % DK;
-        float x[8], y[8], z[8];
-        const int64_t idx = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + c;
-        if constexpr (F32) {
-            load8_as_float(static_cast<const float*>(qv) + idx, x);
-            load8_as_float(static_cast<const float*>(kv) + idx, y);
-        } else {
-            load8_as_float(static_cast<const uint16_t*>(qv) + idx, x);
-            load8_as_float(static_cast<const uint16_t*>(kv) + idx, y);
-        }
-        load8_as_float(g + idx, z);
+    // ---- q, k and the clamped gates to LDS (the piece loaded at the start).  At DK = 128 the piece
+    // of thread t is exactly its own elements of the final step (row t/16, channels 8 (t%16)..), so
+    // q and k stay in registers for it.
+    constexpr bool OWN8 = 8 * DK == NT;
+    float qown[CPT], kown[CPT];
+    if (has8) {
+        float x[8], y[8];
+        raw8_to_float<F32>(xq8, x);
+        raw8_to_float<F32>(xk8, y);
+        const float z[8] = {zg[0].x, zg[0].y, zg[0].z, zg[0].w, zg[1].x, zg[1].y, zg[1].z, zg[1].w};
+        const int r = r8, c = c8;
         const float msk = r < nt ? 1.f : 0.f;
         uint32_t bits = 0u;
 #pragma unroll
@@ -532,6 +562,10 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
             sk[r * LD + c + jj] = msk * y[jj];
             sG[r * LD + c + jj] = msk * fminf(fmaxf(z[jj], -5.f), 0.f);
             bits |= (z[jj] < -5.f || z[jj] > 0.f) ? (1u << jj) : 0u;
+            if constexpr (OWN8) {
+                qown[jj] = msk * x[jj];
+                kown[jj] = msk * y[jj];
+            }
         }
         atomicOr(&sMk[r * (DK / 32) + c / 32], bits << (c % 32));
     }
@@ -595,77 +629,138 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     }
     __syncthreads();
 
-    // ---- row ar against columns i <= ar: aq (from P, for dq), ak1 (from Abar, for dk)
-    float aq[CPT], ak1[CPT], ak2[CPT];
+    // the column-sum gradients of this thread's own elements, loaded while the products below run
+    float pQt[CPT], pKt[CPT], pKb[CPT];
 #pragma unroll
-    for (int b = 0; b < CPT; ++b) aq[b] = ak1[b] = ak2[b] = 0.f;
+    for (int b = 0; b < CPT; b += 4) {
+        const float* base = gin + ar * DK + ac + b;
+        const float4 u = *reinterpret_cast<const float4*>(base + GR::DQT);
+        const float4 v4 = *reinterpret_cast<const float4*>(base + GR::DKT);
+        const float4 w4 = *reinterpret_cast<const float4*>(base + GR::DKB);
+        pQt[b] = u.x; pQt[b + 1] = u.y; pQt[b + 2] = u.z; pQt[b + 3] = u.w;
+        pKt[b] = v4.x; pKt[b + 1] = v4.y; pKt[b + 2] = v4.z; pKt[b + 3] = v4.w;
+        pKb[b] = w4.x; pKb[b + 1] = w4.y; pKb[b + 2] = w4.z; pKb[b + 3] = w4.w;
+    }
+
+    // ---- the decayed Gram contractions on fp32 MFMA (16x16x4).  Wave wv owns the (row block R,
+    // 16-channel block cb) pairs below and, for each, three 16x16 results at rows 16R.. and
+    // channels 16cb.. (F_RR = D_R):
+    //   aq  = sum_{I <= R} F_RI o (dP[R, I] (k B1)[I])          (for dq)
+    //   ak1 = sum_{I <= R} F_RI o (dAbar[R, I] (k B1)[I])       (for dk)
+    //   ak2 = sum_{R2 >= R} F_{R2, R} o (dAbar[R2, R]^T (k A1)[R2] + dP[R2, R]^T (q A1)[R2])
+    // The decay factor depends only on the channel (the result's column), so it scales each block
+    // pair's product as a whole.  MFMA number kk takes reduction index 4 kk + lane / 16 in both
+    // operands; every pair costs 8 (R + 1) + 8 (4 - R) = 40 products.
+    constexpr int NCB = DK / 16, PPW = 4 * NCB / 16;  // pairs per wave
+    const int wv = tid >> 6, mm = tid & 15, cq = (tid >> 4) & 3;
+    f32x4_t oq[PPW], ok1[PPW], ok2[PPW];
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+        const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
+        const int c = 16 * cb + mm;
+        f32x4_t aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f}, aK2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-    for (int I = 0; I <= blk; ++I) {
-        float pq[CPT], pk[CPT];
+        for (int I = 0; I <= R; ++I) {
+            f32x4_t tq = {0.f, 0.f, 0.f, 0.f}, tk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) pq[b] = pk[b] = 0.f;
-#pragma unroll 4
-        for (int i = 16 * I; i < 16 * I + 16; ++i) {
-            const float dp = sM2[ar * 65 + i], da = sM1[ar * 65 + i];  // zero unless i <= ar
+            for (int kk = 0; kk < 4; ++kk) {
+                const int i = 16 * I + 4 * kk + cq;
+                const float bv = sG[i * LD + c];
+                tq = __builtin_amdgcn_mfma_f32_16x16x4f32(sM2[(16 * R + mm) * 65 + i], bv, tq, 0, 0, 0);
+                tk = __builtin_amdgcn_mfma_f32_16x16x4f32(sM1[(16 * R + mm) * 65 + i], bv, tk, 0, 0, 0);
+            }
+            const float f = I < R ? sFf[(R * (R - 1) / 2 + I) * DK + c] : sDf[R * DK + c];
 #pragma unroll
-            for (int b = 0; b < CPT; ++b) {
-                const float kb = sG[i * LD + ac + b];
-                pq[b] = fmaf(dp, kb, pq[b]);
-                pk[b] = fmaf(da, kb, pk[b]);
+            for (int jj = 0; jj < 4; ++jj) {
+                aQ[jj] = fmaf(f, tq[jj], aQ[jj]);
+                aK[jj] = fmaf(f, tk[jj], aK[jj]);
             }
         }
-        const float* f = I < blk ? &sFf[(blk * (blk - 1) / 2 + I) * DK + ac] : &sDf[blk * DK + ac];
+#pragma unroll 1
+        for (int R2 = R; R2 < 4; ++R2) {
+            f32x4_t t2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            aq[b] = fmaf(f[b], pq[b], aq[b]);
-            ak1[b] = fmaf(f[b], pk[b], ak1[b]);
+            for (int kk = 0; kk < 4; ++kk) {
+                const int r = 16 * R2 + 4 * kk + cq;
+                t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sM1[r * 65 + 16 * R + mm], sk[r * LD + c], t2, 0, 0, 0);
+                t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sM2[r * 65 + 16 * R + mm], sq[r * LD + c], t2, 0, 0, 0);
+            }
+            const float f = R2 > R ? sFf[(R2 * (R2 - 1) / 2 + R) * DK + c] : sDf[R * DK + c];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) aK2[jj] = fmaf(f, t2[jj], aK2[jj]);
+        }
+        oq[p] = aQ;
+        ok1[p] = aK;
+        ok2[p] = aK2;
+    }
+    __syncthreads();  // every operand has been read: sq, sk, sG take the three results
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+        const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int e = (16 * R + 4 * cq + jj) * LD + 16 * cb + mm;
+            sq[e] = oq[p][jj];
+            sk[e] = ok1[p][jj];
+            sG[e] = ok2[p][jj];
         }
     }
-    // ---- row ar as the column index i against rows r >= i: ak2 (for dk)
-#pragma unroll 1
-    for (int R_ = blk; R_ < 4; ++R_) {
-        float pp[CPT];
+    __syncthreads();
+    float aq[CPT], ak1[CPT], ak2[CPT];
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) pp[b] = 0.f;
-#pragma unroll 4
-        for (int r = 16 * R_; r < 16 * R_ + 16; ++r) {
-            const float da = sM1[r * 65 + ar], dp = sM2[r * 65 + ar];  // zero unless r >= ar
-#pragma unroll
-            for (int b = 0; b < CPT; ++b)
-                pp[b] = fmaf(da, sk[r * LD + ac + b], fmaf(dp, sq[r * LD + ac + b], pp[b]));
-        }
-        const float* f = R_ > blk ? &sFf[(R_ * (R_ - 1) / 2 + blk) * DK + ac] : &sDf[blk * DK + ac];
-#pragma unroll
-        for (int b = 0; b < CPT; ++b) ak2[b] = fmaf(f[b], pp[b], ak2[b]);
+    for (int b = 0; b < CPT; ++b) {
+        const int e = ar * LD + ac + b;
+        aq[b] = sq[e];
+        ak1[b] = sk[e];
+        ak2[b] = sG[e];
     }
     // ---- own elements: dq, dk, and dG (after every thread has read the tables)
     float dG[CPT], colp[CPT];
     {
         const int r = ar;
         float qx[CPT], kx[CPT];
-        const int64_t idx0 = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + ac;
+        if constexpr (OWN8) {
 #pragma unroll
-        for (int b = 0; b < CPT; ++b) {
-            qx[b] = r < nt ? load_in<F32>(qv, idx0 + b) : 0.f;
-            kx[b] = r < nt ? load_in<F32>(kv, idx0 + b) : 0.f;
+            for (int b = 0; b < CPT; ++b) {
+                qx[b] = qown[b];
+                kx[b] = kown[b];
+            }
+        } else {
+            const int64_t idx0 = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + ac;
+#pragma unroll
+            for (int b = 0; b < CPT; ++b) {
+                qx[b] = r < nt ? load_in<F32>(qv, idx0 + b) : 0.f;
+                kx[b] = r < nt ? load_in<F32>(kv, idx0 + b) : 0.f;
+            }
+        }
+        float gs[CPT], ge[CPT], gc[CPT], dqv[CPT], dkv[CPT];  // running sums at the block start / end, G_C
+#pragma unroll
+        for (int b = 0; b < CPT; b += 4) {
+            const float4 u = *reinterpret_cast<const float4*>(&sGb[blk * DK + ac + b]);
+            const float4 v4 = *reinterpret_cast<const float4*>(&sGb[(blk + 1) * DK + ac + b]);
+            const float4 w4 = *reinterpret_cast<const float4*>(&sGb[4 * DK + ac + b]);
+            gs[b] = u.x; gs[b + 1] = u.y; gs[b + 2] = u.z; gs[b + 3] = u.w;
+            ge[b] = v4.x; ge[b + 1] = v4.y; ge[b + 2] = v4.z; ge[b + 3] = v4.w;
+            gc[b] = w4.x; gc[b + 1] = w4.y; gc[b + 2] = w4.z; gc[b + 3] = w4.w;
         }
 #pragma unroll
         for (int b = 0; b < CPT; ++b) {
-            const int c = ac + b;
-            const float a1 = __expf(Gr[b] - sGb[blk * DK + c]);
-            const float b1 = __expf(sGb[(blk + 1) * DK + c] - Gr[b]);
+            const float a1 = __expf(Gr[b] - gs[b]);
+            const float b1 = __expf(ge[b] - Gr[b]);
             const float q_ = a1 * aq[b], k1 = a1 * ak1[b], k2 = b1 * ak2[b];
-            const float gam = __expf(Gr[b]), gbar = __expf(sGb[4 * DK + c] - Gr[b]);
-            const float dQt = gin[GR::DQT + r * DK + c], dKt = gin[GR::DKT + r * DK + c];
-            const float dKb = gin[GR::DKB + r * DK + c];
-            const float dqv = fmaf(gam, dQt, q_);
-            const float dkv = fmaf(gam, dKt, fmaf(gbar, dKb, k1 + k2));
+            const float gam = __expf(Gr[b]), gbar = __expf(gc[b] - Gr[b]);
+            const float dQt = pQt[b], dKt = pKt[b], dKb = pKb[b];
+            dqv[b] = fmaf(gam, dQt, q_);
+            dkv[b] = fmaf(gam, dKt, fmaf(gbar, dKb, k1 + k2));
             dG[b] = qx[b] * (gam * dQt + q_) + kx[b] * (gam * dKt - gbar * dKb + k1 - k2);
             colp[b] = kx[b] * gbar * dKb;
-            if (r < nt) {
-                const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + c;
-                dq[idx] = dqv;
-                dk[idx] = dkv;
+        }
+        if (r < nt) {
+            const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + ac;
+#pragma unroll
+            for (int b = 0; b < CPT; b += 4) {
+                *reinterpret_cast<float4*>(dq + idx + b) = make_float4(dqv[b], dqv[b + 1], dqv[b + 2], dqv[b + 3]);
+                *reinterpret_cast<float4*>(dk + idx + b) = make_float4(dkv[b], dkv[b + 1], dkv[b + 2], dkv[b + 3]);
             }
         }
     }
