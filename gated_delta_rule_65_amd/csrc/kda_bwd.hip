@@ -310,9 +310,19 @@ __device__ __forceinline__ Frag<false> frag_rows(const float* base, int64_t ld, 
 }
 
 // Per (chunk, head): the products summed over the value columns, all contracting over the stored
-// column index of row-major operands (so every fragment is read straight from memory):
+// column index of row-major operands:
 //   dQt = dO S^T, dKt = -dX S^T, dKb = U dS'^T (64 x DK);  dP = dO U^T, dN = dU X^T (64 x 64);
 //   dgamma = rowsum(S o dS').  Split-bf16 three-pass products; wave w owns rows 16w..16w+15.
+// Per 32-column step the operands every wave needs (S and dS' rows, U and X rows) are read from
+// memory once per workgroup, split once and staged in LDS; the next step's pieces are requested
+// while the current step's products run.  A wave's own rows (dO, dX, U, dU) come straight from memory.
+template <int DK>
+struct ColsumLds {
+    using MS = LMat<false, DK, 32>;  // S, dS' column step [c][n]
+    using MR = LMat<false, 64, 32>;  // U, X column step [t][n]
+    static constexpr int S = 0, DS = S + MS::BYTES, U = DS + MS::BYTES, X = U + MR::BYTES, TOTAL = X + MR::BYTES;
+};
+
 template <int DK>
 __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restrict__ d_o,
                                                             const int32_t* __restrict__ cu, int64_t T_fixed,
@@ -323,7 +333,10 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
                                                             const float* __restrict__ dudx,
                                                             float* __restrict__ grads) {
     using GR = GRec<DK>;
+    using L = ColsumLds<DK>;
     constexpr int CB = DK / 16;
+    constexpr int PS = DK / 8;  // S / dS' values staged per thread per step (32 DK / 256)
+    __shared__ __align__(16) char smem[L::TOTAL];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -341,18 +354,44 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
     const int orow = 16 * w + m;
     const float* dO = d_o + ((t0 + min(orow, nt - 1)) * H + h) * (int64_t)Dv;
     const float omask = orow < nt ? 1.f : 0.f;
+    // staging pieces: S and dS' rows sr (PS columns from sc), U and X rows ur (8 columns from uc)
+    const int sr = (tid * PS) / 32, sc = (tid * PS) % 32, ur = tid >> 2, uc = 8 * (tid & 3);
+    float vS[PS], vD[PS], vU[8], vX[8];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < PS; j += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(S + sr * (int64_t)Dv + k0 + sc + j);
+            const float4 b = *reinterpret_cast<const float4*>(dS + sr * (int64_t)Dv + k0 + sc + j);
+            vS[j] = a.x; vS[j + 1] = a.y; vS[j + 2] = a.z; vS[j + 3] = a.w;
+            vD[j] = b.x; vD[j + 1] = b.y; vD[j + 2] = b.z; vD[j + 3] = b.w;
+        }
+        load8_as_float(U + ur * (int64_t)Dv + k0 + uc, vU);
+        load8_as_float(X + ur * (int64_t)Dv + k0 + uc, vX);
+    };
 
     f32x4_t aQ[CB], aK[CB], aB[CB], aP[4], aN[4];
 #pragma unroll
     for (int i = 0; i < CB; ++i) aQ[i] = aK[i] = aB[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) aP[i] = aN[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float dgam[CB];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) dgam[i] = 0.f;
+    float dgam = 0.f;  // partial row sum of S o dS' for row sr
 
+    fetch(0);
     for (int k0 = 0; k0 < Dv; k0 += 32) {
-        float x[8], y[8];
+        __syncthreads();  // the previous step's fragments have been read
+#pragma unroll
+        for (int j = 0; j < PS; j += 8) {
+            lds_store8<false, DK, 32>(smem + L::S, sr, sc + j, vS + j);
+            lds_store8<false, DK, 32>(smem + L::DS, sr, sc + j, vD + j);
+        }
+#pragma unroll
+        for (int j = 0; j < PS; ++j) dgam = fmaf(vS[j], vD[j], dgam);
+        lds_store8<false, 64, 32>(smem + L::U, ur, uc, vU);
+        lds_store8<false, 64, 32>(smem + L::X, ur, uc, vX);
+        __syncthreads();
+        if (k0 + 32 < Dv) fetch(k0 + 32);
+
+        float x[8];
         load8_as_float(dO + k0 + 8 * cg, x);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] *= omask;
@@ -363,19 +402,16 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
         const Frag<false> fdU = frag_rows(dU, Dv, 16 * w, k0, m, cg, x);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const Frag<false> fS = frag_rows(S, Dv, 16 * cb, k0, m, cg, x);
-            const Frag<false> fdS = frag_rows(dS, Dv, 16 * cb, k0, m, cg, y);
+            const Frag<false> fS = lds_frag<false, DK, 32>(smem + L::S, 16 * cb + m, 8 * cg);
+            const Frag<false> fdS = lds_frag<false, DK, 32>(smem + L::DS, 16 * cb + m, 8 * cg);
             aQ[cb] = mma_full(aQ[cb], fO, fS);
             aK[cb] = mma_full(aK[cb], fX, fS);
             aB[cb] = mma_full(aB[cb], fU, fdS);
-            if (w == 0)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) dgam[cb] = fmaf(x[j], y[j], dgam[cb]);
         }
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
-            aP[ib] = mma_full(aP[ib], fO, frag_rows(U, Dv, 16 * ib, k0, m, cg, x));
-            aN[ib] = mma_full(aN[ib], fdU, frag_rows(X, Dv, 16 * ib, k0, m, cg, x));
+            aP[ib] = mma_full(aP[ib], fO, lds_frag<false, 64, 32>(smem + L::U, 16 * ib + m, 8 * cg));
+            aN[ib] = mma_full(aN[ib], fdU, lds_frag<false, 64, 32>(smem + L::X, 16 * ib + m, 8 * cg));
         }
     }
     float* out = grads + ch * (int64_t)GR::FLOATS;
@@ -394,15 +430,10 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
             out[GR::DN + r * 64 + 16 * ib + m] = aN[ib][i];
         }
     }
-    if (w == 0) {  // rows 16cb + m: sum the four lane groups' column ranges
+    // dgamma: the 32 / PS threads of a row are adjacent
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            float v = dgam[cb];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            if (cg == 0) out[GR::DGM + 16 * cb + m] = v;
-        }
-    }
+    for (int off = 1; off < 32 / PS; off <<= 1) dgam += __shfl_xor(dgam, off);
+    if (sc == 0) out[GR::DGM + sr] = dgam;
 }
 
 // ============================================================================ to dq, dk, dg, db
