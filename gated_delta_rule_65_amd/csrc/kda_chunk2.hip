@@ -217,7 +217,8 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
 }
 
 // F32: precision policy of the records (fp32 MFMA operands, else split bf16); IN_F32: q/k input type.
-// BWD: also write the backward pass's plain operands (BwdRec) to brecs.
+// BWD: also write the backward pass's plain operands (BwdRec) to brecs, and leave out the Qt and P fragments of
+// the record (only the state-only chain reads these records).
 template <int DK, bool F32, bool PRO, bool IN_F32 = F32, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                       const void* __restrict__ gv, const void* __restrict__ bv,
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         Fr fq, fk;
         fq.set(xq);
         fk.set_hi_only(xk);
-        gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);
+        if constexpr (!BWD) gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);  // the state-only chain reads no Qt
         gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane, fk);
         if constexpr (BWD) {  // Qt^T, Kt^T [c][r]; rows past the end as zeros
             const float z = rv ? 1.f : 0.f;
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     // ---- P rows of block w to the record
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        if (kb >= steps_of(w)) continue;
+        if (BWD || kb >= steps_of(w)) continue;  // the state-only chain reads no P
         float x[8];
         lds_read8(&sP[r * 68 + 32 * kb + 8 * cg], x);
         Fr f;
