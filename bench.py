@@ -341,7 +341,7 @@ def measure_backward(args, torch, kda, kda_inputs, device_inputs):
     return {"workload": name + "_backward", "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
-            "workspace_bytes": ws.numel(), "arith": "fp32"}
+            "workspace_bytes": ws.numel(), "arith": "fp32 accumulation; split-bf16 three-pass products in the state recompute and column sums, fp32 MFMA elsewhere"}
 
 
 if __name__ == "__main__":

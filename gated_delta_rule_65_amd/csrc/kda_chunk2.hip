@@ -88,11 +88,12 @@ __device__ __forceinline__ Frag<F32> gfrag_load_hi(const char* grp, int lane) {
 __host__ __device__ constexpr int steps_of(int w) { return w >= 2 ? 2 : 1; }
 __host__ __device__ constexpr int pair_of(int w, int kb) { return w < 2 ? w : 2 * w - 2 + kb; }
 
-// Operand record of one (chunk, head): byte offsets of its parts.
-template <int DK, bool F32>
+// Operand record of one (chunk, head): byte offsets of its parts.  KT2: Kt has both planes (the fp32
+// policy, and the split policy of the backward's state pass, whose products all run in full precision).
+template <int DK, bool F32, bool KT2 = F32>
 struct Rec {
     static constexpr int KS = DK / 32;                      // 32-channel steps
-    static constexpr int KT_PLANES = F32 ? 2 : 1;
+    static constexpr int KT_PLANES = KT2 ? 2 : 1;
     static constexpr int64_t QT = 0;                        // Qt rows:    [w 4][s KS], 2 planes
     static constexpr int64_t KT = QT + 4 * KS * 2 * kPlane;  // Kt rows:    [w 4][s KS], KT_PLANES
     static constexpr int64_t KB = KT + 4 * KS * KT_PLANES * kPlane;  // Kbar^T rows: [c-block DK/16][kb 2], 2 planes
@@ -171,7 +172,8 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
         }
         Fr fqE, fkE, fkd;
         fqE.set(x1);
-        fkE.set_hi_only(x2);
+        if constexpr (BWD) fkE.set(x2);
+        else fkE.set_hi_only(x2);
         fkd.set(x3);
 #pragma unroll
         for (int I = 0; I < W; ++I) {
@@ -188,10 +190,10 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
             }
             Fr colf;
             colf.set(cx);
-            accA[I] = mma_fast(accA[I], fkE, colf);
+            accA[I] = BWD ? mma_full(accA[I], fkE, colf) : mma_fast(accA[I], fkE, colf);
             accP[I] = mma_full(accP[I], fqE, colf);
         }
-        accA[W] = mma_fast(accA[W], fkE, fkd);
+        accA[W] = BWD ? mma_full(accA[W], fkE, fkd) : mma_fast(accA[W], fkE, fkd);
         accP[W] = mma_full(accP[W], fqE, fkd);
     }
 #pragma unroll
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     // input prologue; PRO = false compiles the plain form (fp32 log alpha and beta, q and k as given)
     const Prologue pf{PRO && pro.g_bf16, PRO && pro.g_logit, PRO && pro.b_bf16, PRO && pro.b_logit,
                       PRO && pro.l2norm};
-    using R = Rec<DK, F32>;
+    using R = Rec<DK, F32, F32 || BWD>;
     constexpr int KS = DK / 32;
     const In* __restrict__ q = static_cast<const In*>(qv);
     const In* __restrict__ k = static_cast<const In*>(kv);
@@ -369,9 +371,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         }
         Fr fq, fk;
         fq.set(xq);
-        fk.set_hi_only(xk);
+        if constexpr (BWD) fk.set(xk);
+        else fk.set_hi_only(xk);
         if constexpr (!BWD) gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);  // the state-only chain reads no Qt
-        gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * R::KT_PLANES * kPlane, lane, fk);
+        if constexpr (R::KT_PLANES == 2) gfrag_store<F32>(rec + R::KT + (w * KS + s) * 2 * kPlane, lane, fk);
+        else gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * kPlane, lane, fk);
         if constexpr (BWD) {  // Qt^T, Kt^T [c][r]; rows past the end as zeros
             const float z = rv ? 1.f : 0.f;
 #pragma unroll
@@ -567,7 +571,7 @@ struct ChainMode {
 // 16-column half) tiles of S in the third phase.  Both kinds of wave pass the same three barriers
 // per chunk.
 template <int DK, bool F32, bool SO, bool IN_F32 = F32, bool ST = false>
-__global__ __launch_bounds__(kChainThreads, SO && !F32 ? 4 : 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
+__global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                                  float* __restrict__ o, float* s_final,
                                                                  const int32_t* __restrict__ cu_seqlens,
                                                                  int64_t T_fixed, int64_t total, int64_t N, int H,
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 ? 4 : 1) void chain_kerne
     using In = typename std::conditional<IN_F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
     using L = ChainLds<DK, F32>;
-    using R = Rec<DK, F32>;
+    using R = Rec<DK, F32, F32 || ST>;
     constexpr int KS = DK / 32;
     constexpr int KH = KS / 2;                      // Qt S steps in the first phase (the rest in the second)
     constexpr int TPW = DK / 64;                    // S tiles per wave (all in one channel block)
@@ -703,7 +707,8 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 ? 4 : 1) void chain_kerne
         const In* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * VPL;
 
         auto load_k = [&](Ops& d, const char* rec, int s) {
-            d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (rb * KS + s) * R::KT_PLANES * kPlane, lane);
+            if constexpr (R::KT_PLANES == 2) d.fK[s] = gfrag_load<F32>(rec + R::KT + (rb * KS + s) * 2 * kPlane, lane);
+            else d.fK[s] = gfrag_load_hi<F32>(rec + R::KT + (rb * KS + s) * kPlane, lane);
         };
         auto load_nv = [&](Ops& d, const char* rec, int64_t jc) {
 #pragma unroll
@@ -732,7 +737,8 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 ? 4 : 1) void chain_kerne
             for (int s = 0; s < KS; ++s) {
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    accX[nb] = mma_fast(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
+                    accX[nb] = ST ? mma_full(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg))
+                                  : mma_fast(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
                 load_k(nxt, recn, s);
             }
 #pragma unroll
@@ -1040,8 +1046,9 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     return hipGetLastError();
 }
 
-// States at every chunk start (fp32 records and products for both input types), for the backward
-// pass: prep into `recs` (chunk_slots(a) * H records of chunk_record_bytes(Dk, true)) and the plain
+// States at every chunk start, for the backward pass: split-bf16 records with every product in three
+// passes (Kt with both planes, the Gram of k included; fp32 states and accumulators) for both input
+// types.  prep into `recs` (chunk_slots(a) * H records of chunk_record_bytes(Dk, true)) and the plain
 // backward operands into `brecs`, then the state-only chain in mode 3 writing `states` [slot][h][Dk][Dv]
 // and X, U of every chunk to `xu` [slot][h][2][64][Dv].
 template <int DK, bool IN_F32>
@@ -1049,13 +1056,13 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
                                 hipStream_t st) {
     const int64_t prep_grid = chunk_slots(a) * a.H;
     if (prep_grid > 0)
-        hipLaunchKernelGGL((prep_kernel<DK, true, false, IN_F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st,
+        hipLaunchKernelGGL((prep_kernel<DK, false, false, IN_F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st,
                            a.q, a.k, a.g, a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro,
                            static_cast<char*>(recs), brecs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const ChainMode cm{3, 1, 0, states, nullptr, xu};
-    hipLaunchKernelGGL((chain_kernel<DK, true, true, IN_F32, true>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
+    hipLaunchKernelGGL((chain_kernel<DK, false, true, IN_F32, true>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
                        dim3(kChainThreads), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
                        a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
     return hipGetLastError();
