@@ -20,9 +20,10 @@
 //   then through Abar, P, Qt, Kt, Kb and gamma to q, k and G, and from G to g by a reverse
 //   running sum inside the chunk (the clamp passes the gradient where -5 <= g <= 0).
 //
-// Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) and the state at every chunk start come from
-// the forward pass's prep kernel in its backward form and its chain kernel in mode 3, both with fp32
-// records (launch_chunk_states).  Then three kernels, fp32 arithmetic:
+// Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) (fp32) and the state at every chunk start come
+// from the forward pass's prep kernel in its backward form and its chain kernel in mode 3, on split-bf16
+// records with every product in three passes (launch_chunk_states).  Then three kernels, fp32
+// accumulation (the column sums as three-pass split-bf16 products, the others on fp32 MFMA):
 //   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS', dU, dX of every
 //                      chunk, dv = dX, ds0
 //   bwd_colsum_kernel  per (chunk, head): the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma)

@@ -176,7 +176,9 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
  *   ds0      : [B, H, Dk, Dv] float32 gradient of the initial state (written), or NULL
  * q, k, v, g, beta, s0 as for kda_chunk_fwd (s0 NULL = zero initial state).  The workspace is
  * required (kda_chunk_bwd_workspace_bytes; no initial contents needed); a NULL or smaller one is
- * rejected.  The computation runs in float32 throughout.  T = 0: only ds0 = d_sfinal (or 0).
+ * rejected.  Accumulation and the carried states are float32; the matrix products run either in
+ * float32 or as three-pass split-bf16 products (hi*hi + hi*lo + lo*hi, about 16 significant bits per
+ * operand).  T = 0: only ds0 = d_sfinal (or 0).
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* s0, const float* d_o, const float* d_sfinal, float* dq, float* dk, float* dv,

@@ -2,7 +2,8 @@
 
 Loss L = <d_o, o> + <d_sfinal, S_T> with seeded random d_o, d_sfinal; every gradient (dq, dk, dv,
 dg, dbeta, ds0) is compared element by element: max|gpu - oracle| <= tol * RMS(oracle) per tensor.
-The kernels compute in fp32 for both input types, so one tolerance serves both.
+The kernels accumulate in fp32 and run their products in fp32 or as three-pass split-bf16 products
+for both input types, so one tolerance serves both.
 """
 import numpy as np
 import pytest
