@@ -98,6 +98,12 @@ __device__ __forceinline__ bool slot_chunk(const int32_t* cu, int64_t slot, int6
     return true;
 }
 
+// x where keep holds, else +0.  A bit mask rather than a select, so that a value loaded early is
+// not turned back into a load on the kept branch only (which would wait for every later load).
+__device__ __forceinline__ float keep_if(float x, bool keep) {
+    return __uint_as_float(__float_as_uint(x) & (keep ? 0xffffffffu : 0u));
+}
+
 template <bool F32>
 __device__ __forceinline__ float load_in(const void* p, int64_t i) {
     if constexpr (F32) return static_cast<const float*>(p)[i];
@@ -474,14 +480,18 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     // thread, and one piece of eight q, k, g channels per thread (8 DK <= 1024 pieces)
     static_assert(4096 % NT == 0 && 8 * DK <= NT, "one piece per thread");
     constexpr int EPT = 4096 / NT;
+    // (in the order they are consumed: the first phase waits only for b, dN and Minv)
+    const float vb = tid < 64 ? rec[R::BT + tid] : 0.f;
     float vN[EPT], vM[EPT], vA[EPT], vP[EPT];
 #pragma unroll
     for (int a = 0; a < EPT; ++a) {
-        const int e = tid + a * NT;
-        vN[a] = gin[GR::DN + e];
-        vM[a] = rec[R::MIT + e];
-        vA[a] = rec[R::AB + e];
-        vP[a] = gin[GR::DP + e];
+        vN[a] = gin[GR::DN + tid + a * NT];
+        vM[a] = rec[R::MIT + tid + a * NT];
+    }
+#pragma unroll
+    for (int a = 0; a < EPT; ++a) {
+        vA[a] = rec[R::AB + tid + a * NT];
+        vP[a] = gin[GR::DP + tid + a * NT];
     }
     const bool has8 = tid < 8 * DK;
     const int r8 = (8 * tid) / DK, c8 = (8 * tid) % DK;
@@ -499,15 +509,16 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
         zg[0] = *reinterpret_cast<const float4*>(g + idx);
         zg[1] = *reinterpret_cast<const float4*>(g + idx + 4);
     }
+    const float vgd = rec[R::GM + tid % DK] * gin[GR::DGM + tid % DK];  // gamma dgamma of channel tid % DK
 
     // ---- through N = Minv Diag(b) and Minv = M^{-1}
 #pragma unroll
     for (int a = 0; a < EPT; ++a) {
         const int e = tid + a * NT, r = e >> 6, i = e & 63;
-        sM1[r * 65 + i] = i <= r ? vN[a] : 0.f;  // dN (N is lower triangular)
+        sM1[r * 65 + i] = keep_if(vN[a], i <= r);  // dN (N is lower triangular)
         sM2[i * 65 + r] = vM[a];                 // Minv (from its transpose)
     }
-    if (tid < 64) sB[tid] = rec[R::BT + tid];
+    if (tid < 64) sB[tid] = vb;
     for (int e = tid; e < 64 * DK / 32; e += NT) sMk[e] = 0u;
     __syncthreads();
     {  // db from N: column sums of dN o Minv, 16 partial sums of 4 rows per column
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     for (int a = 0; a < EPT; ++a) {
         const int e = tid + a * NT, r = e >> 6, i = e & 63;
         sM3[r * 65 + i] = vA[a];                 // Abar
-        sM2[r * 65 + i] = i <= r ? vP[a] : 0.f;  // dP (P is lower triangular with the diagonal)
+        sM2[r * 65 + i] = keep_if(vP[a], i <= r);  // dP (P is lower triangular with the diagonal)
     }
     __syncthreads();
     if (tid < 64) sDB[tid] = dbn;
@@ -822,7 +833,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     __syncthreads();
     {
         const int c = sc_;
-        float off = rec[R::GM + c] * gin[GR::DGM + c];  // gamma dgamma
+        float off = vgd;  // gamma dgamma (c = tid % DK)
         for (int wv = 0; wv < 16; ++wv) off += sM3[wv * DK + c];
         for (int s2 = sg_ + 1; s2 < NSEG; ++s2) off += sq[(SEG * s2) * LD + c];
 #pragma unroll
