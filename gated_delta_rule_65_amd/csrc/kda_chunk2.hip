@@ -284,6 +284,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     const int r = 16 * w + m;
     const bool rv = r < nt;
     const int64_t base = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + 8 * cg;
+    // beta first: its LDS store then waits for this one load, not for the rows below
+    float braw = 0.f;
+    if (tid < kC) braw = load1_gate(bv, (t0 + min(tid, nt - 1)) * H + h, pf.b_bf16);
     float qf[KS][8], kf[KS][8], gl[KS][8];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -291,8 +294,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         load8_as_float(k + base + 32 * s, kf[s]);
         load8_gate(gv, base + 32 * s, pf.g_bf16, gl[s]);
     }
-    if (tid < kC)
-        sBeta[tid] = (tid < nt) ? beta_value(load1_gate(bv, (t0 + tid) * H + h, pf.b_bf16), pf.b_logit) : 0.f;
+    if (tid < kC) sBeta[tid] = tid < nt ? beta_value(braw, pf.b_logit) : 0.f;
     if (pf.l2norm) {  // unit q and k rows: each row lives in lanes m, m+16, m+32, m+48
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -622,13 +624,12 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     const float vscale = ident ? 0.f : 1.f;                // V = 0 for the identity columns
     const int nk = steps_of(rb);
 
-    // state of this slice at the segment start / its destination
-    auto state_in = [&](int c, int col) -> float {
-        if (cm.mode == 1) return ident ? (c == colx - Dv + col - col0 ? 1.f : 0.f) : 0.f;
-        if (cm.mode == 2 && p > 0)
-            return cm.sfold[((((n * H + h) * (int64_t)cm.P + p) * DK + c) * Dv) + col];
-        return s0 ? s0[((n * H + h) * DK + c) * (int64_t)Dv + col] : 0.f;
-    };
+    // state of this slice at the segment start (its source chosen once, so that the loads of all of a
+    // wave's elements are issued together) / its destination
+    const float* const s_src = cm.mode == 1 ? nullptr
+                               : (cm.mode == 2 && p > 0 ? cm.sfold + (((n * H + h) * (int64_t)cm.P + p) * DK) * Dv
+                                                        : (s0 ? s0 + (n * H + h) * (int64_t)DK * Dv : nullptr));
+
     float* const sdst = cm.mode == 1 ? cm.sx + (pr * DK) * (int64_t)(Dv + DK)
                                      : ((cm.mode == 0 || p == cm.P - 1) && s_final
                                             ? s_final + (n * H + h) * (int64_t)DK * Dv : nullptr);
@@ -637,12 +638,26 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 
     // initial state of this wave's tiles
     f32x4_t accS[TPW];
+    if (cm.mode == 1) {  // zero value columns; the identity on the identity columns
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) accS[i][jj] = state_in(16 * cbw + 4 * cg + jj, col0 + 16 * nbt(i) + m);
-        lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
+            for (int jj = 0; jj < 4; ++jj) {
+                const int c = 16 * cbw + 4 * cg + jj, col = col0 + 16 * nbt(i) + m;
+                accS[i][jj] = ident && c == colx - Dv + col - col0 ? 1.f : 0.f;
+            }
+    } else if (s_src) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                accS[i][jj] = s_src[(16 * cbw + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nbt(i) + m];
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) accS[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
 
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
