@@ -561,6 +561,7 @@ struct ChainMode {
     float* sx;     // mode 1 output; mode 3: chunk-start states
     const float* sfold;  // mode 2 input
     float* xu = nullptr;  // mode 3: X and U of every chunk, [slot][h][2][64][Dv] (rows past the end zero)
+    const int32_t* order = nullptr;  // packed sequences: item i runs sequence order[i / H] (longest first)
 };
 
 // SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     const int sl = (int)(loc % NS);
     const int64_t pr = (loc / NS) * 8 + (bid & 7);  // slices of one item on one XCD
     if (pr >= items) return;
-    const int64_t n = pr / ((int64_t)H * segs);
+    const int64_t n = cm.order ? (int64_t)cm.order[pr / ((int64_t)H * segs)] : pr / ((int64_t)H * segs);
     const int h = (int)((pr / segs) % H);
     const int p = (int)(pr % segs);
     const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
@@ -1017,7 +1018,38 @@ static int64_t segment_bytes(const ChunkArgs& a, int P) {
     return a.N * a.H * (int64_t)a.Dk * 4 * ((P - 1) * (int64_t)(a.Dv + a.Dk) + P * (int64_t)a.Dv);
 }
 
-int64_t chunk_workspace_bytes(const ChunkArgs& a) { return records_bytes(a) + segment_bytes(a, chunk_segments(a)); }
+// packed sequences: their order, longest first, for the chain's dispatch [N] int32
+static int64_t order_bytes(const ChunkArgs& a) { return a.cu_seqlens ? ((a.N * 4 + 255) / 256) * 256 : 0; }
+
+int64_t chunk_workspace_bytes(const ChunkArgs& a) {
+    return records_bytes(a) + segment_bytes(a, chunk_segments(a)) + order_bytes(a);
+}
+
+// Packed sequences sorted by length, longest first (ties by index): order[rank] = n.  The chain
+// kernel's workgroups start in that order, so the longest chains do not trail at the end of the grid.
+// One workgroup per 256 sequences; the lengths are staged in LDS (up to kOrderMax sequences; beyond
+// that the order is the identity).
+constexpr int kOrderMax = 4096;
+__global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* __restrict__ cu, int64_t N, int64_t total,
+                                                        int32_t* __restrict__ order) {
+    __shared__ int32_t sl[kOrderMax];
+    const int64_t i = blockIdx.x * 256 + threadIdx.x;
+    if (N > kOrderMax) {
+        if (i < N) order[i] = (int32_t)i;
+        return;
+    }
+    auto len = [&](int64_t j) {
+        const int64_t s0 = min<int64_t>(max<int64_t>(cu[j], 0), total);
+        return (int32_t)(min<int64_t>(max<int64_t>(cu[j + 1], s0), total) - s0);
+    };
+    for (int64_t j = threadIdx.x; j < N; j += 256) sl[j] = len(j);
+    __syncthreads();
+    if (i >= N) return;
+    const int32_t li = sl[i];
+    int32_t rank = 0;
+    for (int j = 0; j < (int)N; ++j) rank += (sl[j] > li) || (sl[j] == li && j < (int)i);
+    order[rank] = (int32_t)i;
+}
 
 static int64_t chain_grid(int64_t items, int slices) { return ((items + 7) / 8) * 8 * slices; }
 
@@ -1035,7 +1067,14 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     const int P = chunk_segments(a);
     const int NV = a.Dv / kS;
     if (P < 2) {
-        const ChainMode cm{0, 1, 0, nullptr, nullptr};
+        ChainMode cm{0, 1, 0, nullptr, nullptr};
+        if (a.cu_seqlens && a.N > 0) {
+            int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + records_bytes(a));
+            hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, st, a.cu_seqlens,
+                               a.N, a.total, order);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            cm.order = order;
+        }
         hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(kChainThreads), 0, st,
                            a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, cm,
                            static_cast<const char*>(ws));

@@ -121,7 +121,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
  * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
  * the arguments are unsupported): B * ceil(T/64) * H records of
  * 64*Dk*10 (bf16) or 64*Dk*12 (fp32) + 24576 + 4*Dk bytes
- * (104.5 KiB per chunk and head at Dk = 128 with bf16 inputs).
+ * (104.5 KiB per chunk and head at Dk = 128 with bf16 inputs).  Calls with few
+ * state columns in all (2 * B*H*Dv/32 <= 256) and long sequences are cut into
+ * P = min(256 / (B*H*Dv/32), ceil(T/64) / 64) >= 2 segments along T; they need
+ * B*H*Dk*4*((P-1)*(Dv+Dk) + P*Dv) more bytes for the segment states.
  */
 size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype);
 
@@ -146,7 +149,9 @@ kda_status kda_varlen_fwd(const void* q, const void* k, const void* v, const voi
  * Workspace bytes kda_varlen_fwd needs (0 if none or unsupported sizes): it
  * depends only on N and total, not on the offsets, so a buffer sized once
  * serves every packing of that many tokens: (floor(total/64) + N) * H records
- * of the size given for kda_chunk_workspace_bytes.
+ * of the size given for kda_chunk_workspace_bytes, plus 4*N bytes rounded up to
+ * a multiple of 256 (the order, longest first, in which the sequences' state
+ * chains are started).
  */
 size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int Dv, kda_dtype dtype);
 

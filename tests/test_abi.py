@@ -131,7 +131,9 @@ def test_segment_counts():
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("N,total,H,Dk", [(2, 100, 2, 128), (32, 65536, 16, 128), (1, 1, 1, 64)])
 def test_varlen_workspace_size(N, total, H, Dk, dtype):
-    assert kda.varlen_workspace_bytes(N, total, H, Dk, 128, dtype) == (total // 64 + N) * H * record_bytes(Dk, dtype)
+    order = -(-4 * N // 256) * 256  # the sequences' dispatch order, int32, 256-byte multiple
+    assert kda.varlen_workspace_bytes(N, total, H, Dk, 128, dtype) == ((total // 64 + N) * H * record_bytes(Dk, dtype)
+                                                                        + order)
 
 
 def test_workspace_size_of_unsupported_or_empty_is_zero():
