@@ -287,12 +287,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     // beta first: its LDS store then waits for this one load, not for the rows below
     float braw = 0.f;
     if (tid < kC) braw = load1_gate(bv, (t0 + min(tid, nt - 1)) * H + h, pf.b_bf16);
+    // the gates first: the running sums below start while q and k are still arriving
     float qf[KS][8], kf[KS][8], gl[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) load8_gate(gv, base + 32 * s, pf.g_bf16, gl[s]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         load8_as_float(q + base + 32 * s, qf[s]);
         load8_as_float(k + base + 32 * s, kf[s]);
-        load8_gate(gv, base + 32 * s, pf.g_bf16, gl[s]);
     }
     if (tid < kC) sBeta[tid] = tid < nt ? beta_value(braw, pf.b_logit) : 0.f;
     if (pf.l2norm) {  // unit q and k rows: each row lives in lanes m, m+16, m+32, m+48
