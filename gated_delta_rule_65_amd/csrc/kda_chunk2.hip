@@ -36,23 +36,27 @@ constexpr int kChainThreads = 512;  // chain workgroup: eight waves
 // A fragment (eight values per lane, see Frag) is stored as two planes of
 // 64 lanes x 16 B: bf16 hi and bf16 lo (split policy) or fp32 values 0-3 and
 // 4-7 (fp32 policy).  A hi-only fragment of the split policy has one plane.
+// Records are written with non-temporal stores: they are read back only after the
+// whole preparation pass, and write-back of cached record lines would otherwise
+// overlap the chain kernel's reads.
 constexpr int kPlane = 1024;
 
 template <bool F32>
 __device__ __forceinline__ void gfrag_store(char* grp, int lane, const Frag<F32>& f) {
     if constexpr (F32) {
-        *reinterpret_cast<float4*>(grp + lane * 16) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
-        *reinterpret_cast<float4*>(grp + kPlane + lane * 16) = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+        __builtin_nontemporal_store(f32x4_t{f.v[0], f.v[1], f.v[2], f.v[3]}, reinterpret_cast<f32x4_t*>(grp + lane * 16));
+        __builtin_nontemporal_store(f32x4_t{f.v[4], f.v[5], f.v[6], f.v[7]},
+                                    reinterpret_cast<f32x4_t*>(grp + kPlane + lane * 16));
     } else {
-        *reinterpret_cast<bf16x8_t*>(grp + lane * 16) = f.hi;
-        *reinterpret_cast<bf16x8_t*>(grp + kPlane + lane * 16) = f.lo;
+        __builtin_nontemporal_store(f.hi, reinterpret_cast<bf16x8_t*>(grp + lane * 16));
+        __builtin_nontemporal_store(f.lo, reinterpret_cast<bf16x8_t*>(grp + kPlane + lane * 16));
     }
 }
 
 template <bool F32>
 __device__ __forceinline__ void gfrag_store_hi(char* grp, int lane, const Frag<F32>& f) {
     if constexpr (F32) gfrag_store<true>(grp, lane, f);
-    else *reinterpret_cast<bf16x8_t*>(grp + lane * 16) = f.hi;
+    else __builtin_nontemporal_store(f.hi, reinterpret_cast<bf16x8_t*>(grp + lane * 16));
 }
 
 template <bool F32>
@@ -856,7 +860,9 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
             for (int half = 0; half < 2; ++half) {
                 const int rr = 16 * rb + 8 * half + (lane >> 3);
                 const float4 x = *reinterpret_cast<const float4*>(&sO[rr * (kS + 4) + (lane & 7) * 4]);
-                if (rr < ntc) *reinterpret_cast<float4*>(o_l + (tc + rr) * (int64_t)rs_o) = x;
+                if (rr < ntc)  // o is not read again by this call: streamed past the caches
+                    __builtin_nontemporal_store(f32x4_t{x.x, x.y, x.z, x.w},
+                                                reinterpret_cast<f32x4_t*>(o_l + (tc + rr) * (int64_t)rs_o));
             }
         };
         auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
