@@ -229,7 +229,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
         if (swave) {  // dS' of this chunk
             float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv + col0 + 16 * nb + m;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv] = dS[jj];
+            for (int jj = 0; jj < 4; ++jj) st_nt(&dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv], dS[jj]);
         }
         // stage P^T, Minv^T, Kb, dO^T, b, gamma (the previous chunk's dS phase has finished: barrier)
         lds_store4<F32, 64, 64>(pPT, (4 * tid) >> 6, (4 * tid) & 63, f4(rPT, 1.f));
@@ -269,9 +269,9 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * rb + 4 * cg + jj;
                 accX[jj] *= sB[i];
-                du_o[i * (int64_t)Dv] = accU[jj];
-                du_o[(64 + i) * (int64_t)Dv] = accX[jj];
-                if (i < nt) dv[((t0 + i) * H + h) * (int64_t)Dv + col0 + 16 * nb + m] = accX[jj];
+                st_nt(&du_o[i * (int64_t)Dv], accU[jj]);
+                st_nt(&du_o[(64 + i) * (int64_t)Dv], accX[jj]);
+                if (i < nt) st_nt(&dv[((t0 + i) * H + h) * (int64_t)Dv + col0 + 16 * nb + m], accX[jj]);
             }
             lds_store4<F32, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, accX);
         }
@@ -427,20 +427,20 @@ __global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restr
         const int r = 16 * w + 4 * cg + i;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            out[GR::DQT + r * DK + 16 * cb + m] = aQ[cb][i];
-            out[GR::DKT + r * DK + 16 * cb + m] = -aK[cb][i];
-            out[GR::DKB + r * DK + 16 * cb + m] = aB[cb][i];
+            st_nt(&out[GR::DQT + r * DK + 16 * cb + m], aQ[cb][i]);
+            st_nt(&out[GR::DKT + r * DK + 16 * cb + m], -aK[cb][i]);
+            st_nt(&out[GR::DKB + r * DK + 16 * cb + m], aB[cb][i]);
         }
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
-            out[GR::DP + r * 64 + 16 * ib + m] = aP[ib][i];
-            out[GR::DN + r * 64 + 16 * ib + m] = aN[ib][i];
+            st_nt(&out[GR::DP + r * 64 + 16 * ib + m], aP[ib][i]);
+            st_nt(&out[GR::DN + r * 64 + 16 * ib + m], aN[ib][i]);
         }
     }
     // dgamma: the 32 / PS threads of a row are adjacent
 #pragma unroll
     for (int off = 1; off < 32 / PS; off <<= 1) dgam += __shfl_xor(dgam, off);
-    if (sc == 0) out[GR::DGM + sr] = dgam;
+    if (sc == 0) st_nt(&out[GR::DGM + sr], dgam);
 }
 
 // ============================================================================ to dq, dk, dg, db
@@ -802,8 +802,8 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
             const int64_t idx = ((t0 + r) * H + h) * (int64_t)DK + ac;
 #pragma unroll
             for (int b = 0; b < CPT; b += 4) {
-                *reinterpret_cast<float4*>(dq + idx + b) = make_float4(dqv[b], dqv[b + 1], dqv[b + 2], dqv[b + 3]);
-                *reinterpret_cast<float4*>(dk + idx + b) = make_float4(dkv[b], dkv[b + 1], dkv[b + 2], dkv[b + 3]);
+                st_nt4(dq + idx + b, dqv[b], dqv[b + 1], dqv[b + 2], dqv[b + 3]);
+                st_nt4(dk + idx + b, dkv[b], dkv[b + 1], dkv[b + 2], dkv[b + 3]);
             }
         }
     }

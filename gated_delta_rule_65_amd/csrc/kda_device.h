@@ -121,6 +121,13 @@ struct Frag<true> {
     __device__ __forceinline__ void set_hi_only(const float x[8]) { set(x); }
 };
 
+// Stores of data that no later access of the same kernel reads: streamed past the caches, so that
+// their write-back does not compete with the loads of the kernels that follow.
+__device__ __forceinline__ void st_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt4(float* p, float a, float b, float c, float d) {
+    __builtin_nontemporal_store(f32x4_t{a, b, c, d}, reinterpret_cast<f32x4_t*>(p));
+}
+
 // acc += A * B with the full precision of the policy.
 __device__ __forceinline__ f32x4_t mma_full(f32x4_t acc, const Frag<false>& a, const Frag<false>& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
