@@ -761,7 +761,6 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                 for (int nb = 0; nb < 2; ++nb)
                     accX[nb] = ST ? mma_full(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg))
                                   : mma_fast(accX[nb], cur.fK[s], lds_frag<F32, kS, DK>(pS, 16 * nb + m, 32 * s + 8 * cg));
-                load_k(nxt, recn, s);
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
@@ -784,6 +783,10 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                     }
                 }
             }
+            // the next chunk's Kt rows: requested only now, when the products that read this chunk's
+            // copy (whose registers they may take) have completed, so the requests do not stall
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load_k(nxt, recn, s);
             lds_barrier();  // (1)
 
             // ---- phase 2:  U = M^{-1} Diag(b) X
@@ -795,7 +798,6 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                 for (int nb = 0; nb < 2; ++nb)
                     accU[nb] = mma_full(accU[nb], cur.fN[kb], lds_frag<F32, kS, kC>(pX, 16 * nb + m, 32 * kb + 8 * cg));
             }
-            load_nv(nxt, recn, jn);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * rb + 4 * cg, accU[nb]);
@@ -806,14 +808,15 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                     for (int jj = 0; jj < 4; ++jj) uo[(16 * rb + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accU[nb][jj];
                 }
             }
+            load_nv(nxt, recn, jn);  // after the products that read this chunk's M^{-1} rows
             lds_barrier();  // (2)
 
             // ---- phase 3:  S tiles
             Fr uf[2][2];
             read_u(uf);
             update_state(uf, cur.fKB, cur.gC);
-            load_kb(nxt.fKB, nxt.gC, recn);
             store_state();
+            load_kb(nxt.fKB, nxt.gC, recn);  // after the tile products that read this chunk's copy
             lds_barrier();  // (3)
         };
         Ops opsA, opsB;
@@ -906,12 +909,14 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
                 }
-                load_p(nxt, recn);
             }
             update_state(uf, cur.fKB, cur.gC);
-            load_kb(nxt.fKB, nxt.gC, recn);
             store_state();
-            if constexpr (!SO) stage_o(accO);
+            load_kb(nxt.fKB, nxt.gC, recn);  // after the tile products that read this chunk's copy
+            if constexpr (!SO) {
+                stage_o(accO);
+                load_p(nxt, recn);  // after the P U products that read this chunk's copy
+            }
             lds_barrier();  // (3)
         };
         Ops opsA, opsB;
