@@ -17,8 +17,8 @@
 // kernel is a fully contiguous 1 KiB request.  chain_kernel walks the chunks of one
 // (sequence, head, 32-column slice) in order and only runs the products of the
 // second line, with three workgroup barriers per chunk; each chunk's operands are
-// loaded during the previous chunk, right after the registers they replace are
-// last read.
+// loaded during the previous chunk, once the products that read the registers they
+// replace have completed (the Qt steps right after their last read).
 #include <type_traits>
 
 #include "kda_device.h"
