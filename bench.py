@@ -48,12 +48,19 @@ def decode_alg_bytes(B, H, Dk, Dv, in_bytes):
 
 
 def kernel_source_digest():
+    """Digest of the kernel sources with comments and blank space removed, so that the recorded
+    counters stay attached to the code they were measured on and only a code change drops them."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_65_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)               # line comments (no string holds //)
+        text = " ".join(text.split())
+        h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()
 
 
