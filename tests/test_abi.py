@@ -200,3 +200,13 @@ def test_prologue_struct_defaults_to_none():
     p = kda.prologue(torch.bfloat16, True, torch.float32, False, True)
     assert (p.contents.g_dtype, p.contents.g_logit, p.contents.beta_dtype, p.contents.beta_logit,
             p.contents.qk_l2norm) == (1, 1, 0, 0, 1)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built library the binding raises; there is no fallback path to run instead."""
+    monkeypatch.setattr(kda, "_LIB_PATH", os.path.join(ROOT, "no-such-dir", "libkda.so"))
+    monkeypatch.setattr(kda, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        kda.load_library()
+    with pytest.raises(ImportError):
+        kda.chunk_workspace_bytes(1, 64, 1, 128, 128)
