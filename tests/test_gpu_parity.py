@@ -106,6 +106,17 @@ def test_head_dims(Dk, Dv, dtype, fused):
     check(inp, *run_chunk(inp, fused=fused))
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128)])
+@pytest.mark.parametrize("packed", [False, True], ids=["batched", "packed"])
+def test_more_chains_than_compute_units(Dk, Dv, packed):
+    """Chain grids larger than the CU count (576 and 640 workgroups) run in several rounds."""
+    lengths = [130] * 9 if not packed else [1, 64, 65, 200, 0, 127, 129, 90, 33, 256]
+    spec = kda_inputs.Spec(lengths, 16, Dk, Dv, "bf16", "softplus", s0_std=0.02, seed=21, packed=packed,
+                           name=f"many-chains-{Dk}x{Dv}-{'packed' if packed else 'batched'}")
+    inp = kda_inputs.generate(spec)
+    check(inp, *run_chunk(inp, batched=not packed))
+
+
 @PATHS
 def test_long_memory_gate(fused):
     spec = kda_inputs.Spec([2048], 4, 128, 128, "bf16", "longmem", seed=4, name="longmem-2048")
