@@ -45,6 +45,18 @@ def test_decode_shapes(Dk, Dv, dtype):
     assert rel_err(o, o_ref.reshape(o.shape)) <= TOL[dtype] and rel_err(s, s_ref) <= TOL[dtype]
 
 
+def test_decode_gates_beyond_the_clamp_bounds():
+    spec = kda_inputs.Spec([1] * 6, 4, 128, 128, "bf16", "softplus", s0_std=0.3, seed=42)
+    inp = kda_inputs.generate(spec)
+    sel = np.random.default_rng(42).integers(0, 5, size=inp.g.shape)
+    for i, val in enumerate([-np.inf, -1e4, 3.0, np.inf]):
+        inp.g[sel == i] = val
+    o, s, _ = run_decode(inp)
+    o_ref, s_ref = oracle.forward_inputs(inp)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert rel_err(o, o_ref.reshape(o.shape)) <= TOL["bf16"] and rel_err(s, s_ref) <= TOL["bf16"]
+
+
 def test_decode_inplace():
     spec = kda_inputs.Spec([1] * 7, 4, 128, 128, "bf16", "softplus", s0_std=0.02, seed=32)
     inp = kda_inputs.generate(spec)

@@ -117,6 +117,24 @@ def test_more_chains_than_compute_units(Dk, Dv, packed):
     check(inp, *run_chunk(inp, batched=not packed))
 
 
+def beyond_bounds(inp, seed):
+    """Set a fifth of the gates each to -inf, -1e4, +3 and +inf (all outside [-5, 0])."""
+    sel = np.random.default_rng(seed).integers(0, 5, size=inp.g.shape)
+    for i, val in enumerate([-np.inf, -1e4, 3.0, np.inf]):
+        inp.g[sel == i] = val
+    return inp
+
+
+@PATHS
+def test_gates_beyond_the_clamp_bounds(fused):
+    """log alpha outside [-5, 0], infinities included, acts as the nearest bound."""
+    spec = kda_inputs.Spec([150] * 2, 3, 128, 128, "bf16", "softplus", s0_std=0.02, seed=41, name="gates-beyond")
+    inp = beyond_bounds(kda_inputs.generate(spec), 41)
+    o, s = run_chunk(inp, fused=fused)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    check(inp, o, s)
+
+
 @PATHS
 def test_long_memory_gate(fused):
     spec = kda_inputs.Spec([2048], 4, 128, 128, "bf16", "longmem", seed=4, name="longmem-2048")

@@ -278,9 +278,14 @@ def check_clamp(fwd=None):
     g_out = g_lo.copy()
     g_out[::2] = -9.0
     g_out[1::2] = 2.5
+    g_inf = g_lo.copy()
+    g_inf[::2] = -np.inf
+    g_inf[1::2] = np.inf
     a, sa = run(q, k, v, g_lo, beta, s0=S0, fwd=fwd)
     b, sb = run(q, k, v, g_out, beta, s0=S0, fwd=fwd)
     assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    c, sc = run(q, k, v, g_inf, beta, s0=S0, fwd=fwd)  # infinite logs of alpha sit at the bounds too
+    assert np.array_equal(a, c) and np.array_equal(sa, sc)
     # the lower bound is e^-5 itself: one token, beta = 0, S0 = I-like -> S = e^-5 S0
     z1 = np.zeros((1, 1, 4), dtype=np.float32)
     S0i = np.eye(4)[None, None, :, :3].copy()
