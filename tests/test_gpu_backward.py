@@ -130,6 +130,21 @@ def test_backward_clamp_mask():
     assert outside.any() and np.all(gpu["dg"][outside] == 0.0)
 
 
+def test_backward_infinite_gates():
+    """log alpha = -inf / +inf act as the bounds in every gradient and get a zero gradient themselves."""
+    spec = kda_inputs.Spec([100] * 2, 2, 128, 128, "bf16", "softplus", s0_std=0.1, seed=86, name="bwd-inf")
+    inp = kda_inputs.generate(spec)
+    sel = np.random.default_rng(1).integers(0, 6, size=inp.g.shape)
+    inp.g[sel == 0] = -np.inf
+    inp.g[sel == 1] = np.inf
+    d_o, d_sf = cotangents(spec, 7)
+    gpu = run_bwd(inp, d_o, d_sf)
+    for n in NAMES:
+        assert np.isfinite(gpu[n]).all(), n
+    check(inp, gpu, reference(inp, d_o, d_sf))
+    assert np.all(gpu["dg"][sel <= 1] == 0.0)
+
+
 def test_backward_workspace_reused_and_dirty():
     spec = kda_inputs.Spec([200] * 2, 2, 128, 128, "bf16", "softplus", s0_std=0.02, seed=86, name="bwd-ws")
     inp = kda_inputs.generate(spec)
