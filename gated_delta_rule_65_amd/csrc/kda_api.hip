@@ -82,7 +82,9 @@ kda_status run_chunked(const kda::ChunkArgs& a, void* workspace, size_t workspac
     if (grid > 0x7fffffff) return fail(KDA_ERR_BAD_SHAPE, "%s: %lld sequence-heads exceed the grid limit", what,
                                        (long long)(a.N * a.H));
     if (grid == 0) return ok();
-    if (!workspace) return launched(kda::launch_chunk_fwd(a, st), what);
+    // without tokens there is nothing to prepare (the workspace size queries return 0 then): the
+    // fused kernel passes s0 (or zeros) through to s_final
+    if (!workspace || a.total == 0) return launched(kda::launch_chunk_fwd(a, st), what);
     if (kda::chunk_slots(a) * a.H > 0x7fffffffLL)
         return fail(KDA_ERR_BAD_SHAPE, "%s: %lld chunk-heads exceed the grid limit", what,
                     (long long)(kda::chunk_slots(a) * a.H));

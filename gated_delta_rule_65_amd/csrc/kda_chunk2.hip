@@ -19,6 +19,7 @@
 // second line, with three workgroup barriers per chunk; each chunk's operands are
 // loaded during the previous chunk, once the products that read the registers they
 // replace have completed (the Qt steps right after their last read).
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -112,13 +113,16 @@ struct SeqRange {
     int64_t start, end;
 };
 
-__device__ __forceinline__ SeqRange seq_range(const int32_t* cu, int64_t n, int64_t T_fixed, int64_t total) {
+// Tokens of sequence n: from the offsets, or T_fixed tokens starting at n * T_stride (T_stride =
+// T_fixed for a whole batch; larger when a call covers a window of each sequence).
+__device__ __forceinline__ SeqRange seq_range(const int32_t* cu, int64_t n, int64_t T_fixed, int64_t T_stride,
+                                              int64_t total) {
     SeqRange s;
     if (cu) {
         s.start = min<int64_t>(max<int64_t>(cu[n], 0), total);
         s.end = min<int64_t>(max<int64_t>(cu[n + 1], s.start), total);
     } else {
-        s.start = n * T_fixed;
+        s.start = n * T_stride;
         s.end = s.start + T_fixed;
     }
     return s;
@@ -229,7 +233,7 @@ template <int DK, bool F32, bool PRO, bool IN_F32 = F32, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                       const void* __restrict__ gv, const void* __restrict__ bv,
                                                       const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
-                                                      int64_t total, int64_t N, int H, Prologue pro,
+                                                      int64_t T_stride, int64_t total, int64_t N, int H, Prologue pro,
                                                       char* __restrict__ ws, float* __restrict__ brecs = nullptr) {
     using In = typename std::conditional<IN_F32, float, uint16_t>::type;
     using Fr = Frag<F32>;
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         n = slot / nch;
         j = slot % nch;
     }
-    const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
+    const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, T_stride, total);
     const int64_t t0 = sr.start + j * kC;
     if (j < 0 || t0 >= sr.end) return;  // unused slot
     const int nt = (int)min<int64_t>(kC, sr.end - t0);
@@ -583,7 +587,8 @@ template <int DK, bool F32, bool SO, bool IN_F32 = F32, bool ST = false>
 __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
                                                                  float* __restrict__ o, float* s_final,
                                                                  const int32_t* __restrict__ cu_seqlens,
-                                                                 int64_t T_fixed, int64_t total, int64_t N, int H,
+                                                                 int64_t T_fixed, int64_t T_stride, int64_t total,
+                                                                 int64_t N, int H,
                                                                  int Dv, ChainMode cm,
                                                                  const char* ws) {  // not restrict: keeps the loads of the next chunk where they are written
     using In = typename std::conditional<IN_F32, float, uint16_t>::type;
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     const int64_t n = cm.order ? (int64_t)cm.order[pr / ((int64_t)H * segs)] : pr / ((int64_t)H * segs);
     const int h = (int)((pr / segs) % H);
     const int p = (int)(pr % segs);
-    const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, total);
+    const SeqRange sr = seq_range(cu_seqlens, n, T_fixed, T_stride, total);
     const int64_t start = sr.start, end = sr.end;
     const int64_t nall = (end - start + kC - 1) / kC;
     const bool split = cm.mode == 1 || cm.mode == 2;
@@ -633,9 +638,11 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 
     // state of this slice at the segment start (its source chosen once, so that the loads of all of a
     // wave's elements are issued together) / its destination
+    // (mode 2 reads every segment's initial state from sfold, p = 0 included, where the fold kernel
+    // copied s0: s0 is then read by no launch that also writes s_final, which may alias it)
     const float* const s_src = cm.mode == 1 ? nullptr
-                               : (cm.mode == 2 && p > 0 ? cm.sfold + (((n * H + h) * (int64_t)cm.P + p) * DK) * Dv
-                                                        : (s0 ? s0 + (n * H + h) * (int64_t)DK * Dv : nullptr));
+                               : (cm.mode == 2 ? cm.sfold + (((n * H + h) * (int64_t)cm.P + p) * DK) * Dv
+                                               : (s0 ? s0 + (n * H + h) * (int64_t)DK * Dv : nullptr));
 
     float* const sdst = cm.mode == 1 ? cm.sx + (pr * DK) * (int64_t)(Dv + DK)
                                      : ((cm.mode == 0 || p == cm.P - 1) && s_final
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 
 // Initial states of the segments of a split sequence, one workgroup per (sequence, head,
 // 32-column slice): S_in(0) = s0 (or 0), S_in(p+1) = Phi_p S_in(p) + S0_p for p < P - 1, written
-// to sfold [n][h][p][Dk][Dv] (p >= 1).  fp32 throughout; the running state stays in LDS.
+// to sfold [n][h][p][Dk][Dv] (p = 0 included).  fp32 throughout; the running state stays in LDS.
 template <int DK>
 __global__ __launch_bounds__(256) void fold_kernel(const float* s0, const float* __restrict__ sx,
                                                    float* __restrict__ sfold, int H, int Dv, int P) {
@@ -961,10 +968,13 @@ __global__ __launch_bounds__(256) void fold_kernel(const float* s0, const float*
     const int NV = Dv / kS;
     const int64_t item = blockIdx.x / NV;  // n * H + h
     const int col = (int)(blockIdx.x % NV) * kS + j;
+    float* const dst0 = sfold + (item * P * DK) * (int64_t)Dv;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int c = r0 + 8 * i;
-        sS[c][j] = s0 ? s0[(item * DK + c) * (int64_t)Dv + col] : 0.f;
+        const float x = s0 ? s0[(item * DK + c) * (int64_t)Dv + col] : 0.f;
+        sS[c][j] = x;
+        dst0[c * (int64_t)Dv + col] = x;
     }
     __syncthreads();
     for (int p = 0; p + 1 < P; ++p) {
@@ -997,6 +1007,8 @@ __global__ __launch_bounds__(256) void fold_kernel(const float* s0, const float*
 }
 
 // ============================================================================ host side
+
+static int64_t seq_stride(const ChunkArgs& a) { return a.T_stride > 0 ? a.T_stride : a.T_fixed; }
 
 int64_t chunk_slots(const ChunkArgs& a) {
     if (a.cu_seqlens) return a.total / kC + a.N;
@@ -1067,17 +1079,17 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* __restric
 static int64_t chain_grid(int64_t items, int slices) { return ((items + 7) / 8) * 8 * slices; }
 
 template <int DK, bool F32>
-static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
+static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st, bool allow_split = true) {
     const int64_t prep_grid = chunk_slots(a) * a.H;
     if (prep_grid > 0 && any_prologue(a.pro))
         hipLaunchKernelGGL((prep_kernel<DK, F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st, a.q, a.k, a.g,
-                           a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
+                           a.beta, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
     else if (prep_grid > 0)
         hipLaunchKernelGGL((prep_kernel<DK, F32, false>), dim3((unsigned)prep_grid), dim3(256), 0, st, a.q, a.k, a.g,
-                           a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
+                           a.beta, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N, a.H, a.pro, static_cast<char*>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int P = chunk_segments(a);
+    const int P = allow_split ? chunk_segments(a) : 1;
     const int NV = a.Dv / kS;
     if (P < 2) {
         ChainMode cm{0, 1, 0, nullptr, nullptr};
@@ -1089,7 +1101,7 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
             cm.order = order;
         }
         hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H, NV)), dim3(kChainThreads), 0, st,
-                           a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, cm,
+                           a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N, a.H, a.Dv, cm,
                            static_cast<const char*>(ws));
         return hipGetLastError();
     }
@@ -1100,15 +1112,15 @@ static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st) {
     float* sfold = sx + a.N * a.H * (int64_t)(P - 1) * a.Dk * (a.Dv + a.Dk);
     const ChainMode c1{1, P, L, sx, nullptr};
     hipLaunchKernelGGL((chain_kernel<DK, F32, true>), dim3((unsigned)chain_grid(a.N * a.H * (P - 1), NV + DK / kS)),
-                       dim3(kChainThreads), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H,
-                       a.Dv, c1, static_cast<const char*>(ws));
+                       dim3(kChainThreads), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N,
+                       a.H, a.Dv, c1, static_cast<const char*>(ws));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((fold_kernel<DK>), dim3((unsigned)(a.N * a.H * NV)), dim3(256), 0, st, a.s0, sx, sfold, a.H,
                        a.Dv, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const ChainMode c2{2, P, L, nullptr, sfold};
     hipLaunchKernelGGL((chain_kernel<DK, F32, false>), dim3((unsigned)chain_grid(a.N * a.H * P, NV)), dim3(kChainThreads), 0, st,
-                       a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, c2,
+                       a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N, a.H, a.Dv, c2,
                        static_cast<const char*>(ws));
     return hipGetLastError();
 }
@@ -1124,13 +1136,13 @@ static hipError_t launch_states(const ChunkArgs& a, void* recs, float* brecs, fl
     const int64_t prep_grid = chunk_slots(a) * a.H;
     if (prep_grid > 0)
         hipLaunchKernelGGL((prep_kernel<DK, false, false, IN_F32, true>), dim3((unsigned)prep_grid), dim3(256), 0, st,
-                           a.q, a.k, a.g, a.beta, a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.pro,
+                           a.q, a.k, a.g, a.beta, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total, a.N, a.H, a.pro,
                            static_cast<char*>(recs), brecs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const ChainMode cm{3, 1, 0, states, nullptr, xu};
     hipLaunchKernelGGL((chain_kernel<DK, false, true, IN_F32, true>), dim3((unsigned)chain_grid(a.N * a.H, a.Dv / kS)),
-                       dim3(kChainThreads), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, a.total,
+                       dim3(kChainThreads), 0, st, a.v, a.s0, (float*)nullptr, (float*)nullptr, a.cu_seqlens, a.T_fixed, seq_stride(a), a.total,
                        a.N, a.H, a.Dv, cm, static_cast<const char*>(recs));
     return hipGetLastError();
 }
@@ -1149,6 +1161,55 @@ hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, flo
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st) {
     if (a.Dk == 128) return a.f32 ? launch_two<128, true>(a, ws, st) : launch_two<128, false>(a, ws, st);
     return a.f32 ? launch_two<64, true>(a, ws, st) : launch_two<64, false>(a, ws, st);
+}
+
+// ---------------------------------------------------------------------------- T-windows in a fixed scratch
+// Each window covers tokens [t0, t0 + W*64) of every sequence: its pointers are offset by t0 tokens,
+// its sequences start T tokens apart (T_stride) and are at most W*64 tokens long (T_fixed), so the
+// records of one window occupy B * W * H record slots.  The chain carries the state from window to
+// window in fp32 exactly as it does from chunk to chunk (read at a workgroup's start, written at its
+// end), so the results equal those of the whole-sequence call bit for bit.
+static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t chunk_window_state_bytes(const ChunkArgs& a) {
+    return a.s_final ? 0 : round256(a.N * a.H * (int64_t)a.Dk * a.Dv * 4);
+}
+
+int64_t chunk_window_chunks(const ChunkArgs& a, int64_t scratch_bytes) {
+    const int64_t per_chunk = a.N * a.H * chunk_record_bytes(a.Dk, a.f32);
+    const int64_t room = scratch_bytes - chunk_window_state_bytes(a);
+    if (per_chunk <= 0 || room < per_chunk) return 0;
+    const int64_t nch = (a.T_fixed + kC - 1) / kC;
+    return std::min<int64_t>(room / per_chunk, std::max<int64_t>(nch, 1));
+}
+
+hipError_t launch_chunk_fwd_windows(const ChunkArgs& a, char* scratch, int64_t scratch_bytes, hipStream_t st) {
+    const int64_t W = chunk_window_chunks(a, scratch_bytes);
+    if (W <= 0 || a.cu_seqlens || a.T_fixed <= 0) return hipErrorInvalidValue;
+    float* carry = a.s_final ? a.s_final : reinterpret_cast<float*>(scratch);
+    char* recs = scratch + chunk_window_state_bytes(a);
+    const int64_t qk_es = a.f32 ? 4 : 2, g_es = a.pro.g_bf16 ? 2 : 4, b_es = a.pro.b_bf16 ? 2 : 4;
+    for (int64_t t0 = 0; t0 < a.T_fixed; t0 += W * kC) {
+        ChunkArgs w = a;
+        w.T_fixed = std::min<int64_t>(W * kC, a.T_fixed - t0);
+        w.T_stride = a.T_fixed;
+        const int64_t tk = t0 * a.H;  // token offset times heads
+        w.q = static_cast<const char*>(a.q) + tk * a.Dk * qk_es;
+        w.k = static_cast<const char*>(a.k) + tk * a.Dk * qk_es;
+        w.v = static_cast<const char*>(a.v) + tk * a.Dv * qk_es;
+        w.g = static_cast<const char*>(a.g) + tk * a.Dk * g_es;
+        w.beta = static_cast<const char*>(a.beta) + tk * b_es;
+        w.o = a.o + tk * a.Dv;
+        w.s0 = t0 == 0 ? a.s0 : carry;
+        w.s_final = carry;
+        hipError_t e;
+        if (a.Dk == 128)
+            e = a.f32 ? launch_two<128, true>(w, recs, st, false) : launch_two<128, false>(w, recs, st, false);
+        else
+            e = a.f32 ? launch_two<64, true>(w, recs, st, false) : launch_two<64, false>(w, recs, st, false);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

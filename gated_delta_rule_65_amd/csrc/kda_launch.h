@@ -25,6 +25,7 @@ struct ChunkArgs {
     int H, Dk, Dv;
     bool f32;                   // q/k/v are float32 (else bf16)
     Prologue pro;
+    int64_t T_stride = 0;       // tokens between sequence starts (equal lengths); 0 = T_fixed
 };
 
 struct DecodeArgs {
@@ -44,6 +45,12 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t st);
 int64_t chunk_slots(const ChunkArgs& a);
 int64_t chunk_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st);
+// The two-kernel path over T-windows of equal-length sequences, with the records of one window in
+// a scratch buffer of fixed size (see chunk_window_chunks) and the state carried between windows
+// in fp32 through s_final or, when that is NULL, a state area at the start of the scratch.
+int64_t chunk_window_state_bytes(const ChunkArgs& a);
+int64_t chunk_window_chunks(const ChunkArgs& a, int64_t scratch_bytes);  // chunks per window; 0: too small
+hipError_t launch_chunk_fwd_windows(const ChunkArgs& a, char* scratch, int64_t scratch_bytes, hipStream_t st);
 // The state at every chunk start, [slot][h][Dk][Dv] fp32 (fp32 products for either input type),
 // X = V - Kt S and U of every chunk, [slot][h][2][64][Dv], and the backward pass's operands: `recs`
 // holds chunk_slots(a) * H records of chunk_states_record_bytes(Dk) bytes, `brecs` as many

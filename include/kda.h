@@ -101,6 +101,12 @@ typedef enum {
 
 /*
  * Chunked prefill over B sequences of equal length T.
+ * Defined by: the worldcybernews page cited above, second paragraph (the
+ * recurrence: fixed-size state, delta-rule update with write strength beta and
+ * forget gate alpha in [e^-5, 1]) and third paragraph (the tokens of a chunk
+ * processed in parallel, the state carried from chunk to chunk; long
+ * sequences with few heads are cut into segments whose initial states a
+ * prefix scan recovers, the one-GPU form of that paragraph's scan).
  *   q, k : [B, T, H, Dk]  dtype          v : [B, T, H, Dv]  dtype
  *   g    : [B, T, H, Dk]  log alpha, clamped to [-5, 0] inside (float32 unless
  *                         the prologue says otherwise)
@@ -130,6 +136,10 @@ size_t kda_chunk_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kd
 
 /*
  * Packed variable-length prefill: N independent sequences stored back to back.
+ * Defined by: the same second paragraph -- every sequence keeps its own
+ * fixed-size state, so packed sequences are independent runs of the
+ * recurrence, each starting from its own initial state; chunks as in the
+ * third paragraph, starting at each sequence's first token.
  *   q, k, g : [total, H, Dk]; v, o : [total, H, Dv]; beta : [total, H]
  *   (element types and prologue as for kda_chunk_fwd)
  *   cu_seqlens : DEVICE int32 [N+1], non-decreasing, cu_seqlens[0] = 0,
@@ -157,6 +167,9 @@ size_t kda_varlen_workspace_bytes(int64_t N, int64_t total, int H, int Dk, int D
 
 /*
  * One decoding step (one new token per sequence) on B sequences.
+ * Defined by: the same second paragraph -- the state matrix takes the place
+ * of the key/value cache, so generating a token is one update of S by the
+ * recurrence followed by the read-out o = S^T q.
  *   q, k : [B, H, Dk] dtype;  v : [B, H, Dv] dtype
  *   g    : [B, H, Dk] log alpha;  beta : [B, H]  (float32 unless the prologue
  *          says otherwise; prologue as for kda_chunk_fwd, or NULL)
@@ -171,7 +184,9 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
 
 /*
  * Gradients of kda_chunk_fwd (no prologue: g is log alpha and beta is used as given, both
- * float32).  The pages describe only the forward recurrence; these are its exact derivatives,
+ * float32).  Defined by: the forward recurrence of the same second paragraph, differentiated; the
+ * pages give no backward pass ("Kimi K3: Open Frontier Intelligence" abstract only ties KDA to
+ * training at scale), so every formula here is derived from the forward one.  The pages describe only the forward recurrence; these are its exact derivatives,
  * for a loss L with dL/do = d_o and dL/dS_T = d_sfinal:
  *   d_o      : [B, T, H, Dv] float32;   d_sfinal : [B, H, Dk, Dv] float32, or NULL for zero
  *   dq, dk   : [B, T, H, Dk] float32;   dv : [B, T, H, Dv] float32   (written)
@@ -197,7 +212,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
 size_t kda_chunk_bwd_workspace_bytes(int64_t B, int64_t T, int H, int Dk, int Dv, kda_dtype dtype);
 
 /*
- * Gradients of kda_varlen_fwd: the packed layouts of kda_varlen_fwd, the outputs as for
+ * Gradients of kda_varlen_fwd (defined as for kda_chunk_bwd, per packed sequence): the packed layouts of kda_varlen_fwd, the outputs as for
  * kda_chunk_bwd ([total, H, D] for the token tensors, [N, H, Dk, Dv] for d_sfinal and ds0).
  */
 kda_status kda_varlen_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,

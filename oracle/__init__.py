@@ -176,6 +176,15 @@ def prologue(q, k, g, beta, g_logit=False, beta_logit=False, qk_l2norm=False):
     return q, k, g, beta
 
 
+def rel_err(x: np.ndarray, ref: np.ndarray) -> float:
+    """Parity metric against the oracle: max|x - ref| / RMS(ref) over the whole array
+    (max|x| when ref is all zero)."""
+    rms = float(np.sqrt(np.mean(np.square(ref, dtype=np.float64))))
+    if rms == 0.0:
+        return float(np.abs(x).max()) if x.size else 0.0
+    return float(np.abs(x.astype(np.float64) - ref).max() / rms)
+
+
 def forward_inputs(inp, cols=None, want_state=True, nthreads=0):
     """Oracle on a ``kda_inputs.Inputs`` bundle (its prologue flags applied first)."""
     sp = inp.spec

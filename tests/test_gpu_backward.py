@@ -92,6 +92,15 @@ def test_backward_long_sequences():
     check(inp, run_bwd(inp, d_o, d_sf), reference(inp, d_o, d_sf))
 
 
+def test_backward_workload_chunk_b4_h16_t8192_d128_bf16():
+    """The benchmarked backward call: B=4 H=16 T=8192 d=128 bf16 (bound-forced gates), no final-state
+    gradient, every gradient of the whole batch against the oracle's fp64 reverse mode."""
+    spec = kda_inputs.workload("chunk_b4_h16_t8192_d128_bf16")
+    inp = kda_inputs.generate(spec)
+    d_o, d_sf = cotangents(spec, 5)
+    check(inp, run_bwd(inp, d_o, d_sf, with_dsf=False), reference(inp, d_o, d_sf, with_dsf=False))
+
+
 def test_backward_long_memory_gate():
     spec = kda_inputs.Spec([1500], 2, 128, 128, "bf16", "longmem", seed=82, name="bwd-longmem")
     inp = kda_inputs.generate(spec)

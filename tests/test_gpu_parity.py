@@ -301,13 +301,50 @@ def test_s_final_may_alias_s0(fused):
     assert rc == 0 and torch.equal(st, sf) and torch.equal(o2, o)
 
 
+def test_s_final_may_alias_s0_split_t():
+    """One long sequence with one head runs as a split-T segment scan (P = 2 segments): s0 is read
+    by the segment fold, s_final written by the last segment's workgroups; aliasing the two is safe."""
+    spec = kda_inputs.Spec([8192], 1, 128, 128, "bf16", "softplus", s0_std=0.02, seed=28)
+    inp = kda_inputs.generate(spec)
+    d = device_inputs(inp, True)
+    o, sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    st = d["s0"].clone()
+    o2 = torch.empty_like(o)
+    nws = kda.chunk_workspace_bytes(1, 8192, 1, 128, 128)
+    assert nws > 128 * kda.chunk_workspace_bytes(1, 64, 1, 128, 128)  # the segment states are part of it
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    rc = kda.chunk_fwd_raw(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["g"].data_ptr(),
+                           d["beta"].data_ptr(), st.data_ptr(), o2.data_ptr(), st.data_ptr(), 1, 8192, 1, 128, 128,
+                           64, kda.DTYPE[torch.bfloat16], None, ws.data_ptr(), nws,
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.equal(st, sf) and torch.equal(o2, o)
+    check(inp, o.reshape(8192, 1, 128).cpu().numpy(), sf.cpu().numpy())
+
+
+def test_varlen_without_tokens_takes_the_queried_workspace():
+    """total = 0: the size query returns 0, and a call given that size passes s0 to s_final."""
+    N, H = 3, 2
+    assert kda.varlen_workspace_bytes(N, 0, H, 128, 128) == 0
+    s0 = torch.randn((N, H, 128, 128), device="cuda")
+    sf = torch.full_like(s0, float("nan"))
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    rc = kda.varlen_fwd_raw(None, None, None, None, None, cu.data_ptr(), N, 0, s0.data_ptr(), None, sf.data_ptr(),
+                            H, 128, 128, 64, kda.DTYPE[torch.bfloat16], None, ws.data_ptr(), 0,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0, kda.load_library().kda_last_error()
+    assert torch.equal(sf, s0)
+
+
 def test_workload_prefill_b1_h8_t1m_d128_bf16():
     """Million-token prefill (long-memory gate): final state and outputs on sampled state
     columns, each computed exactly by the oracle on its own (columns are independent)."""
     spec = kda_inputs.workload("prefill_b1_h8_t1m_d128_bf16")
     inp = kda_inputs.generate(spec)
     o, s = run_chunk(inp)
-    cols = [0, 45, 127]
+    cols = [0, 45, 70, 127]  # one column in each 32-column chain slice
     eo, es = check(inp, o, s, cols=cols)
     # the state after a million tokens stays bounded (the update is a contraction plus a write)
     assert np.isfinite(s).all() and np.abs(s).max() < 1e3
