@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_noalloc_raw", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
            "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "chunk_workspace_bytes",
            "varlen_workspace_bytes", "DTYPE", "Prologue", "prologue", "chunk_bwd", "varlen_bwd", "chunk_bwd_raw",
            "varlen_bwd_raw", "chunk_bwd_workspace_bytes", "varlen_bwd_workspace_bytes", "ChunkKDA"]
@@ -80,6 +80,8 @@ def load_library():
     L.kda_chunk_fwd.restype = ci
     L.kda_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, ci, ci, ci, ci, ci, pp, vp, sz, vp]
     L.kda_varlen_fwd.restype = ci
+    L.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, ci, ci, ci, ci, ci, pp, vp]
+    L.kda_chunk_fwd_noalloc.restype = ci
     L.kda_chunk_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_chunk_workspace_bytes.restype = sz
     L.kda_varlen_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
@@ -111,6 +113,11 @@ def chunk_fwd_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtyp
                   workspace_bytes, stream) -> int:
     return load_library().kda_chunk_fwd(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, prologue,
                                         workspace, workspace_bytes, stream)
+
+
+def chunk_fwd_noalloc_raw(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype, prologue, stream) -> int:
+    return load_library().kda_chunk_fwd_noalloc(q, k, v, g, beta, s0, o, s_final, B, T, H, Dk, Dv, chunk, dtype,
+                                                prologue, stream)
 
 
 def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype, prologue, workspace,
@@ -236,6 +243,37 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _check(chunk_fwd_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o), _ptr(sf),
                              B, T, H, Dk, Dv, chunk, DTYPE[q.dtype], pro, _ptr(ws), ws_bytes, _stream(q.device)))
     return o, sf
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                      s0: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                      s_final: Optional[torch.Tensor] = None, g_logit: bool = False, beta_logit: bool = False,
+                      qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """:func:`chunk_fwd` through the library's fixed per-GPU scratch (no workspace, nothing
+    allocated by the library).  Pass preallocated ``o`` [B, T, H, Dv] (fp32) and ``s_final``
+    [B, H, Dk, Dv] (fp32, or None for no final state) to allocate nothing here either; if ``o`` is
+    None it is allocated with torch.  Calls on one GPU share the scratch and must not overlap."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if q.dtype not in DTYPE:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    pro = _gates(g, beta, (B, T, H, Dk), (B, T, H), g_logit, beta_logit, qk_l2norm)
+    if s0 is not None:
+        _need(s0, "s0", torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32, (B, T, H, Dv))
+    if s_final is not None:
+        _need(s_final, "s_final", torch.float32, (B, H, Dk, Dv))
+    with torch.cuda.device(q.device):
+        _check(chunk_fwd_noalloc_raw(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
+                                     _ptr(s_final), B, T, H, Dk, Dv, 64, DTYPE[q.dtype], pro, _stream(q.device)))
+    return o, s_final
 
 
 def varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -4,6 +4,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kda.h"
@@ -95,9 +96,78 @@ kda_status run_chunked(const kda::ChunkArgs& a, void* workspace, size_t workspac
     return launched(kda::launch_chunk_fwd_two_pass(a, workspace, st), what);
 }
 
+// ---------------------------------------------------------------------------- fixed scratch
+// Device memory of kda_chunk_fwd_noalloc, for callers that cannot allocate: the per-window records
+// of the two-kernel path (and the carried state when s_final is NULL).  Every GPU that runs the
+// library holds its own copy for the life of the process.  Its address on a device comes from
+// hipGetSymbolAddress, looked up once per device with that device current; host code uses only that
+// address, never the array's name (which on the host is a stand-in, not a device address).
+constexpr int64_t kScratchBytes = int64_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kda_status scratch_of_current_device(void** out, const char* what) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_HIP, "%s: device %d out of range", what, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KDA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", what, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
+                                 int Dv, int chunk, kda_dtype dtype, const kda_prologue* prologue, void* stream) {
+    const char* what = "kda_chunk_fwd_noalloc";
+    kda_status st;
+    kda::Prologue pro;
+    if ((st = check_dtype(dtype)) != KDA_OK) return st;
+    if ((st = read_prologue(prologue, pro)) != KDA_OK) return st;
+    if ((st = check_head_dims(H, Dk, Dv)) != KDA_OK) return st;
+    if (chunk != 64) return fail(KDA_ERR_BAD_SHAPE, "chunk must be 64 (got %d)", chunk);
+    if (B < 0 || T < 0) return fail(KDA_ERR_BAD_SHAPE, "B and T must be >= 0");
+    if (T > 0 && B > INT64_MAX / T) return fail(KDA_ERR_BAD_SHAPE, "B*T overflows");
+    const bool tokens = B > 0 && T > 0;
+    if ((st = check_ptrs({{q, "q", tokens}, {k, "k", tokens}, {v, "v", tokens}, {g, "g", tokens},
+                          {beta, "beta", tokens}, {o, "o", tokens}, {s0, "s0", false},
+                          {s_final, "s_final", false}})) != KDA_OK)
+        return st;
+    if (B == 0 || (!tokens && !s_final)) return ok();
+    kda::ChunkArgs a{q, k, v, g, beta, s0, o, s_final, nullptr, T, B * T, B, H, Dk, Dv, dtype == KDA_F32, pro};
+    const int64_t grid = kda::chunk_grid_size(a.N, a.H, a.Dv);
+    if (grid > 0x7fffffff) return fail(KDA_ERR_BAD_SHAPE, "%s: %lld sequence-heads exceed the grid limit", what,
+                                       (long long)(a.N * a.H));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!tokens) return launched(kda::launch_chunk_fwd(a, hs), what);  // s0 (or zeros) to s_final, no scratch
+    if (kda::chunk_window_chunks(a, kScratchBytes) < 1)
+        return fail(KDA_ERR_BAD_SHAPE,
+                    "%s: B*H = %lld sequence-heads need %lld bytes of scratch for one 64-token window; the fixed "
+                    "scratch holds %lld",
+                    what, (long long)(a.N * a.H),
+                    (long long)(kda::chunk_window_state_bytes(a) + kda::chunk_workspace_bytes(
+                        kda::ChunkArgs{q, k, v, g, beta, s0, o, s_final, nullptr, 64, B * 64, B, H, Dk, Dv,
+                                       dtype == KDA_F32, pro})),
+                    (long long)kScratchBytes);
+    void* base = nullptr;
+    if ((st = scratch_of_current_device(&base, what)) != KDA_OK) return st;
+    return launched(kda::launch_chunk_fwd_windows(a, static_cast<char*>(base), kScratchBytes, hs), what);
+}
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk, int Dv,

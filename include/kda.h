@@ -124,6 +124,28 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd without any allocation or workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, layouts, results and
+ * errors as for kda_chunk_fwd; the results equal its two-kernel path bit for bit.
+ * The library keeps one fixed scratch area of 128 MiB per GPU (a static device
+ * array, held from the first call on that GPU until the process ends) and
+ * runs the call in windows of W * 64 tokens whose per-chunk records fit there:
+ * W = floor((128 MiB - state) / (B * H * record)), with the record size given
+ * for kda_chunk_workspace_bytes and state = B*H*Dk*Dv*4 bytes (rounded up to
+ * 256) when s_final is NULL, else 0.  Calls with W < 1 (B*H above 1254 at
+ * Dk = 128 with bf16 inputs and s_final given, above 777 without) are rejected with
+ * KDA_ERR_BAD_SHAPE.  The scratch of the current device is used: `stream`
+ * must belong to it.  Every call on a GPU shares that GPU's scratch, so calls
+ * that may overlap on one GPU (different streams, or concurrent host threads)
+ * race and must be serialised by the caller.  Nothing is allocated, freed or
+ * cleared by the library in this call.
+ */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                 const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
+                                 int Dv, int chunk, kda_dtype dtype, const kda_prologue* prologue, void* stream);
+
+/*
  * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
  * the arguments are unsupported): B * ceil(T/64) * H records of
  * 64*Dk*10 (bf16) or 64*Dk*12 (fp32) + 24576 + 4*Dk bytes

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_last_error", "kda_version",
-              "kda_chunk_workspace_bytes", "kda_varlen_workspace_bytes"]:
+              "kda_chunk_workspace_bytes", "kda_varlen_workspace_bytes", "kda_chunk_fwd_noalloc"]:
         assert n in names
 
 
@@ -67,6 +67,38 @@ def test_chunk_nothing_to_do_returns_ok():
     assert chunk(q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
     assert chunk(B=0) == 0
     assert last_error() == ""
+
+
+def chunk_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, s_final=None, B=1, T=64, H=1, Dk=128,
+             Dv=128, chunk=64, dtype=1, prologue=None, stream=None)
+    a.update(kw)
+    return kda.chunk_fwd_noalloc_raw(*a.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Dk=96), 2, "Dk"), (dict(chunk=32), 2, "chunk"), (dict(T=-1), 2, "T"), (dict(dtype=7), 3, "dtype"),
+    (dict(q=None), 1, "q"), (dict(o=None), 1, "o"), (dict(s_final=FAKE + 4), 4, "s_final"),
+    # one 64-token window of 1255 sequence-heads needs more than the fixed 128 MiB scratch (107008 B each)
+    (dict(B=1255, s_final=FAKE), 2, "scratch"),
+    # without s_final the carried state (64 KiB per sequence-head) lives in the scratch too
+    (dict(B=778), 2, "scratch"),
+])
+def test_chunk_noalloc_validation(kw, status, msg):
+    assert chunk_noalloc(**kw) == status
+    assert msg in last_error()
+
+
+def test_chunk_noalloc_largest_accepted_sizes_pass_validation():
+    """The scratch bound: 1254 sequence-heads with s_final, 777 without (the validation tests above
+    reject one more; accepting calls need a device, so only the bound itself is checked here)."""
+    assert (128 << 20) // 107008 == 1254
+    assert ((128 << 20) - 777 * 65536) // 107008 >= 777 and ((128 << 20) - 778 * 65536) // 107008 < 778
+
+
+def test_chunk_noalloc_nothing_to_do_returns_ok():
+    assert chunk_noalloc(q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
+    assert chunk_noalloc(B=0) == 0
 
 
 def varlen(**kw):
