@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 OBJ_DIR = os.path.join(PKG, "_build")
-SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk2.hip", "kda_decode.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_chunk2.hip", "kda_fwd16.hip", "kda_decode.hip", "kda_bwd.hip",
+           "kda_calib.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -554,26 +554,6 @@ struct ChainOutOps {
     float4 gC;
 };
 
-// Long sequences with few heads split the chunk range into P segments of L chunks (the one-GPU
-// form of the segment scan the worldcybernews page's third paragraph describes across GPUs):
-//   mode 1 (segment maps), items (n, h, p < P-1), (Dv + Dk)/32 column slices: the segment run
-//     from a zero state gives S0_p (its Dv value columns); run on the identity with V = 0 it gives
-//     the segment's transition Phi_p (Dk more columns).  Both go to sx [item][Dk][Dv + Dk]; no o.
-//   mode 2 (outputs), items (n, h, p): segment p from its true initial state (s0 for p = 0,
-//     else sfold [n][h][p][Dk][Dv] from the fold kernel), o written, s_final from p = P - 1.
-//   mode 0: whole sequences (items (n, h)), s0 -> s_final.
-//   mode 3: as mode 0, and the state at the start of every chunk goes to sx [slot][h][Dk][Dv]
-//     (for the backward pass; compiled state-only with the stores, SO = ST = true).
-struct ChainMode {
-    int mode;      // 0, 1, 2 or 3
-    int P;         // segments per sequence (modes 1, 2)
-    int64_t L;     // chunks per segment (modes 1, 2)
-    float* sx;     // mode 1 output; mode 3: chunk-start states
-    const float* sfold;  // mode 2 input
-    float* xu = nullptr;  // mode 3: X and U of every chunk, [slot][h][2][64][Dv] (rows past the end zero)
-    const int32_t* order = nullptr;  // packed sequences: item i runs sequence order[i / H] (longest first)
-};
-
 // SO (state only, modes 1 and 3): the output products, their operands and the o traffic are compiled
 // out.  F32: precision policy of the records; IN_F32: type of v; ST: mode 3's stores are compiled in.
 //
@@ -1046,7 +1026,9 @@ static int64_t segment_bytes(const ChunkArgs& a, int P) {
 // packed sequences: their order, longest first, for the chain's dispatch [N] int32
 static int64_t order_bytes(const ChunkArgs& a) { return a.cu_seqlens ? ((a.N * 4 + 255) / 256) * 256 : 0; }
 
+// bf16 inputs take the fp16-operand path of kda_fwd16.hip; fp32 inputs the fp32 records here.
 int64_t chunk_workspace_bytes(const ChunkArgs& a) {
+    if (!a.f32) return chunk16_workspace_bytes(a);
     return records_bytes(a) + segment_bytes(a, chunk_segments(a)) + order_bytes(a);
 }
 
@@ -1077,6 +1059,20 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* __restric
 }
 
 static int64_t chain_grid(int64_t items, int slices) { return ((items + 7) / 8) * 8 * slices; }
+
+hipError_t launch_seq_order(const int32_t* cu, int64_t N, int64_t total, int32_t* order, hipStream_t st) {
+    if (N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, cu, N, total, order);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold(int Dk, const float* s0, const float* sx, float* sfold, int64_t items, int H, int Dv, int P,
+                       hipStream_t st) {
+    const dim3 grid((unsigned)(items * (Dv / kS)));
+    if (Dk == 128) hipLaunchKernelGGL((fold_kernel<128>), grid, dim3(256), 0, st, s0, sx, sfold, H, Dv, P);
+    else hipLaunchKernelGGL((fold_kernel<64>), grid, dim3(256), 0, st, s0, sx, sfold, H, Dv, P);
+    return hipGetLastError();
+}
 
 template <int DK, bool F32>
 static hipError_t launch_two(const ChunkArgs& a, void* ws, hipStream_t st, bool allow_split = true) {
@@ -1159,8 +1155,8 @@ hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, flo
 }
 
 hipError_t launch_chunk_fwd_two_pass(const ChunkArgs& a, void* ws, hipStream_t st) {
-    if (a.Dk == 128) return a.f32 ? launch_two<128, true>(a, ws, st) : launch_two<128, false>(a, ws, st);
-    return a.f32 ? launch_two<64, true>(a, ws, st) : launch_two<64, false>(a, ws, st);
+    if (!a.f32) return launch_chunk_fwd16(a, ws, st, true);
+    return a.Dk == 128 ? launch_two<128, true>(a, ws, st) : launch_two<64, true>(a, ws, st);
 }
 
 // ---------------------------------------------------------------------------- T-windows in a fixed scratch
@@ -1176,7 +1172,7 @@ int64_t chunk_window_state_bytes(const ChunkArgs& a) {
 }
 
 int64_t chunk_window_chunks(const ChunkArgs& a, int64_t scratch_bytes) {
-    const int64_t per_chunk = a.N * a.H * chunk_record_bytes(a.Dk, a.f32);
+    const int64_t per_chunk = a.N * a.H * (a.f32 ? chunk_record_bytes(a.Dk, true) : chunk16_record_bytes(a.Dk));
     const int64_t room = scratch_bytes - chunk_window_state_bytes(a);
     if (per_chunk <= 0 || room < per_chunk) return 0;
     const int64_t nch = (a.T_fixed + kC - 1) / kC;
@@ -1203,10 +1199,8 @@ hipError_t launch_chunk_fwd_windows(const ChunkArgs& a, char* scratch, int64_t s
         w.s0 = t0 == 0 ? a.s0 : carry;
         w.s_final = carry;
         hipError_t e;
-        if (a.Dk == 128)
-            e = a.f32 ? launch_two<128, true>(w, recs, st, false) : launch_two<128, false>(w, recs, st, false);
-        else
-            e = a.f32 ? launch_two<64, true>(w, recs, st, false) : launch_two<64, false>(w, recs, st, false);
+        if (!a.f32) e = launch_chunk_fwd16(w, recs, st, false);
+        else e = a.Dk == 128 ? launch_two<128, true>(w, recs, st, false) : launch_two<64, true>(w, recs, st, false);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -39,6 +39,26 @@ struct DecodeArgs {
     Prologue pro;
 };
 
+// Long sequences with few heads split the chunk range into P segments of L chunks (the one-GPU
+// form of the segment scan the worldcybernews page's third paragraph describes across GPUs):
+//   mode 1 (segment maps), items (n, h, p < P-1), (Dv + Dk)/32 column slices: the segment run
+//     from a zero state gives S0_p (its Dv value columns); run on the identity with V = 0 it gives
+//     the segment's transition Phi_p (Dk more columns).  Both go to sx [item][Dk][Dv + Dk]; no o.
+//   mode 2 (outputs), items (n, h, p): segment p from its true initial state, sfold [n][h][p][Dk][Dv]
+//     from the fold kernel (which copies s0 into p = 0), o written, s_final from p = P - 1.
+//   mode 0: whole sequences (items (n, h)), s0 -> s_final.
+//   mode 3: as mode 0, and the state at the start of every chunk goes to sx [slot][h][Dk][Dv]
+//     (for the backward pass; compiled state-only with the stores, SO = ST = true).
+struct ChainMode {
+    int mode;      // 0, 1, 2 or 3
+    int P;         // segments per sequence (modes 1, 2)
+    int64_t L;     // chunks per segment (modes 1, 2)
+    float* sx;     // mode 1 output; mode 3: chunk-start states
+    const float* sfold;  // mode 2 input
+    float* xu = nullptr;  // mode 3: X and U of every chunk, [slot][h][2][64][Dv] (rows past the end zero)
+    const int32_t* order = nullptr;  // packed sequences: item i runs sequence order[i / H] (longest first)
+};
+
 int64_t chunk_grid_size(int64_t N, int H, int Dv);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t st);
 // Two-kernel path: per-chunk preparation into a workspace, then the state chain.
@@ -59,6 +79,17 @@ int64_t chunk_states_record_bytes(int Dk);
 hipError_t launch_chunk_states(const ChunkArgs& a, void* recs, float* brecs, float* states, float* xu,
                                hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// Shared pieces of the two-kernel paths (kda_chunk2.hip): the packed sequences ranked longest first
+// (order[rank] = n), and the split-T fold S_in(p+1) = Phi_p S_in(p) + S0_p over `items` = N*H heads.
+hipError_t launch_seq_order(const int32_t* cu, int64_t N, int64_t total, int32_t* order, hipStream_t st);
+hipError_t launch_fold(int Dk, const float* s0, const float* sx, float* sfold, int64_t items, int H, int Dv, int P,
+                       hipStream_t st);
+int chunk_segments(const ChunkArgs& a);
+// The bf16-input forward with fp16 matrix-core operands (kda_fwd16.hip): record bytes per (chunk, head),
+// workspace bytes and launch.
+int64_t chunk16_record_bytes(int Dk);
+int64_t chunk16_workspace_bytes(const ChunkArgs& a);
+hipError_t launch_chunk_fwd16(const ChunkArgs& a, void* ws, hipStream_t st, bool allow_split);
 
 // Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets):
 // Qt^T, Kt^T [DK][64]; Kb [64][DK]; P^T, Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1};

@@ -55,7 +55,7 @@ def chunk(**kw):
     (dict(beta=None), 1, "beta"), (dict(o=None), 1, "o"),
     (dict(q=FAKE + 2), 4, "q"), (dict(v=FAKE + 8), 4, "v"), (dict(s0=FAKE + 4), 4, "s0"),
     (dict(s_final=FAKE + 12), 4, "s_final"), (dict(workspace=FAKE + 8, workspace_bytes=1 << 30), 4, "workspace"),
-    (dict(workspace=FAKE, workspace_bytes=107007), 2, "workspace"),
+    (dict(workspace=FAKE, workspace_bytes=74239), 2, "workspace"),
 ])
 def test_chunk_validation(kw, status, msg):
     assert chunk(**kw) == status
@@ -79,10 +79,10 @@ def chunk_noalloc(**kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(Dk=96), 2, "Dk"), (dict(chunk=32), 2, "chunk"), (dict(T=-1), 2, "T"), (dict(dtype=7), 3, "dtype"),
     (dict(q=None), 1, "q"), (dict(o=None), 1, "o"), (dict(s_final=FAKE + 4), 4, "s_final"),
-    # one 64-token window of 1255 sequence-heads needs more than the fixed 128 MiB scratch (107008 B each)
-    (dict(B=1255, s_final=FAKE), 2, "scratch"),
+    # one 64-token window of 1808 sequence-heads needs more than the fixed 128 MiB scratch (74240 B each)
+    (dict(B=1808, s_final=FAKE), 2, "scratch"),
     # without s_final the carried state (64 KiB per sequence-head) lives in the scratch too
-    (dict(B=778), 2, "scratch"),
+    (dict(B=961), 2, "scratch"),
 ])
 def test_chunk_noalloc_validation(kw, status, msg):
     assert chunk_noalloc(**kw) == status
@@ -90,10 +90,11 @@ def test_chunk_noalloc_validation(kw, status, msg):
 
 
 def test_chunk_noalloc_largest_accepted_sizes_pass_validation():
-    """The scratch bound: 1254 sequence-heads with s_final, 777 without (the validation tests above
-    reject one more; accepting calls need a device, so only the bound itself is checked here)."""
-    assert (128 << 20) // 107008 == 1254
-    assert ((128 << 20) - 777 * 65536) // 107008 >= 777 and ((128 << 20) - 778 * 65536) // 107008 < 778
+    """The scratch bound at Dk = Dv = 128 with bf16 inputs: 1807 sequence-heads with s_final, 960 without
+    (the validation tests above reject one more; accepting calls need a device, so only the bound
+    itself is checked here)."""
+    assert (128 << 20) // 74240 == 1807
+    assert ((128 << 20) - 960 * 65536) // 74240 >= 960 and ((128 << 20) - 961 * 65536) // 74240 < 961
 
 
 def test_chunk_noalloc_nothing_to_do_returns_ok():
@@ -112,7 +113,7 @@ def varlen(**kw):
     (dict(cu=None), 1, "cu_seqlens"), (dict(N=-1), 2, "N"), (dict(total=-5), 2, "total"),
     (dict(total=1 << 31), 2, "int32"), (dict(Dk=48), 2, "Dk"), (dict(chunk=128), 2, "chunk"),
     (dict(o=FAKE + 4), 4, "o"), (dict(dtype=-1), 3, "dtype"), (dict(g=None), 1, "g"),
-    (dict(workspace=FAKE, workspace_bytes=(100 // 64 + 2) * 2 * 107008 - 1), 2, "workspace"),
+    (dict(workspace=FAKE, workspace_bytes=(100 // 64 + 2) * 2 * 74240 - 1), 2, "workspace"),
 ])
 def test_varlen_validation(kw, status, msg):
     assert varlen(**kw) == status
@@ -120,15 +121,16 @@ def test_varlen_validation(kw, status, msg):
 
 
 def record_bytes(Dk, dtype):
-    """Operand record of one (chunk, head): Qt (split, 4 B/value), Kt (bf16 hi 2 B or fp32 4 B),
-    Kbar^T (4 B), six 2 KiB fragments each of M^{-1} Diag(b) and of P, gamma_C (fp32)."""
-    kt = 4 if dtype == 0 else 2
-    return 64 * Dk * (4 + kt + 4) + 2 * 6 * 2048 + 4 * Dk
+    """Operand record of one (chunk, head).  fp32 inputs: Qt, Kt, Kbar^T as fp32 (4 B/value), six
+    2 KiB fragments each of M^{-1} Diag(b) and of P, gamma_C (fp32).  bf16 inputs: -W, Qh, Kbar^T as
+    fp16 (2 B/value), M^{-1} Diag(b) and P as six fp16 hi + lo fragment pairs (2 KiB each), gamma_C."""
+    per_value = 12 if dtype == 0 else 6
+    return 64 * Dk * per_value + 2 * 6 * 2048 + 4 * Dk
 
 
 def test_record_sizes():
-    assert record_bytes(128, 1) == 107008 and record_bytes(128, 0) == 123392
-    assert record_bytes(64, 1) == 65792 and record_bytes(64, 0) == 73984
+    assert record_bytes(128, 1) == 74240 and record_bytes(128, 0) == 123392
+    assert record_bytes(64, 1) == 49408 and record_bytes(64, 0) == 73984
 
 
 def segments(B, T, H, Dv):

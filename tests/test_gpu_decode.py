@@ -86,5 +86,13 @@ def test_decode_steps_equal_chunked_prefill():
         outs.append(o_t)
     torch.cuda.synchronize()
     o_d = torch.stack(outs, 1)
-    assert rel_err(o_d.cpu().numpy(), o_c.double().cpu().numpy()) < 5e-3
-    assert rel_err(st.cpu().numpy(), s_c.double().cpu().numpy()) < 5e-3
+    # the decode step runs in fp32 and lands on the oracle to ~1e-6; the chunked pass rounds its
+    # matrix-core operands (up to ~5e-3 of RMS on these gates): both are held to the oracle's bar, and
+    # to each other within twice the chunked pass's error
+    o_ref, s_ref = oracle.forward_inputs(inp)
+    assert rel_err(o_d.reshape(B * T, H, D).cpu().numpy(), o_ref) <= 1e-4
+    assert rel_err(st.cpu().numpy(), s_ref) <= 1e-4
+    assert rel_err(o_c.reshape(B * T, H, D).cpu().numpy(), o_ref) <= TOL["bf16"]
+    assert rel_err(s_c.cpu().numpy(), s_ref) <= TOL["bf16"]
+    assert rel_err(o_d.cpu().numpy(), o_c.double().cpu().numpy()) < 1e-2
+    assert rel_err(st.cpu().numpy(), s_c.double().cpu().numpy()) < 1e-2

@@ -220,9 +220,15 @@ def test_split_resume_matches_unbroken(fused):
     oa, sa = kda.chunk_fwd(*(sl(d[n], 0, T1) for n in "q k v g beta".split()), d["s0"], fused=fused)
     ob, sb = kda.chunk_fwd(*(sl(d[n], T1, 256) for n in "q k v g beta".split()), sa, fused=fused)
     torch.cuda.synchronize()
+    # the split moves every chunk boundary after T1, so the two runs round differently: both are held
+    # to the oracle's bar, and to each other within twice the error either shows on these gates
     ref = o.cpu().numpy()
     split = torch.cat([oa, ob], 1).cpu().numpy()
-    assert rel_err(split, ref) < 2e-3 and rel_err(sb.cpu().numpy(), sf.cpu().numpy()) < 2e-3
+    o_ref, s_ref = reference(inp)
+    for oo, ss in ((split, sb), (ref, sf)):
+        assert rel_err(oo.reshape(256, 2, 128), o_ref) <= TOL["bf16"]
+        assert rel_err(ss.cpu().numpy(), s_ref) <= TOL["bf16"]
+    assert rel_err(split, ref) < 1e-2 and rel_err(sb.cpu().numpy(), sf.cpu().numpy()) < 1e-2
 
 
 @PATHS
