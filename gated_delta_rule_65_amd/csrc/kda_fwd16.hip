@@ -12,8 +12,10 @@
 //
 // prep16_kernel computes, per (chunk, head), -W, Qh, Kbar^T (fp16), N and P (fp16 hi + lo) and
 // gamma_C, and stores them in matrix-core operand order.  chain16_kernel carries the state of one
-// (sequence, head, 32-column slice) through the chunks: per chunk, U (state waves), then the state
-// tiles (all waves), two workgroup barriers; the outputs and U0 of the next chunk fill the gaps.
+// (sequence, head, 32-column slice) through the chunks with two workgroup barriers per chunk: U (state
+// waves), then the state tiles (all waves).  The rest fills the gaps: the state waves stage V and form
+// U0 of the next chunk; the output waves form Qh S after the state tiles and add P U0 in the next
+// chunk's first phase.
 //
 // Channel order.  Within each 32-channel step, lane group g of an operand fragment holds the
 // channels 32s + 4g + {0..3} and 32s + 16 + 4g + {0..3} (pi order).  A 16x16 product result holds,
@@ -36,7 +38,7 @@ namespace {
 
 constexpr int kC = 64;            // tokens per chunk
 constexpr int kS = 32;            // state columns per chain workgroup
-constexpr int kThreads = 512;     // chain workgroup: eight waves
+constexpr int kThreads = 576;     // chain workgroup: eight computing waves and one prefetching wave
 constexpr int kPl = 1024;         // one fragment plane: 64 lanes x 16 bytes
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -577,7 +579,7 @@ struct Chain16Lds {
 };
 
 // Operands of one chunk.  A state wave (row block rb) holds -W rows of rb and the Kbar^T rows and
-// gamma_C of its state tiles, plus N rows of rb and its v pieces for the chunk after (U0 of the next
+// gamma_C of its state tiles, and, for the chunk after, N rows of rb and its pieces of v (U0 of the next
 // chunk is formed during this one).  An output wave holds Qh and P rows of rb and its state tiles'
 // Kbar^T rows and gamma_C.
 template <int DK>
@@ -616,9 +618,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
     float* sO = reinterpret_cast<float*>(smem + L::O);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
-    const int rb = w & 3;
-    const int cbw = (w * TPW) >> 1;                            // channel block of this wave's state tiles
-    auto nbt = [&](int i) { return (w * TPW + i) & 1; };      // column half of state tile i
+    const bool prefetcher = w == 8;                            // the ninth wave only prefetches records
+    const int wt = prefetcher ? 0 : w;
+    const int rb = wt & 3;
+    const int cbw = (wt * TPW) >> 1;                           // channel block of this wave's state tiles
+    auto nbt = [&](int i) { return (wt * TPW + i) & 1; };     // column half of state tile i
     const int NV = Dv / kS;
     const int NS = cm.mode == 1 ? NV + DK / kS : NV;
     const int segs = cm.mode == 1 ? cm.P - 1 : (cm.mode == 2 ? cm.P : 1);
@@ -654,7 +658,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
 
     // ---- state tiles of this wave (fp32, registers) and their fp16 copy in LDS
     f32x4_t accS[TPW];
-    if (cm.mode == 1) {  // zero value columns; the identity on the identity columns
+    if (prefetcher) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) accS[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else if (cm.mode == 1) {  // zero value columns; the identity on the identity columns
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
@@ -683,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             *reinterpret_cast<f16x4_t*>(sS + (buf * kS + 16 * nbt(i) + m) * L::SST + spos) = x;
         }
     };
-    store_state(jbeg & 1);
+    if (!prefetcher) store_state(jbeg & 1);
 
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
@@ -715,69 +722,79 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
         return lds_h8(sS + (buf * kS + 16 * nb + m) * L::SST + 32 * s + 8 * cg);
     };
 
-    if (w < 4) {
-        // ======================= state waves: U of row block rb, U0 of the next chunk
-        using Ops = StOps16<DK>;
-        const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
-        const int vrow = 16 * rb + (lane >> 2), vpiece = lane & 3;  // 16 rows x 4 pieces of 8 columns
-        const uint16_t* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * 8;
+    // V of a chunk as fp16 V^T in LDS, and U0 = N V (two passes: N hi, N lo) of row block rb: the state
+    // waves form both, for the chunk after the current one
+    const uint32_t rs_v = (uint32_t)H * (uint32_t)Dv;
+    const int vrow = 16 * rb + (lane >> 2), vpiece = lane & 3;  // 16 rows x 4 pieces of 8 columns
+    const uint16_t* __restrict__ v_l = v + (int64_t)h * Dv + col0 + vpiece * 8;
 
+    if (w < 4) {
+        // ======================= state waves: U of row block rb, V and U0 of the next chunk
+        using Ops = StOps16<DK>;
         auto load_w = [&](Ops& d, const char* rec) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) d.fW[s] = gld_h8(rec + R::W + (rb * KS + s) * kPl, lane);
         };
-        // N rows of rb and the v pieces of chunk jn (used to form U0 of chunk jn)
-        auto load_nv = [&](Ops& d, int64_t jn) {
-            const char* rec = record(jn);
+        auto load_n = [&](Ops& d, int64_t jx) {  // N rows of rb of chunk jx
+            const char* rec = record(jx);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {  // blocks 0, 1 stop at token 31: their second step repeats the first
                 const char* g = rec + R::NM + pair_of(rb, min(kb, nk - 1)) * 2 * kPl;
                 d.fN[kb][0] = gld_h8(g, lane);
                 d.fN[kb][1] = gld_h8(g + kPl, lane);
             }
-            const uint32_t rvo = (uint32_t)min(vrow, chunk_len(jn) - 1) * rs_v;
-            d.vraw = *reinterpret_cast<const uint4*>(v_l + chunk_start(jn) * (int64_t)rs_v + rvo);
         };
-        // V of the chunk whose v pieces d holds, as fp16 V^T in LDS
-        auto stage_v = [&](const Ops& d) {
-            const uint32_t u[4] = {d.vraw.x, d.vraw.y, d.vraw.z, d.vraw.w};
+        auto load_v = [&](uint4& raw, int64_t jx) {
+            const uint32_t rvo = (uint32_t)min(vrow, chunk_len(jx) - 1) * rs_v;
+            raw = *reinterpret_cast<const uint4*>(v_l + chunk_start(jx) * (int64_t)rs_v + rvo);
+        };
+        auto stage_v = [&](uint4 raw) {
+            const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sV[(vpiece * 8 + 2 * i) * L::TST + vrow] = (_Float16)(vscale * __uint_as_float(u[i] << 16));
                 sV[(vpiece * 8 + 2 * i + 1) * L::TST + vrow] = (_Float16)(vscale * __uint_as_float(u[i] & 0xffff0000u));
             }
         };
-        // U0 = N V for rows rb (two passes: N hi, N lo), into accU0 and, split, into U0^T buffer buf
         f32x4_t accU0[2];
-        auto form_u0 = [&](const Ops& d, int buf) {
+        auto form_u0 = [&](const f16x8_t (&fN)[2][2], int buf) {
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                accU0[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     if (kb >= nk) continue;
-                    const f16x8_t b = lds_h8(sV + (16 * nb + m) * L::TST + 32 * kb + 8 * cg);
-                    accU0[nb] = mma16(accU0[nb], d.fN[kb][0], b);
-                    accU0[nb] = mma16(accU0[nb], d.fN[kb][1], b);
+                    const f16x8_t bv = lds_h8(sV + (16 * nb + m) * L::TST + 32 * kb + 8 * cg);
+                    acc = mma16(acc, fN[kb][0], bv);
+                    acc = mma16(acc, fN[kb][1], bv);
                 }
+                accU0[nb] = acc;
                 f16x4_t hi, lo;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const _Float16 x = (_Float16)accU0[nb][jj];
+                    const _Float16 x = (_Float16)acc[jj];
                     hi[jj] = x;
-                    lo[jj] = (_Float16)(accU0[nb][jj] - (float)x);
+                    lo[jj] = (_Float16)(acc[jj] - (float)x);
                 }
                 _Float16* dst = sU0 + ((buf * 2) * kS + 16 * nb + m) * L::TST + 16 * rb + 4 * cg;
                 *reinterpret_cast<f16x4_t*>(dst) = hi;
                 *reinterpret_cast<f16x4_t*>(dst + kS * L::TST) = lo;
             }
         };
+        // Register sets: the set of chunk x holds -W, Kbar^T, gamma_C of chunk x and N of chunk x + 1
+        // (loaded one chunk ahead), and v of chunk x + 1 (loaded two chunks ahead, into the set of the
+        // same parity right after it is staged).
         auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
             const int64_t jn = next_chunk(jc);
             const char* recn = record(jn);
             const int b = (int)(jc & 1);
 
             // ---- phase 1:  U = U0 - W S;  V of the next chunk to LDS
+            // v two chunks ahead, first in the step: memory requests complete in order, and the loop's
+            // first wait covers every request made before it, so this one (usually an HBM miss) gets a
+            // whole step to arrive
+            const uint4 vcur = cur.vraw;
+            load_v(cur.vraw, next_chunk(next_chunk(jn)));
             f32x4_t accU[2] = {accU0[0], accU0[1]};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
@@ -790,31 +807,34 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
                 for (int jj = 0; jj < 4; ++jj) x[jj] = (_Float16)accU[nb][jj];
                 *reinterpret_cast<f16x4_t*>(sU + (16 * nb + m) * L::TST + 16 * rb + 4 * cg) = x;
             }
-            stage_v(cur);
+            stage_v(vcur);
             load_w(nxt, recn);  // after the products that read this chunk's copy
             lds_barrier();  // (1)
 
             // ---- phase 2:  state tiles;  U0 of the next chunk
             update_state(cur.fKB, cur.gC, b ^ 1);
             load_kb(nxt.fKB, nxt.gC, recn);
-            form_u0(cur, b ^ 1);
-            load_nv(nxt, next_chunk(jn));  // after the products that read this copy of N
+            form_u0(cur.fN, b ^ 1);
+            load_n(nxt, next_chunk(jn));  // after the products that read this copy of N
             lds_barrier();  // (2)
         };
         Ops opsA, opsB;
-        // U0 of the first chunk, then the operands of the first chunk and N, v of the second (the
-        // barriers are passed by every wave whether or not the sequence has chunks)
+        // U0 of the first chunk; the first chunk's operands, N of the second, v of the second and third
+        // (the barriers are passed by every wave whether or not the sequence has chunks)
         if (jbeg < jend) {
-            load_nv(opsB, jbeg);
-            stage_v(opsB);
+            load_n(opsB, jbeg);
+            load_v(opsB.vraw, jbeg);
+            stage_v(opsB.vraw);
         }
         lds_barrier();
         if (jbeg < jend) {
-            form_u0(opsB, (int)(jbeg & 1));
+            form_u0(opsB.fN, (int)(jbeg & 1));
             const char* rec = record(jbeg);
             load_w(opsA, rec);
             load_kb(opsA.fKB, opsA.gC, rec);
-            load_nv(opsA, next_chunk(jbeg));
+            load_n(opsA, next_chunk(jbeg));
+            load_v(opsA.vraw, next_chunk(jbeg));
+            load_v(opsB.vraw, next_chunk(next_chunk(jbeg)));
         }
         lds_barrier();
         // two chunks per iteration, so that the operand sets alternate without copies
@@ -824,8 +844,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             step(opsB, opsA, jc + 1);
         }
         if (jc < jend) step(opsA, opsB, jc);
-    } else {
-        // ======================= output waves: O of row block rb, and state tiles
+    } else if (w < 8) {
+        // ======================= output waves: state tiles; O = Qh S (phase 2) + P U0 (next phase 1)
         using Ops = OutOps16<DK>;
         const uint32_t rs_o = (uint32_t)H * (uint32_t)Dv;
         float* __restrict__ o_l = o + (int64_t)h * Dv + col0 + (lane & 7) * 4;
@@ -846,13 +866,37 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
                 }
             }
         };
+        // O += P U0 of the chunk whose P fragments are given (U0^T buffer buf), then o rows to HBM
+        f32x4_t accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        float4 ost[2];  // this lane's two o pieces, stored after the step's loads
+        auto finish_o = [&](const f16x8_t (&fP)[2][2], int buf) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb >= nk) continue;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const _Float16* u0 = sU0 + ((buf * 2) * kS + 16 * nb + m) * L::TST + 32 * kb + 8 * cg;
+                    const f16x8_t uh = lds_h8(u0), ul = lds_h8(u0 + kS * L::TST);
+                    accO[nb] = mma16(accO[nb], fP[kb][0], uh);
+                    accO[nb] = mma16(accO[nb], fP[kb][0], ul);
+                    accO[nb] = mma16(accO[nb], fP[kb][1], uh);
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) sO[(16 * rb + 4 * cg + jj) * (kS + 4) + 16 * nb + m] = accO[nb][jj];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)  // this wave's own rows: no barrier needed
+                ost[half] = *reinterpret_cast<const float4*>(&sO[(16 * rb + 8 * half + (lane >> 3)) * (kS + 4) +
+                                                                   (lane & 7) * 4]);
+        };
         auto store_o = [&](int64_t tc, int ntc) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int rr = 16 * rb + 8 * half + (lane >> 3);
-                const float4 x = *reinterpret_cast<const float4*>(&sO[rr * (kS + 4) + (lane & 7) * 4]);
                 if (rr < ntc)  // o is not read again by this call: streamed past the caches
-                    __builtin_nontemporal_store(f32x4_t{x.x, x.y, x.z, x.w},
+                    __builtin_nontemporal_store(f32x4_t{ost[half].x, ost[half].y, ost[half].z, ost[half].w},
                                                 reinterpret_cast<f32x4_t*>(o_l + (tc + rr) * (int64_t)rs_o));
             }
         };
@@ -861,38 +905,26 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             const char* recn = record(jn);
             const int b = (int)(jc & 1);
 
-            // ---- phase 1:  O = Qh S + P U0
+            // ---- phase 1:  O of the previous chunk (its P U0 part) to HBM, stored after the loads
+            // (memory requests complete in order: a wait for a load made after a store waits for the store)
             if constexpr (!SO) {
-                f32x4_t accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                if (jc > jbeg) finish_o(nxt.fP, b ^ 1);
+                load_p(nxt, recn);  // after the products that read the previous chunk's copy
+                if (jc > jbeg) store_o(chunk_start(jc - 1), kC);
+            }
+            lds_barrier();  // (1)
+
+            // ---- phase 2:  state tiles;  Qh S of this chunk
+            update_state(cur.fKB, cur.gC, b ^ 1);
+            load_kb(nxt.fKB, nxt.gC, recn);
+            if constexpr (!SO) {
+                accO[0] = accO[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) accO[nb] = mma16(accO[nb], cur.fQ[s], s_frag(b, s, nb));
                 load_q(nxt, recn);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    if (kb >= nk) continue;
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        const _Float16* u0 = sU0 + ((b * 2) * kS + 16 * nb + m) * L::TST + 32 * kb + 8 * cg;
-                        const f16x8_t uh = lds_h8(u0), ul = lds_h8(u0 + kS * L::TST);
-                        accO[nb] = mma16(accO[nb], cur.fP[kb][0], uh);
-                        accO[nb] = mma16(accO[nb], cur.fP[kb][0], ul);
-                        accO[nb] = mma16(accO[nb], cur.fP[kb][1], uh);
-                    }
-                }
-                load_p(nxt, recn);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) sO[(16 * rb + 4 * cg + jj) * (kS + 4) + 16 * nb + m] = accO[nb][jj];
-                store_o(chunk_start(jc), chunk_len(jc));
             }
-            lds_barrier();  // (1)
-
-            // ---- phase 2:  state tiles
-            update_state(cur.fKB, cur.gC, b ^ 1);
-            load_kb(nxt.fKB, nxt.gC, recn);
             lds_barrier();  // (2)
         };
         Ops opsA, opsB;
@@ -902,17 +934,63 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             load_p(opsA, rec);
             load_kb(opsA.fKB, opsA.gC, rec);
         }
-        lds_barrier();  // (the state waves' U0 of the first chunk)
-        lds_barrier();
+        lds_barrier();  // (the state waves' V of the first chunk)
+        lds_barrier();  // (their U0 of the first chunk)
         int64_t jc = jbeg;
         for (; jc + 1 < jend; jc += 2) {
             step(opsA, opsB, jc);
             step(opsB, opsA, jc + 1);
         }
         if (jc < jend) step(opsA, opsB, jc);
+        // the last chunk's P U0 (its P fragments are in the set of its parity)
+        if constexpr (!SO) {
+            if (jbeg < jend) {
+                const int64_t jl = jend - 1;
+                finish_o(((jl - jbeg) & 1) ? opsB.fP : opsA.fP, (int)(jl & 1));
+                store_o(chunk_start(jl), chunk_len(jl));
+            }
+        }
     }
 
-    if (sdst) {
+    else {
+        // ======================= prefetch wave: the record of the chunk three ahead into L2 (this slice's
+        // quarter of its 128-byte lines), so that the other waves' loads one chunk ahead find it there.
+        // Its loads are consumed two steps after they are made: memory requests complete in order, and
+        // the computing waves, which wait for their own loads every step, would otherwise wait for these.
+        constexpr int kLines = (int)((R::BYTES + 127) / 128);
+        uint32_t sink = 0;
+        auto touch = [&](int64_t jx, uint32_t (&r)[3]) {
+            const char* rec = record(jx);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int line = (i * 64 + lane) * 4 + (sl & 3);
+                r[i] = line < kLines ? *reinterpret_cast<const uint32_t*>(rec + line * 128) : 0u;
+            }
+        };
+        uint32_t rA[3] = {0u, 0u, 0u}, rB[3] = {0u, 0u, 0u};
+        auto pstep = [&](uint32_t (&r)[3], int64_t jc) {
+            sink |= r[0] | r[1] | r[2];
+            touch(min<int64_t>(jc + 3, jend - 1), r);
+            lds_barrier();  // (1)
+            lds_barrier();  // (2)
+        };
+        if (jbeg < jend) {
+            touch(min<int64_t>(jbeg + 1, jend - 1), rA);
+            touch(min<int64_t>(jbeg + 2, jend - 1), rB);
+        }
+        lds_barrier();
+        lds_barrier();
+        int64_t jc = jbeg;
+        for (; jc + 1 < jend; jc += 2) {
+            pstep(rA, jc);
+            pstep(rB, jc + 1);
+        }
+        if (jc < jend) pstep(rA, jc);
+        sink |= rA[0] | rA[1] | rA[2] | rB[0] | rB[1] | rB[2];
+        if (Dv == 7) sO[0] = (float)sink;  // keeps the loads (Dv is 64 or 128)
+    }
+
+    if (sdst && !prefetcher) {
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
