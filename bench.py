@@ -3,18 +3,34 @@
 Timed step: one kda_chunk_fwd call over the chunked-prefill batch B=4, H=16,
 T=8192, d_k=d_v=128 (bf16 q/k/v, fp32 gates, fp32 state and output), inputs
 and the workspace resident in HBM (the call launches the per-chunk preparation
-kernel and the state-chain kernel).  value = B*T tokens per step / seconds per step.
+kernel prep16_kernel and the state-chain kernel chain16_kernel).
+value = B*T tokens per step / seconds per step, over the K timed steps.
+
+Order of a default run: the calibration leg (plain HBM copy and matrix-core
+loops), the other workloads, the flushed-cache protocol on the timed batch,
+then the W warm-up and K timed steps.  The legs before the timed steps keep the
+GPU busy for several seconds, so the timed steps run at a settled clock.
 
 Also reported on the same JSON line:
-  roofline      the call's two kernels against HBM bandwidth (algorithmic bytes / time)
-  mfma          the same call's algorithmic FLOPs against the dense bf16 MFMA peak
+  roofline      the call against HBM bandwidth: algorithmic bytes / mean launch time
+                (events on the library's stream over the timed steps); bytes counted
+                as 1,540 per head-token (o at 2 bytes) plus the final state, with the
+                fp32-output byte count as a second, named figure; the flushed-cache
+                median and min (512 MB written before each of 20 launches)
+  mfma          the call's algorithmic FLOPs against the dense bf16 matrix-core peak,
+                beside the ceiling that the HBM roofline puts on that fraction
+  peaks         this GPU's plain-copy HBM rate and bf16 matrix-core rates, measured here
   fused         the single fused kernel (workspace NULL) on the same batch
   decode        single-token decode step, B=256, H=32, d=128: GB/s against HBM peak
-  varlen        packed varlen prefill, 32 sequences, H=16, d=128: tokens/s
-  cpu_baseline  the fp64 CPU oracle on the same chunked batch (rank 0 only)
+  varlen        packed varlen prefill, 32 sequences, H=16, d=128
+  prefill_1m    one million-token prefill, B=1, H=8, d=128
+  raw_gates     the timed batch with bf16 gate/beta logits and the fused prologue
+  backward      gradients of the timed batch
+  cpu_baseline  the fp64 CPU oracle on the same chunked batch
   parity        max|err|/RMS of the timed output against that oracle run
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+                       [--only {chunk,decode,varlen,prefill_1m,raw_gates,backward,peaks}]
 """
 import argparse
 import json
@@ -27,14 +43,16 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FLUSH_BYTES = 512 << 20         # written before each flushed-protocol launch (L2 + Infinity Cache are 256 MB)
 
 
-def chunk_alg_bytes(n_head_tokens, n_heads, Dk, Dv, in_bytes, with_s0, gate_bytes=4):
-    # q, k, v in the input type; g (Dk) and beta in the gate type (fp32 unless given); o fp32 (Dv);
-    # final state fp32 (+ initial state if given)
-    per_tok = (2 * Dk + Dv) * in_bytes + gate_bytes * (Dk + 1) + 4 * Dv
+def chunk_alg_bytes(n_head_tokens, n_heads, Dk, Dv, in_bytes, with_s0, gate_bytes=4, o_bytes=2):
+    """Bytes the method must move once: q, k, v in the input type; g (Dk) and beta in the gate type;
+    o (Dv, at o_bytes: 2 as the cost model counts it, 4 as the library writes it); the final state fp32
+    (and the initial state when given)."""
+    per_tok = (2 * Dk + Dv) * in_bytes + gate_bytes * (Dk + 1) + o_bytes * Dv
     return n_head_tokens * per_tok + n_heads * Dk * Dv * 4 * (2 if with_s0 else 1)
 
 
@@ -78,9 +96,11 @@ def measured_traffic(key):
     return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
 
-def time_launches(fn, steps, warmup, torch):
-    """Run fn warmup times, then `steps` times bracketed by synchronize; per-launch
-    durations from events on the current stream (the stream the library launches on)."""
+def time_launches(fn, steps, warmup, torch, flush=None):
+    """Run fn `warmup` times, then `steps` times bracketed by synchronize; per-launch durations from
+    events on the current stream (the stream the library launches on).  With `flush`, it runs before
+    each launch, outside the events.  Returns wall seconds of the timed loop and the mean, median and
+    min launch time in ms."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -88,29 +108,70 @@ def time_launches(fn, steps, warmup, torch):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in evs:
+        if flush is not None:
+            flush()
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in evs]
-    return wall, float(np.mean(per)), float(np.min(per))
+    per = np.array([a.elapsed_time(b) for a, b in evs])
+    return wall, float(per.mean()), float(np.median(per)), float(per.min())
+
+
+def cpu_threads():
+    """Threads for the CPU oracle: the CPUs this process may run on, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
+def measure_peaks(args, torch, kda):
+    """This GPU's achievable rates: a plain copy of 1 GiB (2 GiB moved), median of 10; the two bf16
+    matrix-core instructions on 8 workgroups of 4 waves per compute unit, median of 5."""
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def copy():
+        assert kda.calib_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, st) == 0
+
+    _, c_mean, c_med, c_min = time_launches(copy, 10, 3, torch)
+    out = {"copy": {"bytes_moved": 2 * nbytes, "median_ms": c_med, "min_ms": c_min,
+                    "GB_s": 2 * nbytes / (c_med * 1e-3) / 1e9, "kernel": "kda_calib_copy (16-byte non-temporal)"}}
+    del src, dst
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * n_cu
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for kind, name, flops in [(0, "v_mfma_f32_16x16x32_bf16", 16 * 16 * 32 * 2),
+                              (1, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16 * 2)]:
+        iters = 20000 if kind == 0 else 10000
+
+        def loop():
+            assert kda.calib_mfma_raw(buf.data_ptr(), blocks, iters, kind, st) == 0
+
+        _, m_mean, m_med, m_min = time_launches(loop, 5, 2, torch)
+        total = blocks * 4 * 4 * iters * flops
+        out[name] = {"median_ms": m_med, "TFLOP_s": total / (m_med * 1e-3) / 1e12,
+                     "frac_of_peak": total / (m_med * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    out["compute_units"] = n_cu
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU clock settles only after ~40 back-to-back calls (~25 ms of load); earlier calls run
-    # up to 14% slower, so the default warm-up covers that ramp
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the decode and varlen measurements")
-    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m", "raw_gates", "backward"],
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the calibration leg and the other workloads")
+    ap.add_argument("--only", choices=["chunk", "decode", "varlen", "prefill_1m", "raw_gates", "backward", "peaks"],
                     default=None,
                     help="time one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
+                    help="only run kda_calib_copy three times on MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single device.",
@@ -121,7 +182,7 @@ def main():
 
     import gated_delta_rule_65_amd as kda
     import kda_inputs
-    from tests.gpu_util import device_inputs, rel_err, to_dev
+    from kda_inputs.device import device_inputs, to_dev
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -129,30 +190,26 @@ def main():
     kda.load_library()
 
     if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        st = torch.cuda.current_stream().cuda_stream
         for _ in range(3):
-            dst.copy_(src)
+            assert kda.calib_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, st) == 0
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
         return
 
-    if args.only == "decode":
-        print(json.dumps({"decode": measure_decode(args, torch, kda, kda_inputs, to_dev)}))
+    solo = {"decode": lambda: measure_decode(args, torch, kda, kda_inputs, to_dev),
+            "varlen": lambda: measure_varlen(args, torch, kda, kda_inputs, device_inputs),
+            "prefill_1m": lambda: measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs),
+            "raw_gates": lambda: measure_raw_gates(args, torch, kda, kda_inputs, device_inputs),
+            "backward": lambda: measure_backward(args, torch, kda, kda_inputs, device_inputs),
+            "peaks": lambda: measure_peaks(args, torch, kda)}
+    if args.only in solo:
+        print(json.dumps({args.only: solo[args.only]()}))
         return
-    if args.only == "varlen":
-        print(json.dumps({"varlen": measure_varlen(args, torch, kda, kda_inputs, device_inputs)}))
-        return
-    if args.only == "prefill_1m":
-        print(json.dumps({"prefill_1m": measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)}))
-        return
-    if args.only == "backward":
-        print(json.dumps({"backward": measure_backward(args, torch, kda, kda_inputs, device_inputs)}))
-        return
-    if args.only == "raw_gates":
-        print(json.dumps({"raw_gates": measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)}))
-        return
+    extras = args.only is None and not args.no_extras
 
     # ------------------------------------------------ chunked prefill, B=4 H=16 T=8192 d=128 bf16
     name = "chunk_b4_h16_t8192_d128_bf16"
@@ -169,16 +226,55 @@ def main():
     def step_fused():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], fused=True)
 
-    wall, k_ms, k_min = time_launches(step, args.steps, args.warmup, torch)
-    ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
-    value = tokens * args.steps / wall
     n_ht = tokens * H
-    alg_bytes = chunk_alg_bytes(n_ht, B * H, Dk, Dv, 2, with_s0=False)
+    line_extras = {}
+    flushed = None
+    if extras:
+        line_extras["peaks"] = measure_peaks(args, torch, kda)
+        _, f_mean, f_med, f_min = time_launches(step_fused, 20, 3, torch)
+        line_extras["fused"] = {"kernel": "chunk_fwd_kernel<128,false>", "kernel_ms": f_mean,
+                                "kernel_ms_median": f_med, "kernel_ms_min": f_min,
+                                "tokens_per_s": tokens / (f_mean * 1e-3)}
+        line_extras["decode"] = solo["decode"]()
+        line_extras["varlen"] = solo["varlen"]()
+        line_extras["prefill_1m"] = solo["prefill_1m"]()
+        line_extras["raw_gates"] = solo["raw_gates"]()
+        line_extras["backward"] = solo["backward"]()
+        # the cost model's protocol: 512 MB written before each of 20 launches, median and min
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        _, fl_mean, fl_med, fl_min = time_launches(step, 20, 3, torch, flush=lambda: scratch.fill_(1.0))
+        flushed = {"median_ms": fl_med, "min_ms": fl_min, "flush_bytes": FLUSH_BYTES}
+        del scratch
+
+    wall, k_mean, k_med, k_min = time_launches(step, args.steps, args.warmup, torch)
+    ms_per_step = wall * 1e3 / args.steps
+    value = tokens * args.steps / wall
+    alg_bytes = chunk_alg_bytes(n_ht, B * H, Dk, Dv, 2, with_s0=False)            # o counted at 2 bytes
+    alg_bytes_o32 = chunk_alg_bytes(n_ht, B * H, Dk, Dv, 2, with_s0=False, o_bytes=4)
     alg_flops = chunk_alg_flops(n_ht, Dk, Dv)
-    gbs = alg_bytes / (k_ms * 1e-3) / 1e9
-    tflops = alg_flops / (k_ms * 1e-3) / 1e12
-    traffic = measured_traffic(name)
+    gbs = alg_bytes / (k_mean * 1e-3) / 1e9
+    tflops = alg_flops / (k_mean * 1e-3) / 1e12
+    # at the HBM roofline the call takes alg_bytes / peak; the matrix-core fraction cannot exceed
+    # what that time allows
+    mfma_ceiling = alg_flops / (alg_bytes / (HBM_PEAK_GBS * 1e9)) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+
+    roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                "kernel": "prep16_kernel<128,false> + chain16_kernel<128,false> (one kda_chunk_fwd call)",
+                "kernel_ms": k_mean, "kernel_ms_median": k_med, "kernel_ms_min": k_min,
+                "alg_bytes_per_launch": alg_bytes,
+                "alg_bytes_def": "1540 B per head-token (q,k,v bf16 768; g fp32 512; beta 4; o 256 at 2 B) "
+                                 "+ final state fp32",
+                "fp32_o": {"alg_bytes_per_launch": alg_bytes_o32,
+                           "achieved": alg_bytes_o32 / (k_mean * 1e-3) / 1e9,
+                           "frac": alg_bytes_o32 / (k_mean * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                "workspace_bytes": ws.numel()}
+    if flushed is not None:
+        flushed["frac_median"] = alg_bytes / (flushed["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        roofline["flushed"] = flushed
+    if "peaks" in line_extras:
+        roofline["frac_of_copy_rate"] = gbs / line_extras["peaks"]["copy"]["GB_s"]
 
     line = {
         "metric": "KDA fwd tokens/s (H=16,d=128,T=8192) + % MFMA peak; decode % HBM BW",
@@ -195,38 +291,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": B, "T": T, "H": H, "d_k": Dk, "d_v": Dv, "chunk": 64,
                    "qkv": "bf16", "gates": "fp32", "state": "fp32", "output": "fp32", "parallelism": "none"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prep_kernel<128,false,false,false,false> + chain_kernel<128,false,false,false,false>", "kernel_ms": k_ms,
-                     "kernel_ms_min": k_min, "alg_bytes_per_launch": alg_bytes,
-                     "workspace_bytes": ws.numel()},
+        "roofline": roofline,
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops},
+                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "alg_flops_per_launch": alg_flops,
+                 "ceiling_frac_at_hbm_roofline": mfma_ceiling},
     }
-    if args.only is None and not args.no_extras:
-        _, f_ms, f_min = time_launches(step_fused, max(10, args.steps // 2), args.warmup, torch)
-        line["fused"] = {"kernel": "chunk_fwd_kernel<128,false>", "kernel_ms": f_ms, "kernel_ms_min": f_min,
-                         "tokens_per_s": tokens / (f_ms * 1e-3),
-                         "achieved": alg_bytes / (f_ms * 1e-3) / 1e9, "unit": "GB/s"}
-
-    if args.only is None and not args.no_extras:
-        line["decode"] = measure_decode(args, torch, kda, kda_inputs, to_dev)
-        line["varlen"] = measure_varlen(args, torch, kda, kda_inputs, device_inputs)
-        line["prefill_1m"] = measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs)
-        line["raw_gates"] = measure_raw_gates(args, torch, kda, kda_inputs, device_inputs)
-        line["backward"] = measure_backward(args, torch, kda, kda_inputs, device_inputs)
+    line.update(line_extras)
 
     if args.only is None and not args.no_cpu_baseline:
         import oracle
+        nthreads = cpu_threads()
         t0 = time.perf_counter()
-        o_ref, s_ref = oracle.forward_inputs(inp)
+        o_ref, s_ref = oracle.forward_inputs(inp, nthreads=nthreads)
         dt = time.perf_counter() - t0
-        line["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-                                "kind": "oracle", "seconds": dt,
+        line["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s", "cores": nthreads,
+                                "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": dt,
                                 "sample": f"the whole timed batch ({B}x{T} tokens, {H} heads, all {Dv} columns), "
                                           "fp64 token-by-token recurrence"}
         o_gpu = out["o"].reshape(tokens, H, Dv).cpu().numpy()
-        line["parity"] = {"o_err": rel_err(o_gpu, o_ref), "s_err": rel_err(out["s"].cpu().numpy(), s_ref),
+        line["parity"] = {"o_err": oracle.rel_err(o_gpu, o_ref), "s_err": oracle.rel_err(out["s"].cpu().numpy(), s_ref),
                           "tol": 2e-2, "metric": "max|err|/RMS vs fp64 oracle"}
 
     print(json.dumps(line))
@@ -257,10 +340,10 @@ def measure_decode(args, torch, kda, kda_inputs, to_dev):
         assert rc == 0
         flip[0] = 1 - a
 
-    _, dk_ms, dk_min = time_launches(dstep, max(20, args.steps), args.warmup, torch)
+    _, dk_ms, dk_med, dk_min = time_launches(dstep, max(20, args.steps), args.warmup, torch)
     dbytes = decode_alg_bytes(Bd, Hd, 128, 128, 2)
     dgbs = dbytes / (dk_ms * 1e-3) / 1e9
-    return {"workload": name, "kernel_ms": dk_ms, "kernel_ms_min": dk_min, "achieved": dgbs,
+    return {"workload": name, "kernel_ms": dk_ms, "kernel_ms_median": dk_med, "kernel_ms_min": dk_min, "achieved": dgbs,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS, "alg_bytes_per_launch": dbytes,
             "tokens_per_s": Bd / (dk_ms * 1e-3), "traffic": measured_traffic(name)}
 
@@ -279,11 +362,12 @@ def measure_varlen(args, torch, kda, kda_inputs, device_inputs):
     def vstep():
         kda.varlen_fwd(vd["q"], vd["k"], vd["v"], vd["g"], vd["beta"], vd["cu_seqlens"], vd["s0"], workspace=ws)
 
-    _, vk_ms, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
+    _, vk_ms, vk_med, vk_min = time_launches(vstep, max(10, args.steps // 2), args.warmup, torch)
     vbytes = chunk_alg_bytes(vspec.total * vspec.H, vspec.n_seq * vspec.H, 128, 128, 2, with_s0=True)
     return {"workload": name, "tokens": vspec.total, "longest": max(vspec.lengths), "kernel_ms": vk_ms,
-            "kernel_ms_min": vk_min, "tokens_per_s": vspec.total / (vk_ms * 1e-3),
-            "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s", "alg_bytes_per_launch": vbytes}
+            "kernel_ms_median": vk_med, "kernel_ms_min": vk_min, "tokens_per_s": vspec.total / (vk_ms * 1e-3),
+            "achieved": vbytes / (vk_ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac": vbytes / (vk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": vbytes}
 
 
 def measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs):
@@ -298,9 +382,9 @@ def measure_prefill_1m(args, torch, kda, kda_inputs, device_inputs):
     def pstep():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws)
 
-    _, k_ms, k_min = time_launches(pstep, 5, max(1, args.warmup // 25), torch)
+    _, k_ms, k_med, k_min = time_launches(pstep, 5, max(1, args.warmup // 25), torch)
     alg = chunk_alg_bytes(B * T * H, B * H, Dk, Dv, 2, with_s0=False)
-    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_median": k_med, "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
             "workspace_bytes": ws.numel()}
@@ -322,9 +406,9 @@ def measure_raw_gates(args, torch, kda, kda_inputs, device_inputs):
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws, g_logit=True,
                       beta_logit=True, qk_l2norm=True)
 
-    _, k_ms, k_min = time_launches(rstep, max(10, args.steps // 2), args.warmup, torch)
+    _, k_ms, k_med, k_min = time_launches(rstep, max(10, args.steps // 2), args.warmup, torch)
     alg = chunk_alg_bytes(B * T * H, B * H, Dk, Dv, 2, with_s0=False, gate_bytes=2)
-    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+    return {"workload": name, "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_median": k_med, "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg}
 
@@ -343,11 +427,12 @@ def measure_backward(args, torch, kda, kda_inputs, device_inputs):
     def bstep():
         kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_o, d["s0"], None, workspace=ws)
 
-    _, k_ms, k_min = time_launches(bstep, max(5, args.steps // 5), max(2, args.warmup // 5), torch)
+    _, k_ms, k_med, k_min = time_launches(bstep, max(5, args.steps // 5), max(2, args.warmup // 5), torch)
     # reads q, k, v (bf16), g, beta, d_o (fp32); writes dq, dk, dv, dg, dbeta (fp32) and ds0
     n_ht = B * T * H
     alg = n_ht * ((2 * Dk + Dv) * 2 + 4 * Dk + 4 + 4 * Dv + 4 * (3 * Dk + Dv) + 4) + B * H * Dk * Dv * 4
-    return {"workload": name + "_backward", "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_min": k_min,
+    return {"workload": name + "_backward", "tokens": B * T, "kernel_ms": k_ms, "kernel_ms_median": k_med,
+            "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
             "workspace_bytes": ws.numel(), "arith": "fp32 accumulation; split-bf16 three-pass products in the state recompute and column sums, fp32 MFMA elsewhere"}

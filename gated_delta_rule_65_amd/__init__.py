@@ -27,7 +27,8 @@ import torch
 __all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_noalloc_raw", "varlen_fwd", "decode_step", "library_path", "load_library", "KDAError",
            "chunk_fwd_raw", "varlen_fwd_raw", "decode_step_raw", "chunk_workspace_bytes",
            "varlen_workspace_bytes", "DTYPE", "Prologue", "prologue", "chunk_bwd", "varlen_bwd", "chunk_bwd_raw",
-           "varlen_bwd_raw", "chunk_bwd_workspace_bytes", "varlen_bwd_workspace_bytes", "ChunkKDA"]
+           "varlen_bwd_raw", "chunk_bwd_workspace_bytes", "varlen_bwd_workspace_bytes", "ChunkKDA",
+           "calib_copy_raw", "calib_mfma_raw"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -96,6 +97,10 @@ def load_library():
     L.kda_chunk_bwd_workspace_bytes.restype = sz
     L.kda_varlen_bwd_workspace_bytes.argtypes = [i64, i64, ci, ci, ci, ci]
     L.kda_varlen_bwd_workspace_bytes.restype = sz
+    L.kda_calib_copy.argtypes = [vp, vp, sz, vp]
+    L.kda_calib_copy.restype = ci
+    L.kda_calib_mfma.argtypes = [vp, ci, i64, ci, vp]
+    L.kda_calib_mfma.restype = ci
     L.kda_last_error.restype = ctypes.c_char_p
     L.kda_version.restype = ctypes.c_char_p
     _lib = L
@@ -124,6 +129,16 @@ def varlen_fwd_raw(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, ch
                    workspace_bytes, stream) -> int:
     return load_library().kda_varlen_fwd(q, k, v, g, beta, cu, N, total, s0, o, s_final, H, Dk, Dv, chunk, dtype,
                                          prologue, workspace, workspace_bytes, stream)
+
+
+def calib_copy_raw(src, dst, nbytes, stream) -> int:
+    """kda_calib_copy: a plain device copy of nbytes (the achievable HBM rate)."""
+    return load_library().kda_calib_copy(src, dst, nbytes, stream)
+
+
+def calib_mfma_raw(out, blocks, iters, kind, stream) -> int:
+    """kda_calib_mfma: a dense bf16 matrix-core loop (kind 0: 16x16x32, kind 1: 32x32x16)."""
+    return load_library().kda_calib_mfma(out, blocks, iters, kind, stream)
 
 
 def _dtype_code(dtype) -> int:

@@ -74,6 +74,34 @@ __device__ __forceinline__ f16x8_t gld_h8(const char* grp, int lane) {
 }
 __device__ __forceinline__ f16x8_t lds_h8(const _Float16* p) { return *reinterpret_cast<const f16x8_t*>(p); }
 
+// Range of the fp16 state and values.  The recurrence is linear in (V, S0) jointly, so the chain may
+// run on V 2^-e and S 2^-e and scale o and the final state back by 2^e.  Each chunk's e is the
+// smallest e >= 0 that keeps below 2^6 the max|v| of that chunk and of the one before it, and below
+// 2^10 the state's max as last measured (after the chunk before the previous one); e falls again
+// when the magnitudes do, so that values after a decayed spike do not sink into fp16's subnormals.
+// Inputs in the usual range keep e = 0 and are computed exactly as without it.
+// range_exp(m, lg, off) is the smallest e >= 0 with m 2^(off - e) < 2^lg, capped at 100.
+constexpr int kMaxRangeExp = 100;
+__device__ __forceinline__ int range_exp(float m, int lg, int off = 0) {
+    const int bexp = (int)((__float_as_uint(m) >> 23) & 0xff);  // m < 2^(bexp - 126)
+    return min(max(bexp - 126 - lg + off, 0), kMaxRangeExp);
+}
+__device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }  // 2^e, |e| <= 126
+// Maximum over the wave of x >= 0 (compared as bit patterns): row reductions with DPP row shifts (lanes
+// shifted in from outside the row read 0), then the four row results.
+__device__ __forceinline__ float wave_max(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x111, 0xf, 0xf, true));  // row_shr:1
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x112, 0xf, 0xf, true));  // row_shr:2
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x114, 0xf, 0xf, true));  // row_shr:4
+    u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x118, 0xf, 0xf, true));  // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)u, 63);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 // Row blocks of N and P are lower triangular: row block w meets 32-wide token steps kb < steps_of(w);
 // the six (w, kb) pairs are stored in order.
 __host__ __device__ constexpr int steps_of(int w) { return w >= 2 ? 2 : 1; }
@@ -573,9 +601,10 @@ struct Chain16Lds {
     static constexpr int S = 0;                             // fp16 S^T [2 bufs][32 cols][SST]
     static constexpr int U = S + 2 * kS * SST * 2;          // fp16 U^T [32][TST]
     static constexpr int U0 = U + kS * TST * 2;             // fp16 U0^T [2 bufs][hi, lo][32][TST]
-    static constexpr int V = U0 + 2 * 2 * kS * TST * 2;     // fp16 V^T [32][TST]
+    static constexpr int V = U0 + 2 * 2 * kS * TST * 2;     // bf16 V^T [32][TST] (as loaded, scaled when read)
     static constexpr int O = V + kS * TST * 2;              // fp32 output rows [64][kS + 4] on their way to HBM
-    static constexpr int TOTAL = O + 64 * (kS + 4) * 4;
+    static constexpr int MX = O + 64 * (kS + 4) * 4;  // fp32 maxima: [12] s0 and V, [2][4] V, [2][8] state
+    static constexpr int TOTAL = MX + 36 * 4;
 };
 
 // Operands of one chunk.  A state wave (row block rb) holds -W rows of rb and the Kbar^T rows and
@@ -614,7 +643,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
     _Float16* sS = reinterpret_cast<_Float16*>(smem + L::S);
     _Float16* sU = reinterpret_cast<_Float16*>(smem + L::U);
     _Float16* sU0 = reinterpret_cast<_Float16*>(smem + L::U0);
-    _Float16* sV = reinterpret_cast<_Float16*>(smem + L::V);
+    uint16_t* sV = reinterpret_cast<uint16_t*>(smem + L::V);
+    float* sMx = reinterpret_cast<float*>(smem + L::MX);
     float* sO = reinterpret_cast<float*>(smem + L::O);
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
@@ -690,7 +720,40 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             *reinterpret_cast<f16x4_t*>(sS + (buf * kS + 16 * nbt(i) + m) * L::SST + spos) = x;
         }
     };
-    if (!prefetcher) store_state(jbeg & 1);
+    int e = 0;  // range exponent of the current chunk (uniform over the workgroup)
+    if (!prefetcher) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, fabsf(accS[i][jj]));
+        mx = wave_max(mx);
+        if (lane == 0) sMx[w] = mx;
+    }
+    // Maxima in LDS: sMx[0..7] the initial state's per wave; V of chunk x at 12 + 4 ((x + 1) & 1), per
+    // row block; the state after chunk x (in the units of chunk x + 1) at 20 + 8 (x & 1), per wave.
+    const int vslot0 = 12 + 4 * (int)((jbeg + 1) & 1);
+    // after the first barrier: the range of the first chunk from the initial state and its V; the
+    // state's fp16 copy in those units and its maximum there (as the state "after chunk jbeg - 1")
+    auto first_range = [&]() {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, sMx[i]);
+        e = range_exp(mx, 10);
+        mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sMx[vslot0 + i]);
+        e = max(e, range_exp(mx, 6));
+        if (!prefetcher) {
+            const float sc = pow2i(-e);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) accS[i][jj] *= sc;
+            store_state(jbeg & 1);
+            if (lane == 0) sMx[20 + 8 * (int)((jbeg + 1) & 1) + w] = sc * sMx[w];
+        }
+    };
 
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
@@ -699,8 +762,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
     auto chunk_len = [&](int64_t jc) { return (int)min<int64_t>(kC, end - chunk_start(jc)); };
     auto next_chunk = [&](int64_t jc) { return jc + 1 < jend ? jc + 1 : jc; };
 
-    // S' = Diag(gamma_C) S + Kbar^T U on this wave's tiles, from U^T in LDS; then its fp16 copy
-    auto update_state = [&](const f16x8_t (&fKB)[2], float4 gC, int buf) {
+    // S' = Diag(gamma_C) S + Kbar^T U of chunk jc on this wave's tiles, from U^T in LDS; then, in the
+    // units of the next chunk (range exponent en), its fp16 copy and its maximum
+    auto update_state = [&](const f16x8_t (&fKB)[2], float4 gC, int buf, int en, int64_t jc) {
         const float gcv[4] = {gC.x, gC.y, gC.z, gC.w};
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -710,7 +774,32 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             for (int kb = 0; kb < 2; ++kb)
                 accS[i] = mma16(accS[i], fKB[kb], lds_h8(sU + (16 * nbt(i) + m) * L::TST + 32 * kb + 8 * cg));
         }
+        if (en != e) {
+            const float sc = pow2i(e - en);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) accS[i][jj] *= sc;
+        }
         store_state(buf);
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, fabsf(accS[i][jj]));
+        mx = wave_max(mx);
+        if (lane == 0) sMx[20 + 8 * (int)(jc & 1) + w] = mx;
+    };
+    // range exponent of the chunk after jc, in step jc after its first barrier: from the V maxima of
+    // chunks jc + 1 (posted in step jc) and jc, and the state maximum after chunk jc - 1 (in units e)
+    auto next_range = [&](int64_t jc) {
+        const float* ms = sMx + 20 + 8 * (int)((jc + 1) & 1);
+        float mv = 0.f, mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mv = fmaxf(mv, sMx[12 + i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ms[i]);
+        return max(range_exp(mv, 6), range_exp(mx, 10, e));
     };
     auto load_kb = [&](f16x8_t (&fKB)[2], float4& gC, const char* rec) {
 #pragma unroll
@@ -748,23 +837,39 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             const uint32_t rvo = (uint32_t)min(vrow, chunk_len(jx) - 1) * rs_v;
             raw = *reinterpret_cast<const uint4*>(v_l + chunk_start(jx) * (int64_t)rs_v + rvo);
         };
-        auto stage_v = [&](uint4 raw) {
+        // V of a chunk to LDS as loaded (bf16, transposed); its largest |value| over this wave's rows
+        // posted to sMx[slot]
+        auto stage_v = [&](uint4 raw, int slot) {
             const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+            float mx = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sV[(vpiece * 8 + 2 * i) * L::TST + vrow] = (_Float16)(vscale * __uint_as_float(u[i] << 16));
-                sV[(vpiece * 8 + 2 * i + 1) * L::TST + vrow] = (_Float16)(vscale * __uint_as_float(u[i] & 0xffff0000u));
+                sV[(vpiece * 8 + 2 * i) * L::TST + vrow] = (uint16_t)(u[i] & 0xffffu);
+                sV[(vpiece * 8 + 2 * i + 1) * L::TST + vrow] = (uint16_t)(u[i] >> 16);
+                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(u[i] << 16)), fabsf(__uint_as_float(u[i] & 0xffff0000u))));
             }
+            mx = wave_max(vscale * mx);
+            if (lane == 0) sMx[slot] = mx;
         };
         f32x4_t accU0[2];
-        auto form_u0 = [&](const f16x8_t (&fN)[2][2], int buf) {
+        // U0 = N V (two passes: N hi, N lo) for rows rb, V in the units of range exponent ev: into accU0
+        // and, split, into U0^T buffer buf
+        auto form_u0 = [&](const f16x8_t (&fN)[2][2], int buf, int ev) {
+            const float sc = vscale * pow2i(-ev);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     if (kb >= nk) continue;
-                    const f16x8_t bv = lds_h8(sV + (16 * nb + m) * L::TST + 32 * kb + 8 * cg);
+                    const uint4 raw = *reinterpret_cast<const uint4*>(sV + (16 * nb + m) * L::TST + 32 * kb + 8 * cg);
+                    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+                    f16x8_t bv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bv[2 * i] = (_Float16)(sc * __uint_as_float(u[i] << 16));
+                        bv[2 * i + 1] = (_Float16)(sc * __uint_as_float(u[i] & 0xffff0000u));
+                    }
                     acc = mma16(acc, fN[kb][0], bv);
                     acc = mma16(acc, fN[kb][1], bv);
                 }
@@ -807,15 +912,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
                 for (int jj = 0; jj < 4; ++jj) x[jj] = (_Float16)accU[nb][jj];
                 *reinterpret_cast<f16x4_t*>(sU + (16 * nb + m) * L::TST + 16 * rb + 4 * cg) = x;
             }
-            stage_v(vcur);
+            stage_v(vcur, 12 + 4 * b + rb);  // V of chunk jc + 1
             load_w(nxt, recn);  // after the products that read this chunk's copy
             lds_barrier();  // (1)
 
-            // ---- phase 2:  state tiles;  U0 of the next chunk
-            update_state(cur.fKB, cur.gC, b ^ 1);
+            // ---- phase 2:  state tiles;  U0 of the next chunk (both in the next chunk's units)
+            const int en = next_range(jc);
+            update_state(cur.fKB, cur.gC, b ^ 1, en, jc);
             load_kb(nxt.fKB, nxt.gC, recn);
-            form_u0(cur.fN, b ^ 1);
+            form_u0(cur.fN, b ^ 1, en);
             load_n(nxt, next_chunk(jn));  // after the products that read this copy of N
+            e = en;
             lds_barrier();  // (2)
         };
         Ops opsA, opsB;
@@ -824,11 +931,14 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
         if (jbeg < jend) {
             load_n(opsB, jbeg);
             load_v(opsB.vraw, jbeg);
-            stage_v(opsB.vraw);
+            stage_v(opsB.vraw, vslot0 + rb);
+        } else if (lane == 0) {
+            sMx[vslot0 + rb] = 0.f;
         }
         lds_barrier();
+        first_range();
         if (jbeg < jend) {
-            form_u0(opsB.fN, (int)(jbeg & 1));
+            form_u0(opsB.fN, (int)(jbeg & 1), e);
             const char* rec = record(jbeg);
             load_w(opsA, rec);
             load_kb(opsA.fKB, opsA.gC, rec);
@@ -891,15 +1001,19 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
                 ost[half] = *reinterpret_cast<const float4*>(&sO[(16 * rb + 8 * half + (lane >> 3)) * (kS + 4) +
                                                                    (lane & 7) * 4]);
         };
-        auto store_o = [&](int64_t tc, int ntc) {
+        // o rows of the chunk with range exponent eo, back in the units of the inputs
+        auto store_o = [&](int64_t tc, int ntc, int eo) {
+            const float sc = pow2i(eo);
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int rr = 16 * rb + 8 * half + (lane >> 3);
                 if (rr < ntc)  // o is not read again by this call: streamed past the caches
-                    __builtin_nontemporal_store(f32x4_t{ost[half].x, ost[half].y, ost[half].z, ost[half].w},
-                                                reinterpret_cast<f32x4_t*>(o_l + (tc + rr) * (int64_t)rs_o));
+                    __builtin_nontemporal_store(
+                        f32x4_t{sc * ost[half].x, sc * ost[half].y, sc * ost[half].z, sc * ost[half].w},
+                        reinterpret_cast<f32x4_t*>(o_l + (tc + rr) * (int64_t)rs_o));
             }
         };
+        int eprev = 0;  // range exponent of the previous chunk
         auto step = [&](Ops& cur, Ops& nxt, int64_t jc) {
             const int64_t jn = next_chunk(jc);
             const char* recn = record(jn);
@@ -910,12 +1024,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             if constexpr (!SO) {
                 if (jc > jbeg) finish_o(nxt.fP, b ^ 1);
                 load_p(nxt, recn);  // after the products that read the previous chunk's copy
-                if (jc > jbeg) store_o(chunk_start(jc - 1), kC);
+                if (jc > jbeg) store_o(chunk_start(jc - 1), kC, eprev);
             }
             lds_barrier();  // (1)
 
             // ---- phase 2:  state tiles;  Qh S of this chunk
-            update_state(cur.fKB, cur.gC, b ^ 1);
+            const int en = next_range(jc);
+            update_state(cur.fKB, cur.gC, b ^ 1, en, jc);
             load_kb(nxt.fKB, nxt.gC, recn);
             if constexpr (!SO) {
                 accO[0] = accO[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -925,6 +1040,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
                     for (int nb = 0; nb < 2; ++nb) accO[nb] = mma16(accO[nb], cur.fQ[s], s_frag(b, s, nb));
                 load_q(nxt, recn);
             }
+            eprev = e;
+            e = en;
             lds_barrier();  // (2)
         };
         Ops opsA, opsB;
@@ -935,6 +1052,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             load_kb(opsA.fKB, opsA.gC, rec);
         }
         lds_barrier();  // (the state waves' V of the first chunk)
+        first_range();
         lds_barrier();  // (their U0 of the first chunk)
         int64_t jc = jbeg;
         for (; jc + 1 < jend; jc += 2) {
@@ -947,7 +1065,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
             if (jbeg < jend) {
                 const int64_t jl = jend - 1;
                 finish_o(((jl - jbeg) & 1) ? opsB.fP : opsA.fP, (int)(jl & 1));
-                store_o(chunk_start(jl), chunk_len(jl));
+                store_o(chunk_start(jl), chunk_len(jl), eprev);
             }
         }
     }
@@ -991,11 +1109,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
     }
 
     if (sdst && !prefetcher) {
+        const float sc = pow2i(e);
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                sdst[(16 * cbw + 4 * cg + jj) * (int64_t)ld_dst + col_dst + 16 * nbt(i) + m] = accS[i][jj];
+                sdst[(16 * cbw + 4 * cg + jj) * (int64_t)ld_dst + col_dst + 16 * nbt(i) + m] = sc * accS[i][jj];
     }
 }
 

@@ -10,21 +10,37 @@ import gated_delta_rule_65_amd as kda
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 FAKE = 1 << 20  # 16-byte aligned stand-in address; never dereferenced because validation fails first
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for n in ["kda_chunk_fwd", "kda_varlen_fwd", "kda_decode_step", "kda_last_error", "kda_version",
               "kda_chunk_workspace_bytes", "kda_varlen_workspace_bytes", "kda_chunk_fwd_noalloc"]:
         assert n in names
+    assert {"kda_calib_copy", "kda_calib_mfma"} <= set(declared_functions())
+
+
+@pytest.mark.parametrize("args", [(None, FAKE, 1 << 20), (FAKE, None, 1 << 20), (FAKE + 4, FAKE, 1 << 20),
+                                  (FAKE, FAKE + 8, 1 << 20), (FAKE, FAKE, 100)])
+def test_calib_copy_validation(args):
+    assert kda.calib_copy_raw(*args, None) == 2
+
+
+@pytest.mark.parametrize("args", [(None, 1, 1, 0), (FAKE, 0, 1, 0), (FAKE, 1, 0, 0), (FAKE, 1, 1, 2)])
+def test_calib_mfma_validation(args):
+    assert kda.calib_mfma_raw(*args, None) == 2
 
 
 def test_library_exports_every_declared_symbol():

@@ -135,6 +135,76 @@ def test_gates_beyond_the_clamp_bounds(fused):
     check(inp, o, s)
 
 
+def scale_bf16(bits, factor):
+    """bf16 bit patterns times a power of two (exact)."""
+    return kda_inputs.f32_to_bf16_bits(kda_inputs.bf16_bits_to_f32(bits) * np.float32(factor))
+
+
+def check_rows(o_gpu, o_ref, rows, tol, what):
+    e = rel_err(o_gpu[rows], o_ref[rows])
+    print(f"  {what}: o err {e:.3e}", flush=True)
+    assert e <= tol, (what, e)
+
+
+@PATHS
+def test_values_beyond_half_precision_range(fused):
+    """Values up to about 2^18 and an initial state up to about 2^14 (half precision ends at 65504):
+    the bf16 bar holds on the output and the final state."""
+    spec = kda_inputs.Spec([640] * 2, 2, 128, 128, "bf16", "softplus_bounds", 0.05, s0_std=0.02, seed=43,
+                           name="wide-range")
+    inp = kda_inputs.generate(spec)
+    inp.v = scale_bf16(inp.v, 2.0 ** 16)
+    inp.s0 = (inp.s0 * np.float32(2.0 ** 16)).astype(np.float32)
+    o, s = run_chunk(inp, fused=fused)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    check(inp, o, s)
+
+
+@PATHS
+def test_value_spike(fused):
+    """One chunk of values 2^20 larger than the rest in the middle of each sequence.  Everything but the
+    chunk after it keeps the bf16 bar: the rows before the spike, the rows from the second chunk after
+    it on (each against its own scale), the whole output and the final state.  The chunk right after
+    the spike holds the spike's decay over six orders of magnitude within one chunk; it is only
+    required to be finite."""
+    spec = kda_inputs.Spec([640] * 2, 2, 128, 128, "bf16", "softplus_bounds", 0.05, s0_std=0.02, seed=43,
+                           name="value-spike")
+    inp = kda_inputs.generate(spec)
+    inp.v = scale_bf16(inp.v, 2.0 ** 12)
+    v = inp.v.reshape(2, 640, 2, 128)
+    v[:, 320:384] = scale_bf16(v[:, 320:384], 2.0 ** 20)
+    o, s = run_chunk(inp, fused=fused)
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    tol = TOL["bf16"]
+    check(inp, o, s)
+    o_ref, _ = reference(inp)
+    ob, rb = o.reshape(2, 640, 2, 128), o_ref.reshape(2, 640, 2, 128)
+    check_rows(ob, rb, np.s_[:, :320], tol, "before the spike")
+    for c in range(7, 10):
+        check_rows(ob, rb, np.s_[:, 64 * c:64 * (c + 1)], tol, f"chunk {c}")
+
+
+@PATHS
+def test_state_growing_past_value_range(fused):
+    """Keys of 2^-5 on two coordinates with beta = 1, no decay and v = 60 everywhere drive those state
+    rows toward 60 / 2^-5 = 1920 (thirty times the largest value), so the state alone sets the
+    working range part way through the sequence."""
+    T, H, D = 4096, 2, 128
+    spec = kda_inputs.Spec([T], H, D, D, "bf16", "softplus", seed=44, name="state-growth")
+    inp = kda_inputs.generate(spec)
+    k = np.zeros((T, H, D), np.float32)
+    t = np.arange(T)
+    k[t, :, (t % 2) * 37] = 2.0 ** -5
+    inp.k = kda_inputs.f32_to_bf16_bits(k)
+    inp.v = kda_inputs.f32_to_bf16_bits(np.full((T, H, D), 60.0, np.float32))
+    inp.g[:] = 0.0
+    inp.beta[:] = 1.0
+    o, s = run_chunk(inp, fused=fused)
+    _, s_ref = reference(inp)
+    assert np.abs(s_ref).max() > 1024.0  # the state outgrows 2^10 while |v| < 2^6
+    check(inp, o, s)
+
+
 @PATHS
 def test_long_memory_gate(fused):
     spec = kda_inputs.Spec([2048], 4, 128, 128, "bf16", "longmem", seed=4, name="longmem-2048")
