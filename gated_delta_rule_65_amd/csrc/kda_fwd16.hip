@@ -1071,10 +1071,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
     }
 
     else {
-        // ======================= prefetch wave: the record of the chunk three ahead into L2 (this slice's
-        // quarter of its 128-byte lines), so that the other waves' loads one chunk ahead find it there.
-        // Its loads are consumed two steps after they are made: memory requests complete in order, and
-        // the computing waves, which wait for their own loads every step, would otherwise wait for these.
+        // ======================= prefetch wave: at the start of each step, this slice's quarter of the
+        // 128-byte lines of the next chunk's record into L2, ahead of the other waves' loads of it, which
+        // are spread over the step.  One chunk ahead and no further: the four slices of a sequence-head
+        // share each record through L2, and a longer distance makes the lines in flight on an XCD
+        // outgrow its L2, so that records are fetched from HBM more than once.  Its loads are consumed
+        // two steps after they are made: memory requests complete in order, and the computing waves,
+        // which wait for their own loads every step, would otherwise wait for these.
         constexpr int kLines = (int)((R::BYTES + 127) / 128);
         uint32_t sink = 0;
         auto touch = [&](int64_t jx, uint32_t (&r)[3]) {
@@ -1088,14 +1091,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
         uint32_t rA[3] = {0u, 0u, 0u}, rB[3] = {0u, 0u, 0u};
         auto pstep = [&](uint32_t (&r)[3], int64_t jc) {
             sink |= r[0] | r[1] | r[2];
-            touch(min<int64_t>(jc + 3, jend - 1), r);
+            touch(min<int64_t>(jc + 1, jend - 1), r);
             lds_barrier();  // (1)
             lds_barrier();  // (2)
         };
-        if (jbeg < jend) {
-            touch(min<int64_t>(jbeg + 1, jend - 1), rA);
-            touch(min<int64_t>(jbeg + 2, jend - 1), rB);
-        }
         lds_barrier();
         lds_barrier();
         int64_t jc = jbeg;
