@@ -22,12 +22,13 @@
 //
 // Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) (fp32) and the state at every chunk start come
 // from the forward pass's prep kernel in its backward form and its chain kernel in mode 3, on split-bf16
-// records with every product in three passes (launch_chunk_states).  Then three kernels, fp32
-// accumulation (the column sums as three-pass split-bf16 products, the others on fp32 MFMA):
+// records with every product in three passes (launch_chunk_states).  Then two kernels, fp32
+// accumulation (the reverse chain and the column sums as three-pass split-bf16 products, the rest of the
+// gradient kernel on fp32 MFMA):
 //   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS', dU, dX of every
 //                      chunk, dv = dX, ds0
-//   bwd_colsum_kernel  per (chunk, head): the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma)
-//   bwd_grad_b_kernel  per (chunk, head): through the inverse, the decayed Gram blocks and the gates
+//   bwd_grad_kernel    per (chunk, head): the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma),
+//                      kept in LDS, then through the inverse, the decayed Gram blocks and the gates
 #include <type_traits>
 
 #include "kda_device.h"
@@ -42,13 +43,6 @@ constexpr int kBS = 32;  // state columns per chain workgroup
 
 template <int DK>
 using BRec = BwdRec<DK>;
-// Per (chunk, head) output of bwd_colsum (float offsets).
-template <int DK>
-struct GRec {
-    static constexpr int DQT = 0, DKT = 64 * DK, DKB = 128 * DK, DP = 192 * DK, DN = DP + 4096, DGM = DN + 4096,
-                         FLOATS = DGM + DK;
-    static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
-};
 
 struct BSeq {
     int64_t start, end;
@@ -252,7 +246,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
             for (int s = s0u; s < 2; ++s)
                 accU = mma_full(accU, lds_frag<F32, 64, 64>(pPT, 16 * rb + m, 32 * s + 8 * cg),
                                 lds_frag<F32, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
-#pragma unroll
+#pragma unroll 1  // (unrolled, the fragments of several steps are read ahead and registers spill)
             for (int s = 0; s < DK / 32; ++s)
                 accU = mma_full(accU, lds_frag<F32, 64, DK>(pKB, 16 * rb + m, 32 * s + 8 * cg),
                                 lds_frag<F32, kBS, DK>(pDS, 16 * nb + m, 32 * s + 8 * cg));
@@ -297,10 +291,11 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
         }
         __syncthreads();
     }
-    if (ds0 && swave)
+    if (ds0 && swave) {
+        float* d0 = ds0 + (n * H + h) * (int64_t)DK * Dv + col0;  // uniform base, small per-lane offsets
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            ds0[((n * H + h) * DK + 16 * cb + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nb + m] = dS[jj];
+        for (int jj = 0; jj < 4; ++jj) d0[(16 * cb + 4 * cg + jj) * Dv + 16 * nb + m] = dS[jj];
+    }
 }
 
 // ============================================================================ sums over the value columns
@@ -316,150 +311,146 @@ __device__ __forceinline__ Frag<false> frag_rows(const float* base, int64_t ld, 
     return f;
 }
 
-// Per (chunk, head): the products summed over the value columns, all contracting over the stored
+// Per (chunk, head), the products summed over the value columns, all contracting over the stored
 // column index of row-major operands:
 //   dQt = dO S^T, dKt = -dX S^T, dKb = U dS'^T (64 x DK);  dP = dO U^T, dN = dU X^T (64 x 64);
-//   dgamma = rowsum(S o dS').  Split-bf16 three-pass products; wave w owns rows 16w..16w+15.
-// Per 32-column step the operands every wave needs (S and dS' rows, U and X rows) are read from
-// memory once per workgroup, split once and staged in LDS; the next step's pieces are requested
-// while the current step's products run.  A wave's own rows (dO, dX, U, dU) come straight from memory.
+//   dgamma = rowsum(S o dS').
+// Split-bf16 three-pass products on the gradient kernel's 16 waves: the four waves of row block rb
+// (w & 3) take dQt, dKt, dKb, and dP with dN respectively (w >> 2).  Per 32-column step the operands
+// every wave needs (S and dS' rows, U and X rows) are read from memory once per workgroup, split once
+// and staged in LDS (S over sq, dS' over sk, U over sG, X over sM2: none of them holds anything yet);
+// the next step's pieces are requested while the current step's products run.  A wave's own rows (dO,
+// dX, U, dU) come straight from memory.  The results land in LDS for the phases that follow: dQt in sq,
+// dKt in sk, dKb in sG (rows [64][LD]), dN in sM1 and dP in sM3 ([64][65]), dgamma in sGam.
 template <int DK>
-struct ColsumLds {
+__device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int64_t t0, int nt, int H, int h,
+                                              int Dv, const float* __restrict__ S, const float* __restrict__ dS,
+                                              const float* __restrict__ X, const float* __restrict__ dU,
+                                              float* sq, float* sk, float* sG, float* sM1, float* sM2, float* sM3,
+                                              float* sGam, int tid) {
     using MS = LMat<false, DK, 32>;  // S, dS' column step [c][n]
     using MR = LMat<false, 64, 32>;  // U, X column step [t][n]
-    static constexpr int S = 0, DS = S + MS::BYTES, U = DS + MS::BYTES, X = U + MR::BYTES, TOTAL = X + MR::BYTES;
-};
-
-template <int DK>
-__global__ __launch_bounds__(256, 2) void bwd_colsum_kernel(const float* __restrict__ d_o,
-                                                            const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                            int64_t total, int64_t N, int H, int Dv,
-                                                            const float* __restrict__ states,
-                                                            const float* __restrict__ dstates,
-                                                            const float* __restrict__ xu,
-                                                            const float* __restrict__ dudx,
-                                                            float* __restrict__ grads) {
-    using GR = GRec<DK>;
-    using L = ColsumLds<DK>;
+    constexpr int LD = DK + 4;
     constexpr int CB = DK / 16;
-    constexpr int PS = DK / 8;  // S / dS' values staged per thread per step (32 DK / 256)
-    __shared__ __align__(16) char smem[L::TOTAL];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
-    const int64_t slot = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
-    int64_t n, t0;
-    int nt;
-    if (!slot_chunk(cu, slot, T_fixed, total, N, n, t0, nt)) return;
-    const int64_t ch = slot * H + h;
-    const float* S = states + ch * DK * (int64_t)Dv;
-    const float* dS = dstates + ch * DK * (int64_t)Dv;
-    const float* X = xu + ch * 128 * (int64_t)Dv;
+    static_assert(MS::BYTES <= 64 * LD * 4 && MR::BYTES <= 64 * LD * 4 && MR::BYTES <= 64 * 65 * 4,
+                  "the column steps fit the areas they are staged in");
     const float* U = X + 64 * (int64_t)Dv;
-    const float* dU = dudx + ch * 128 * (int64_t)Dv;
     const float* dX = dU + 64 * (int64_t)Dv;
-    // dO rows of this wave: tokens past the end read the last token and count as zero
-    const int orow = 16 * w + m;
+    char* pS = reinterpret_cast<char*>(sq);
+    char* pD = reinterpret_cast<char*>(sk);
+    char* pU = reinterpret_cast<char*>(sG);
+    char* pX = reinterpret_cast<char*>(sM2);
+    const int w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
+    const int rb = w & 3, role = w >> 2;
+    // dO rows of row block rb: tokens past the end read the last token and count as zero
+    const int orow = 16 * rb + m;
     const float* dO = d_o + ((t0 + min(orow, nt - 1)) * H + h) * (int64_t)Dv;
     const float omask = orow < nt ? 1.f : 0.f;
-    // staging pieces: S and dS' rows sr (PS columns from sc), U and X rows ur (8 columns from uc)
-    const int sr = (tid * PS) / 32, sc = (tid * PS) % 32, ur = tid >> 2, uc = 8 * (tid & 3);
-    float vS[PS], vD[PS], vU[8], vX[8];
+    // staging pieces of four values: S and dS' row tid / 8 (threads below 8 DK), U (threads below 512) or
+    // X row (tid % 512) / 8; columns 4 (tid % 8)
+    const bool hasS = tid < 8 * DK;
+    const int srow = tid >> 3, scol = 4 * (tid & 7), urow = (tid & 511) >> 3;
+    const float* UX = tid < 512 ? U : X;
+    float4 vS = make_float4(0.f, 0.f, 0.f, 0.f), vD = vS, vR = vS;
     auto fetch = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < PS; j += 4) {
-            const float4 a = *reinterpret_cast<const float4*>(S + sr * (int64_t)Dv + k0 + sc + j);
-            const float4 b = *reinterpret_cast<const float4*>(dS + sr * (int64_t)Dv + k0 + sc + j);
-            vS[j] = a.x; vS[j + 1] = a.y; vS[j + 2] = a.z; vS[j + 3] = a.w;
-            vD[j] = b.x; vD[j + 1] = b.y; vD[j + 2] = b.z; vD[j + 3] = b.w;
+        if (hasS) {
+            vS = *reinterpret_cast<const float4*>(S + srow * (int64_t)Dv + k0 + scol);
+            vD = *reinterpret_cast<const float4*>(dS + srow * (int64_t)Dv + k0 + scol);
         }
-        load8_as_float(U + ur * (int64_t)Dv + k0 + uc, vU);
-        load8_as_float(X + ur * (int64_t)Dv + k0 + uc, vX);
+        vR = *reinterpret_cast<const float4*>(UX + urow * (int64_t)Dv + k0 + scol);
     };
-
-    f32x4_t aQ[CB], aK[CB], aB[CB], aP[4], aN[4];
+    // one set of accumulator tiles for every role: CB tiles of dQt, dKt or dKb, or dN (0..3) and dP (4..7)
+    constexpr int NACC = CB > 8 ? CB : 8;
+    f32x4_t acc[NACC];
 #pragma unroll
-    for (int i = 0; i < CB; ++i) aQ[i] = aK[i] = aB[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aP[i] = aN[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float dgam = 0.f;  // partial row sum of S o dS' for row sr
-
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float dgam = 0.f;
     fetch(0);
     for (int k0 = 0; k0 < Dv; k0 += 32) {
         __syncthreads();  // the previous step's fragments have been read
-#pragma unroll
-        for (int j = 0; j < PS; j += 8) {
-            lds_store8<false, DK, 32>(smem + L::S, sr, sc + j, vS + j);
-            lds_store8<false, DK, 32>(smem + L::DS, sr, sc + j, vD + j);
+        if (hasS) {
+            lds_store4<false, DK, 32>(pS, srow, scol, f32x4_t{vS.x, vS.y, vS.z, vS.w});
+            lds_store4<false, DK, 32>(pD, srow, scol, f32x4_t{vD.x, vD.y, vD.z, vD.w});
+            dgam = fmaf(vS.x, vD.x, fmaf(vS.y, vD.y, fmaf(vS.z, vD.z, fmaf(vS.w, vD.w, dgam))));
         }
-#pragma unroll
-        for (int j = 0; j < PS; ++j) dgam = fmaf(vS[j], vD[j], dgam);
-        lds_store8<false, 64, 32>(smem + L::U, ur, uc, vU);
-        lds_store8<false, 64, 32>(smem + L::X, ur, uc, vX);
+        lds_store4<false, 64, 32>(tid < 512 ? pU : pX, urow, scol, f32x4_t{vR.x, vR.y, vR.z, vR.w});
         __syncthreads();
         if (k0 + 32 < Dv) fetch(k0 + 32);
 
         float x[8];
-        load8_as_float(dO + k0 + 8 * cg, x);
+        if (role == 0 || role == 3) {
+            load8_as_float(dO + k0 + 8 * cg, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= omask;
-        Frag<false> fO;
-        fO.set(x);
-        const Frag<false> fX = frag_rows(dX, Dv, 16 * w, k0, m, cg, x);
-        const Frag<false> fU = frag_rows(U, Dv, 16 * w, k0, m, cg, x);
-        const Frag<false> fdU = frag_rows(dU, Dv, 16 * w, k0, m, cg, x);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const Frag<false> fS = lds_frag<false, DK, 32>(smem + L::S, 16 * cb + m, 8 * cg);
-            const Frag<false> fdS = lds_frag<false, DK, 32>(smem + L::DS, 16 * cb + m, 8 * cg);
-            aQ[cb] = mma_full(aQ[cb], fO, fS);
-            aK[cb] = mma_full(aK[cb], fX, fS);
-            aB[cb] = mma_full(aB[cb], fU, fdS);
-        }
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            aP[ib] = mma_full(aP[ib], fO, lds_frag<false, 64, 32>(smem + L::U, 16 * ib + m, 8 * cg));
-            aN[ib] = mma_full(aN[ib], fdU, lds_frag<false, 64, 32>(smem + L::X, 16 * ib + m, 8 * cg));
-        }
-    }
-    float* out = grads + ch * (int64_t)GR::FLOATS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * cg + i;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            st_nt(&out[GR::DQT + r * DK + 16 * cb + m], aQ[cb][i]);
-            st_nt(&out[GR::DKT + r * DK + 16 * cb + m], -aK[cb][i]);
-            st_nt(&out[GR::DKB + r * DK + 16 * cb + m], aB[cb][i]);
-        }
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            st_nt(&out[GR::DP + r * 64 + 16 * ib + m], aP[ib][i]);
-            st_nt(&out[GR::DN + r * 64 + 16 * ib + m], aN[ib][i]);
+            for (int j = 0; j < 8; ++j) x[j] *= omask;
+            Frag<false> fO;
+            fO.set(x);
+            // (loops unrolled by two: fully unrolled, every fragment is read ahead and registers spill)
+            if (role == 0) {
+#pragma unroll 2
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[cb] = mma_full(acc[cb], fO, lds_frag<false, DK, 32>(pS, 16 * cb + m, 8 * cg));
+            } else {
+#pragma unroll 2
+                for (int ib = 0; ib < 4; ++ib)
+                    acc[4 + ib] = mma_full(acc[4 + ib], fO, lds_frag<false, 64, 32>(pU, 16 * ib + m, 8 * cg));
+                const Frag<false> fdU = frag_rows(dU, Dv, 16 * rb, k0, m, cg, x);
+#pragma unroll 2
+                for (int ib = 0; ib < 4; ++ib)
+                    acc[ib] = mma_full(acc[ib], fdU, lds_frag<false, 64, 32>(pX, 16 * ib + m, 8 * cg));
+            }
+        } else {
+            const Frag<false> fr = frag_rows(role == 1 ? dX : U, Dv, 16 * rb, k0, m, cg, x);
+            const char* pB = role == 1 ? pS : pD;
+#pragma unroll 2
+            for (int cb = 0; cb < CB; ++cb) acc[cb] = mma_full(acc[cb], fr, lds_frag<false, DK, 32>(pB, 16 * cb + m, 8 * cg));
         }
     }
-    // dgamma: the 32 / PS threads of a row are adjacent
+    // dgamma: the eight threads of a row are adjacent lanes
+    dgam += __shfl_xor(dgam, 1);
+    dgam += __shfl_xor(dgam, 2);
+    dgam += __shfl_xor(dgam, 4);
+    __syncthreads();  // every staged operand has been read
+    if (hasS && (tid & 7) == 0) sGam[srow] = dgam;
 #pragma unroll
-    for (int off = 1; off < 32 / PS; off <<= 1) dgam += __shfl_xor(dgam, off);
-    if (sc == 0) st_nt(&out[GR::DGM + sr], dgam);
+    for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * rb + 4 * cg + jj;
+        if (role == 3) {
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                sM1[r * 65 + 16 * ib + m] = acc[ib][jj];      // dN
+                sM3[r * 65 + 16 * ib + m] = acc[4 + ib][jj];  // dP
+            }
+        } else {
+            float* dst = role == 0 ? sq : (role == 1 ? sk : sG);
+            const float sgn = role == 1 ? -1.f : 1.f;  // dKt = -dX S^T
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) dst[r * LD + 16 * cb + m] = sgn * acc[cb][jj];
+        }
+    }
+    __syncthreads();
 }
 
 // ============================================================================ to dq, dk, dg, db
 
-// Per (chunk, head), 1024 threads: through N = Minv Diag(b) and Minv = (I + Diag(b) Abar)^{-1} to db and
-// dAbar, then through the decayed Gram blocks Abar and P, Qt, Kt, Kb and gamma to dq, dk and dG, and
-// from G to dg.  Thread t owns row t/16 and channels (t%16)*DK/16 .. of the token-by-channel tensors.
+// Per (chunk, head), 1024 threads: first the sums over the value columns (colsum_to_lds), then through
+// N = Minv Diag(b) and Minv = (I + Diag(b) Abar)^{-1} to db and dAbar, then through the decayed Gram
+// blocks Abar and P, Qt, Kt, Kb and gamma to dq, dk and dG, and from G to dg.  Thread t owns row t/16
+// and channels (t%16)*DK/16 .. of the token-by-channel tensors.
 template <int DK, bool F32>
-__global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restrict__ qv,
-                                                             const void* __restrict__ kv,
-                                                             const float* __restrict__ g,
-                                                             const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                             int64_t total, int64_t N, int H,
-                                                             const float* __restrict__ recs,
-                                                             const float* __restrict__ grads,
-                                                             float* __restrict__ dq, float* __restrict__ dk,
-                                                             float* __restrict__ dg, float* __restrict__ dbeta) {
+__global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restrict__ qv,
+                                                           const void* __restrict__ kv,
+                                                           const float* __restrict__ g,
+                                                           const float* __restrict__ d_o,
+                                                           const int32_t* __restrict__ cu, int64_t T_fixed,
+                                                           int64_t total, int64_t N, int H, int Dv,
+                                                           const float* __restrict__ recs,
+                                                           const float* __restrict__ states,
+                                                           const float* __restrict__ dstates,
+                                                           const float* __restrict__ xu,
+                                                           const float* __restrict__ dudx,
+                                                           float* __restrict__ dq, float* __restrict__ dk,
+                                                           float* __restrict__ dg, float* __restrict__ dbeta) {
     using R = BRec<DK>;
-    using GR = GRec<DK>;
     constexpr int NT = 1024;
     constexpr int LD = DK + 4;
     constexpr int CPT = DK / 16;
@@ -472,27 +463,46 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     int64_t n, t0;
     int nt;
     if (!slot_chunk(cu, slot, T_fixed, total, N, n, t0, nt)) return;
-    const float* rec = recs + (slot * H + h) * (int64_t)R::FLOATS;
-    const float* gin = grads + (slot * H + h) * (int64_t)GR::FLOATS;
+    const int64_t ch = slot * H + h;
+    const float* rec = recs + ch * (int64_t)R::FLOATS;
 
-    // ---- every global operand of the chunk is requested up front (the phases below are short and
-    // would otherwise each wait out a full memory latency): four elements of each 64x64 block per
-    // thread, and one piece of eight q, k, g channels per thread (8 DK <= 1024 pieces)
+    // ---- the records' operands of the later phases are requested up front, to arrive while the
+    // column sums run: four elements of each 64x64 block per thread
     static_assert(4096 % NT == 0 && 8 * DK <= NT, "one piece per thread");
     constexpr int EPT = 4096 / NT;
-    // (in the order they are consumed: the first phase waits only for b, dN and Minv)
     const float vb = tid < 64 ? rec[R::BT + tid] : 0.f;
     float vN[EPT], vM[EPT], vA[EPT], vP[EPT];
 #pragma unroll
-    for (int a = 0; a < EPT; ++a) {
-        vN[a] = gin[GR::DN + tid + a * NT];
-        vM[a] = rec[R::MIT + tid + a * NT];
-    }
+    for (int a = 0; a < EPT; ++a) vM[a] = rec[R::MIT + tid + a * NT];
+#pragma unroll
+    for (int a = 0; a < EPT; ++a) vA[a] = rec[R::AB + tid + a * NT];
+    const float vgm = rec[R::GM + tid % DK];
+
+    // ---- the sums over the value columns, into LDS
+    colsum_to_lds<DK>(d_o, t0, nt, H, h, Dv, states + ch * DK * (int64_t)Dv, dstates + ch * DK * (int64_t)Dv,
+                      xu + ch * 128 * (int64_t)Dv, dudx + ch * 128 * (int64_t)Dv, sq, sk, sG, sM1, sM2, sM3, sFf,
+                      tid);
+    // this thread's pieces of them: dN and dP elements as in the loads above, dgamma of channel tid % DK,
+    // and its own elements of dQt, dKt, dKb (row tid / 16, channels (tid % 16) DK / 16 ..)
 #pragma unroll
     for (int a = 0; a < EPT; ++a) {
-        vA[a] = rec[R::AB + tid + a * NT];
-        vP[a] = gin[GR::DP + tid + a * NT];
+        const int e = tid + a * NT;
+        vN[a] = sM1[(e >> 6) * 65 + (e & 63)];
+        vP[a] = sM3[(e >> 6) * 65 + (e & 63)];
     }
+    const float vgd = vgm * sFf[tid % DK];  // gamma dgamma of channel tid % DK
+    float pQt[CPT], pKt[CPT], pKb[CPT];
+    {
+        const int e0 = (tid >> 4) * LD + CPT * (tid & 15);
+#pragma unroll
+        for (int b = 0; b < CPT; ++b) {
+            pQt[b] = sq[e0 + b];
+            pKt[b] = sk[e0 + b];
+            pKb[b] = sG[e0 + b];
+        }
+    }
+    __syncthreads();  // read before the phases below reuse these areas
+    // q, k and g: one piece of eight channels per thread (first needed a few phases below)
     const bool has8 = tid < 8 * DK;
     const int r8 = (8 * tid) / DK, c8 = (8 * tid) % DK;
     Raw8<F32> xq8, xk8;
@@ -509,7 +519,6 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
         zg[0] = *reinterpret_cast<const float4*>(g + idx);
         zg[1] = *reinterpret_cast<const float4*>(g + idx + 4);
     }
-    const float vgd = rec[R::GM + tid % DK] * gin[GR::DGM + tid % DK];  // gamma dgamma of channel tid % DK
 
     // ---- through N = Minv Diag(b) and Minv = M^{-1}
 #pragma unroll
@@ -672,18 +681,6 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_b_kernel(const void* __restr
     }
     __syncthreads();
 
-    // the column-sum gradients of this thread's own elements, loaded while the products below run
-    float pQt[CPT], pKt[CPT], pKb[CPT];
-#pragma unroll
-    for (int b = 0; b < CPT; b += 4) {
-        const float* base = gin + ar * DK + ac + b;
-        const float4 u = *reinterpret_cast<const float4*>(base + GR::DQT);
-        const float4 v4 = *reinterpret_cast<const float4*>(base + GR::DKT);
-        const float4 w4 = *reinterpret_cast<const float4*>(base + GR::DKB);
-        pQt[b] = u.x; pQt[b + 1] = u.y; pQt[b + 2] = u.z; pQt[b + 3] = u.w;
-        pKt[b] = v4.x; pKt[b + 1] = v4.y; pKt[b + 2] = v4.z; pKt[b + 3] = v4.w;
-        pKb[b] = w4.x; pKb[b + 1] = w4.y; pKb[b + 2] = w4.z; pKb[b + 3] = w4.w;
-    }
 
     // ---- the decayed Gram contractions on fp32 MFMA (16x16x4).  Wave wv owns the (row block R,
     // 16-channel block cb) pairs below and, for each, three 16x16 results at rows 16R.. and
@@ -855,11 +852,12 @@ int64_t bwd_slots(const BwdArgs& a) {
 }
 
 static int64_t bwd_rec_floats(int Dk) { return Dk == 128 ? BRec<128>::FLOATS : BRec<64>::FLOATS; }
-static int64_t bwd_grad_floats(int Dk) { return Dk == 128 ? GRec<128>::FLOATS : GRec<64>::FLOATS; }
+// the state recompute's fragment records, in floats (their bytes are a multiple of 256)
+static int64_t bwd_frag_floats(int Dk) { return chunk_states_record_bytes(Dk) / 4; }
 
-// [records][states][state gradients][column sums][X, U][dU, dX], each per (slot, head)
+// [records][states][state gradients][fragment records][X, U][dU, dX], each per (slot, head)
 int64_t bwd_workspace_bytes(const BwdArgs& a) {
-    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_grad_floats(a.Dk) + 4 * 64 * (int64_t)a.Dv;
+    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_frag_floats(a.Dk) + 4 * 64 * (int64_t)a.Dv;
     return bwd_slots(a) * a.H * per * 4;
 }
 
@@ -870,30 +868,27 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     float* recs = static_cast<float*>(ws);
     float* states = recs + ch * (int64_t)BRec<DK>::FLOATS;
     float* dstates = states + ch * (int64_t)DK * a.Dv;
-    float* grads = dstates + ch * (int64_t)DK * a.Dv;
-    float* xu = grads + ch * (int64_t)GRec<DK>::FLOATS;
+    float* frecs = dstates + ch * (int64_t)DK * a.Dv;
+    float* xu = frecs + ch * bwd_frag_floats(DK);
     float* dudx = xu + ch * 128 * (int64_t)a.Dv;
     const int64_t items = a.N * (int64_t)a.H;
     const int NS = a.Dv / kBS;
     const unsigned chain = (unsigned)(((items + 7) / 8) * 8 * NS);
     if (ch > 0) {
-        // the forward pass's preparation (fp32 records, plus the plain operands `recs`) and its
-        // state-only chain give the chunk-start states and X, U; the fragment records borrow the
-        // column-sum area, which bwd_colsum writes only later
+        // the forward pass's preparation (fragment records `frecs`, plus the plain operands `recs`)
+        // and its state-only chain give the chunk-start states and X, U
         const ChunkArgs fa{a.q, a.k, a.v, a.g, a.beta, a.s0, nullptr, nullptr, a.cu_seqlens, a.T_fixed, a.total,
                            a.N, a.H, a.Dk, a.Dv, a.f32, Prologue{false, false, false, false, false}};
-        if ((int64_t)GRec<DK>::FLOATS * 4 < chunk_states_record_bytes(DK)) return hipErrorInvalidValue;
-        const hipError_t e = launch_chunk_states(fa, grads, recs, states, xu, st);
+        const hipError_t e = launch_chunk_states(fa, frecs, recs, states, xu, st);
         if (e != hipSuccess) return e;
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK, true>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
+    hipLaunchKernelGGL((bwd_dstates_kernel<DK, false>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
                        a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, dudx, a.dv);
     if (ch > 0) {
-        hipLaunchKernelGGL((bwd_colsum_kernel<DK>), dim3((unsigned)ch), dim3(256), 0, st, a.d_o, a.cu_seqlens,
-                           a.T_fixed, a.total, a.N, a.H, a.Dv, states, dstates, xu, dudx, grads);
-        hipLaunchKernelGGL((bwd_grad_b_kernel<DK, F32>), dim3((unsigned)ch), dim3(1024), 0, st, a.q, a.k, a.g,
-                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, recs, grads, a.dq, a.dk, a.dg, a.dbeta);
+        hipLaunchKernelGGL((bwd_grad_kernel<DK, F32>), dim3((unsigned)ch), dim3(1024), 0, st, a.q, a.k, a.g, a.d_o,
+                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, states, dstates, xu, dudx, a.dq,
+                           a.dk, a.dg, a.dbeta);
     }
     return hipGetLastError();
 }

@@ -180,7 +180,9 @@ struct Prep16Lds {
     static constexpr int COL = 0;                          // fp32 Gram column operands, sub-blocks 0..2 [48][DK+4]
                                                            // (pi positions); later fp16 Kbar^T, then Kt^T [DK][72]
     static constexpr int PM = COL + COL_BYTES;             // fp32 P [64][68], later -P N (rows of block w by wave w)
-    static constexpr int A = PM + 64 * 68 * 4;             // fp32 b_r A_ri [64][68], later N
+    static constexpr int A = PM + 64 * 68 * 4;             // fp32 b_r A_ri [64][68], later N; before the
+                                                           // Gram results, row block 3's Gram operands
+    static_assert(DK / 32 * 3 * 64 * 16 <= 64 * 68 * 4, "row block 3's Gram operands fit over A");
     static constexpr int D = A + 64 * 68 * 4;              // fp32 diagonal inverses [4][16][17]
     static constexpr int TAB = D + 4 * 16 * 17 * 4;        // fp32 tables [15][DK] (pi positions)
     static constexpr int GT = TAB + 15 * DK * 4;           // fp32 sub-block gate sums (log2) [4][DK]
@@ -189,65 +191,130 @@ struct Prep16Lds {
     static_assert(TOTAL <= 80 * 1024, "two prep workgroups per CU");
 };
 
-// Gram row block W (rows 16W..16W+15), column blocks I <= W: A (one bf16 pass) into sA, scaled by b_r
-// and strictly lower on the diagonal block; P (three passes) into sP, lower with diagonal.  xq = q E,
-// xk = k E, x3 = k / E with E = e^{Gloc} (sub-block-relative decay), all in pi order.
+// The decay-folded Gram blocks (R, I), I <= R, of A (one bf16 pass; scaled by b_r and strictly lower on
+// the diagonal block) and P (three passes; lower with diagonal), in 16x16 blocks.  Row block R's
+// operands are q E and k E of its rows (E = e^{Gloc}, the sub-block-relative decay), column block I's
+// are k e^{G_end(I) - G} times the decay over the blocks between (sCol, tD) or, on the diagonal,
+// k / E of the same rows; all in pi order.  Row block 3 has four blocks and row block 0 one, so the
+// work is shared out: wave W computes (W, I) for I <= W except that (3, 0) and (3, 1) go to waves 0
+// and 1, which read row block 3's operands from the fragments wave 3 staged in LDS (sRow3).  Results
+// stay in registers until every wave has read its operands (the staging lies over sA).
+template <int DK>
+struct GramOut {
+    f32x4_t a[3], p[3];
+};
 template <int W, int DK>
 __device__ __forceinline__ void gram16(const float (*xq)[8], const float (*xk)[8], const float (*x3)[8],
-                                       const float* sCol, const float* tD, const float* sBeta, float* sA, float* sP,
-                                       int m, int cg) {
+                                       const float* sCol, const float* tD, const bf16x8_t* sRow3, int lane,
+                                       int m, int cg, GramOut<DK>& g) {
     using Fr = Frag<false>;
     constexpr int KS = DK / 32;
-    f32x4_t accA[W + 1], accP[W + 1];
+    constexpr int ILO = W == 3 ? 2 : 0;   // own row block: column blocks ILO..W
+    constexpr int NX = W < 2 ? 1 : 0;     // one block of row block 3: (3, W)
 #pragma unroll
-    for (int I = 0; I <= W; ++I) accA[I] = accP[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 3; ++i) g.a[i] = g.p[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // column operand of block I for row block R, channels of step s
+    auto col = [&](int R, int I, int s, Fr& colf) {
+        float cx[8];
+        lds_read8(sCol + (16 * I + m) * (DK + 4) + 32 * s + 8 * cg, cx);
+        if (R - I >= 2) {
+            const int dsel = (R - I == 3) ? 2 : I;  // (0,2)->0, (1,3)->1, (0,3)->2
+            float d[8];
+            lds_read8(&tD[dsel * DK + 32 * s + 8 * cg], d);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cx[j] *= d[j];
+        }
+        colf.set(cx);
+    };
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const int p0 = 32 * s + 8 * cg;
         Fr fqE, fkE, fkd;
         fqE.set(xq[s]);
         fkE.set_hi_only(xk[s]);
         fkd.set(x3[s]);
 #pragma unroll
-        for (int I = 0; I < W; ++I) {
-            float cx[8];
-            lds_read8(sCol + (16 * I + m) * (DK + 4) + p0, cx);
-            if constexpr (W >= 2) {
-                if (W - I >= 2) {
-                    const int dsel = (W - I == 3) ? 2 : I;  // (0,2)->0, (1,3)->1, (0,3)->2
-                    float d[8];
-                    lds_read8(&tD[dsel * DK + p0], d);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) cx[j] *= d[j];
-                }
-            }
+        for (int I = ILO; I < W; ++I) {
             Fr colf;
-            colf.set(cx);
-            accA[I] = mma_fast(accA[I], fkE, colf);
-            accP[I] = mma_full(accP[I], fqE, colf);
+            col(W, I, s, colf);
+            g.a[I - ILO] = mma_fast(g.a[I - ILO], fkE, colf);
+            g.p[I - ILO] = mma_full(g.p[I - ILO], fqE, colf);
         }
-        accA[W] = mma_fast(accA[W], fkE, fkd);
-        accP[W] = mma_full(accP[W], fqE, fkd);
+        g.a[W - ILO] = mma_fast(g.a[W - ILO], fkE, fkd);
+        g.p[W - ILO] = mma_full(g.p[W - ILO], fqE, fkd);
+        if constexpr (NX) {
+            Fr rq, rk, colf;
+            rq.hi = sRow3[(s * 3 + 0) * 64 + lane];
+            rq.lo = sRow3[(s * 3 + 1) * 64 + lane];
+            rk.hi = sRow3[(s * 3 + 2) * 64 + lane];
+            col(3, W, s, colf);
+            g.a[W + 1] = mma_fast(g.a[W + 1], rk, colf);
+            g.p[W + 1] = mma_full(g.p[W + 1], rq, colf);
+        }
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
+}
+// Gram results of wave W to sA (times b_r) and sP: its own row block (zeros right of the diagonal block;
+// for row block 3 only its blocks 2 and 3) and, for waves 0 and 1, block (3, W).
+template <int W, int DK>
+__device__ __forceinline__ void gram16_store(const GramOut<DK>& g, const float* sBeta, float* sA, float* sP, int m,
+                                             int cg) {
+    constexpr int ILO = W == 3 ? 2 : 0;
+    auto put = [&](int R, int I, const f32x4_t& a, const f32x4_t& pv, bool diag) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int rr = 4 * cg + jj;
-            const int gr = 16 * W + rr, gi = 16 * I + m;
-            float a = 0.f, pv = 0.f;
-            if (I <= W) {
-                a = accA[I][jj];
-                pv = accP[I][jj];
-                if (I == W) {
-                    if (m >= rr) a = 0.f;
-                    if (m > rr) pv = 0.f;
-                }
+            const int gr = 16 * R + rr, gi = 16 * I + m;
+            float av = a[jj], pp = pv[jj];
+            if (diag) {
+                if (m >= rr) av = 0.f;
+                if (m > rr) pp = 0.f;
             }
-            sA[gr * 68 + gi] = a * sBeta[gr];
-            sP[gr * 68 + gi] = pv;
+            sA[gr * 68 + gi] = av * sBeta[gr];
+            sP[gr * 68 + gi] = pp;
         }
+    };
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int I = ILO; I < 4; ++I) {
+        if (I <= W) put(W, I, g.a[I - ILO], g.p[I - ILO], I == W);
+        else put(W, I, z, z, false);
     }
+    if constexpr (W < 2) put(3, W, g.a[W + 1], g.p[W + 1], false);
+}
+
+// -P N in 16x16 tiles (R, ct), ct <= R: tile (R, ct) = sum_{J=ct}^{R} P_RJ N_Jct (fp32 MFMA, P rows from
+// sP, N from sA).  Row block 3 has four tiles of up to four products and row block 0 one, so wave W
+// takes (W, ct) for ct <= W except that (3, 0) and (3, 1) go to waves 0 and 1.  Tiles are stored over
+// the P rows only after every wave has read them.
+template <int W>
+__device__ __forceinline__ void pn_tiles(const float* sP, const float* sA, int m, int cg, f32x4_t (&pn)[3]) {
+    constexpr int CLO = W == 3 ? 2 : 0;
+    auto tile = [&](int R, int ct) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J < ct || J > R) continue;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(16 * R + m) * 68 + 16 * J + 4 * kk + cg],
+                                                           sA[(16 * J + 4 * kk + cg) * 68 + 16 * ct + m], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+#pragma unroll
+    for (int ct = CLO; ct <= W; ++ct) pn[ct - CLO] = tile(W, ct);
+    if constexpr (W < 2) pn[W + 1] = tile(3, W);
+}
+template <int W>
+__device__ __forceinline__ void pn_store(float* sP, int m, int cg, const f32x4_t (&pn)[3]) {
+    constexpr int CLO = W == 3 ? 2 : 0;
+    auto put = [&](int R, int ct, const f32x4_t& x) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sP[(16 * R + 4 * cg + jj) * 68 + 16 * ct + m] = -x[jj];
+    };
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = CLO; ct < 4; ++ct) put(W, ct, ct <= W ? pn[ct - CLO] : z);
+    if constexpr (W < 2) put(3, W, pn[W + 1]);
 }
 
 // One workgroup (four waves, wave w = token rows 16w..16w+15) per (chunk, head); two per CU.
@@ -271,6 +338,7 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
     _Float16* sStg = reinterpret_cast<_Float16*>(smem + L::COL);
     float* sP = reinterpret_cast<float*>(smem + L::PM);
     float* sA = reinterpret_cast<float*>(smem + L::A);
+    bf16x8_t* sRow3 = reinterpret_cast<bf16x8_t*>(smem + L::A);  // over sA until the Gram results
     float* sD = reinterpret_cast<float*>(smem + L::D);
     float* tPw = reinterpret_cast<float*>(smem + L::TAB);   // e^{sum_{J<w} Gt_J}     [4][DK]
     float* tBt = tPw + 4 * DK;                              // e^{Gt_w}               [4][DK]
@@ -400,15 +468,32 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
             float* dst = sCol + r * (DK + 4) + p0;
             *reinterpret_cast<float4*>(dst) = make_float4(xc[0], xc[1], xc[2], xc[3]);
             *reinterpret_cast<float4*>(dst + 4) = make_float4(xc[4], xc[5], xc[6], xc[7]);
+        } else {  // row block 3's Gram operands (q E split, k E high part) for waves 0 and 1
+            Frag<false> fq, fk;
+            fq.set(xq[s]);
+            fk.set_hi_only(xk[s]);
+            sRow3[(s * 3 + 0) * 64 + lane] = fq.hi;
+            sRow3[(s * 3 + 1) * 64 + lane] = fq.lo;
+            sRow3[(s * 3 + 2) * 64 + lane] = fk.hi;
         }
     }
     lds_barrier();  // (3)
 
-    switch (w) {
-        case 0: gram16<0, DK>(xq, xk, x3, sCol, tD, sBeta, sA, sP, m, cg); break;
-        case 1: gram16<1, DK>(xq, xk, x3, sCol, tD, sBeta, sA, sP, m, cg); break;
-        case 2: gram16<2, DK>(xq, xk, x3, sCol, tD, sBeta, sA, sP, m, cg); break;
-        default: gram16<3, DK>(xq, xk, x3, sCol, tD, sBeta, sA, sP, m, cg); break;
+    {
+        GramOut<DK> go;
+        switch (w) {
+            case 0: gram16<0, DK>(xq, xk, x3, sCol, tD, sRow3, lane, m, cg, go); break;
+            case 1: gram16<1, DK>(xq, xk, x3, sCol, tD, sRow3, lane, m, cg, go); break;
+            case 2: gram16<2, DK>(xq, xk, x3, sCol, tD, sRow3, lane, m, cg, go); break;
+            default: gram16<3, DK>(xq, xk, x3, sCol, tD, sRow3, lane, m, cg, go); break;
+        }
+        lds_barrier();  // (3b) the staged operands are read
+        switch (w) {
+            case 0: gram16_store<0, DK>(go, sBeta, sA, sP, m, cg); break;
+            case 1: gram16_store<1, DK>(go, sBeta, sA, sP, m, cg); break;
+            case 2: gram16_store<2, DK>(go, sBeta, sA, sP, m, cg); break;
+            default: gram16_store<3, DK>(go, sBeta, sA, sP, m, cg); break;
+        }
     }
     lds_barrier();  // (4)
 
@@ -515,25 +600,20 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
         gst_h8(dst + kPl, lane, lo);
     }
     {
-        f32x4_t pn[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            pn[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (ct > w) continue;
-#pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J < ct || J > w) continue;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    pn[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(16 * w + m) * 68 + 16 * J + 4 * kk + cg],
-                                                                  sA[(16 * J + 4 * kk + cg) * 68 + 16 * ct + m], pn[ct],
-                                                                  0, 0, 0);
-            }
+        f32x4_t pn[3];
+        switch (w) {
+            case 0: pn_tiles<0>(sP, sA, m, cg, pn); break;
+            case 1: pn_tiles<1>(sP, sA, m, cg, pn); break;
+            case 2: pn_tiles<2>(sP, sA, m, cg, pn); break;
+            default: pn_tiles<3>(sP, sA, m, cg, pn); break;
         }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sP[(16 * w + 4 * cg + jj) * 68 + 16 * ct + m] = -pn[ct][jj];
+        lds_barrier();  // (7b) every P row is read
+        switch (w) {
+            case 0: pn_store<0>(sP, m, cg, pn); break;
+            case 1: pn_store<1>(sP, m, cg, pn); break;
+            case 2: pn_store<2>(sP, m, cg, pn); break;
+            default: pn_store<3>(sP, m, cg, pn); break;
+        }
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
