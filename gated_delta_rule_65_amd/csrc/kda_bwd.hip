@@ -316,48 +316,53 @@ __device__ __forceinline__ Frag<false> frag_rows(const float* base, int64_t ld, 
 //   dQt = dO S^T, dKt = -dX S^T, dKb = U dS'^T (64 x DK);  dP = dO U^T, dN = dU X^T (64 x 64);
 //   dgamma = rowsum(S o dS').
 // Split-bf16 three-pass products on the gradient kernel's 16 waves: the four waves of row block rb
-// (w & 3) take dQt, dKt, dKb, and dP with dN respectively (w >> 2).  Per 32-column step the operands
-// every wave needs (S and dS' rows, U and X rows) are read from memory once per workgroup, split once
-// and staged in LDS (S over sq, dS' over sk, U over sG, X over sM2: none of them holds anything yet);
-// the next step's pieces are requested while the current step's products run.  A wave's own rows (dO,
-// dX, U, dU) come straight from memory.  The results land in LDS for the phases that follow: dQt in sq,
-// dKt in sk, dKb in sG (rows [64][LD]), dN in sM1 and dP in sM3 ([64][65]), dgamma in sGam.
+// (w & 3) take dQt, dKt, dKb, and dP with dN respectively (w >> 2).  Per 32-column step every operand
+// (S, dS', dO, dX, U, X, dU) is read from memory once per workgroup, one step ahead, split once and
+// staged in LDS, one after the other from the start of sq (over sq, sk, sG and, at Dk = 64, sM1 and
+// part of sM2: none of them holds anything yet), so the products of a step wait for no memory request.  The results land in LDS
+// for the phases that follow: dQt in sq, dKt in sk, dKb in sG (rows [64][LD]), dN in sM1 and dP in sM3
+// ([64][65]), and gamma o dgamma (gamma from `gam`) in sGam.
 template <int DK>
 __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int64_t t0, int nt, int H, int h,
                                               int Dv, const float* __restrict__ S, const float* __restrict__ dS,
                                               const float* __restrict__ X, const float* __restrict__ dU,
-                                              float* sq, float* sk, float* sG, float* sM1, float* sM2, float* sM3,
-                                              float* sGam, int tid) {
+                                              const float* __restrict__ gam, float* sq, float* sk, float* sG,
+                                              float* sM1, float* sM3, float* sGam, int tid) {
     using MS = LMat<false, DK, 32>;  // S, dS' column step [c][n]
-    using MR = LMat<false, 64, 32>;  // U, X column step [t][n]
+    using MR = LMat<false, 64, 32>;  // U, X, dO, dX, dU column step [t][n]
     constexpr int LD = DK + 4;
     constexpr int CB = DK / 16;
-    static_assert(MS::BYTES <= 64 * LD * 4 && MR::BYTES <= 64 * LD * 4 && MR::BYTES <= 64 * 65 * 4,
-                  "the column steps fit the areas they are staged in");
     const float* U = X + 64 * (int64_t)Dv;
     const float* dX = dU + 64 * (int64_t)Dv;
     char* pS = reinterpret_cast<char*>(sq);
-    char* pD = reinterpret_cast<char*>(sk);
-    char* pU = reinterpret_cast<char*>(sG);
-    char* pX = reinterpret_cast<char*>(sM2);
+    char* pD = pS + MS::BYTES;
+    char* pU = pD + MS::BYTES;
+    char* pX = pU + MR::BYTES;
+    char* pO = pX + MR::BYTES;
+    char* pDX = pO + MR::BYTES;
+    char* pDU = pDX + MR::BYTES;
     const int w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int rb = w & 3, role = w >> 2;
-    // dO rows of row block rb: tokens past the end read the last token and count as zero
-    const int orow = 16 * rb + m;
-    const float* dO = d_o + ((t0 + min(orow, nt - 1)) * H + h) * (int64_t)Dv;
-    const float omask = orow < nt ? 1.f : 0.f;
-    // staging pieces of four values: S and dS' row tid / 8 (threads below 8 DK), U (threads below 512) or
-    // X row (tid % 512) / 8; columns 4 (tid % 8)
-    const bool hasS = tid < 8 * DK;
+    // staging pieces of four values, columns 4 (tid % 8) of the step: S and dS' row tid / 8 (threads
+    // below 8 DK); row (tid % 512) / 8 of U or X (threads below / from 512) and of dO or dX (likewise);
+    // dU row tid / 8 (threads below 512).  dO rows past the end read the last token and count as zero.
+    const bool hasS = tid < 8 * DK, lo = tid < 512;
     const int srow = tid >> 3, scol = 4 * (tid & 7), urow = (tid & 511) >> 3;
-    const float* UX = tid < 512 ? U : X;
-    float4 vS = make_float4(0.f, 0.f, 0.f, 0.f), vD = vS, vR = vS;
+    const float gam_row = hasS && (tid & 7) == 0 ? gam[srow] : 0.f;  // gamma of row srow, for its writer
+    const float* UX = lo ? U : X;
+    const float* OD = lo ? d_o + ((t0 + min(urow, nt - 1)) * H + h) * (int64_t)Dv - urow * (int64_t)Dv : dX;
+    const float omask = lo && urow >= nt ? 0.f : 1.f;
+    char* pUX = lo ? pU : pX;
+    char* pOD = lo ? pO : pDX;
+    float4 vS = make_float4(0.f, 0.f, 0.f, 0.f), vD = vS, vR = vS, vO = vS, vW = vS;
     auto fetch = [&](int k0) {
         if (hasS) {
             vS = *reinterpret_cast<const float4*>(S + srow * (int64_t)Dv + k0 + scol);
             vD = *reinterpret_cast<const float4*>(dS + srow * (int64_t)Dv + k0 + scol);
         }
         vR = *reinterpret_cast<const float4*>(UX + urow * (int64_t)Dv + k0 + scol);
+        vO = *reinterpret_cast<const float4*>(OD + urow * (int64_t)Dv + k0 + scol);
+        if (lo) vW = *reinterpret_cast<const float4*>(dU + urow * (int64_t)Dv + k0 + scol);
     };
     // one set of accumulator tiles for every role: CB tiles of dQt, dKt or dKb, or dN (0..3) and dP (4..7)
     constexpr int NACC = CB > 8 ? CB : 8;
@@ -373,33 +378,30 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
             lds_store4<false, DK, 32>(pD, srow, scol, f32x4_t{vD.x, vD.y, vD.z, vD.w});
             dgam = fmaf(vS.x, vD.x, fmaf(vS.y, vD.y, fmaf(vS.z, vD.z, fmaf(vS.w, vD.w, dgam))));
         }
-        lds_store4<false, 64, 32>(tid < 512 ? pU : pX, urow, scol, f32x4_t{vR.x, vR.y, vR.z, vR.w});
+        lds_store4<false, 64, 32>(pUX, urow, scol, f32x4_t{vR.x, vR.y, vR.z, vR.w});
+        lds_store4<false, 64, 32>(pOD, urow, scol, f32x4_t{omask * vO.x, omask * vO.y, omask * vO.z, omask * vO.w});
+        if (lo) lds_store4<false, 64, 32>(pDU, urow, scol, f32x4_t{vW.x, vW.y, vW.z, vW.w});
         __syncthreads();
         if (k0 + 32 < Dv) fetch(k0 + 32);
 
-        float x[8];
-        if (role == 0 || role == 3) {
-            load8_as_float(dO + k0 + 8 * cg, x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] *= omask;
-            Frag<false> fO;
-            fO.set(x);
-            // (loops unrolled by two: fully unrolled, every fragment is read ahead and registers spill)
-            if (role == 0) {
+        // (loops unrolled by two: fully unrolled, every fragment is read ahead and registers spill)
+        const int ar = 16 * rb + m;
+        if (role == 0) {
+            const Frag<false> fO = lds_frag<false, 64, 32>(pO, ar, 8 * cg);
 #pragma unroll 2
-                for (int cb = 0; cb < CB; ++cb)
-                    acc[cb] = mma_full(acc[cb], fO, lds_frag<false, DK, 32>(pS, 16 * cb + m, 8 * cg));
-            } else {
+            for (int cb = 0; cb < CB; ++cb)
+                acc[cb] = mma_full(acc[cb], fO, lds_frag<false, DK, 32>(pS, 16 * cb + m, 8 * cg));
+        } else if (role == 3) {
+            const Frag<false> fO = lds_frag<false, 64, 32>(pO, ar, 8 * cg);
 #pragma unroll 2
-                for (int ib = 0; ib < 4; ++ib)
-                    acc[4 + ib] = mma_full(acc[4 + ib], fO, lds_frag<false, 64, 32>(pU, 16 * ib + m, 8 * cg));
-                const Frag<false> fdU = frag_rows(dU, Dv, 16 * rb, k0, m, cg, x);
+            for (int ib = 0; ib < 4; ++ib)
+                acc[4 + ib] = mma_full(acc[4 + ib], fO, lds_frag<false, 64, 32>(pU, 16 * ib + m, 8 * cg));
+            const Frag<false> fdU = lds_frag<false, 64, 32>(pDU, ar, 8 * cg);
 #pragma unroll 2
-                for (int ib = 0; ib < 4; ++ib)
-                    acc[ib] = mma_full(acc[ib], fdU, lds_frag<false, 64, 32>(pX, 16 * ib + m, 8 * cg));
-            }
+            for (int ib = 0; ib < 4; ++ib)
+                acc[ib] = mma_full(acc[ib], fdU, lds_frag<false, 64, 32>(pX, 16 * ib + m, 8 * cg));
         } else {
-            const Frag<false> fr = frag_rows(role == 1 ? dX : U, Dv, 16 * rb, k0, m, cg, x);
+            const Frag<false> fr = lds_frag<false, 64, 32>(role == 1 ? pDX : pU, ar, 8 * cg);
             const char* pB = role == 1 ? pS : pD;
 #pragma unroll 2
             for (int cb = 0; cb < CB; ++cb) acc[cb] = mma_full(acc[cb], fr, lds_frag<false, DK, 32>(pB, 16 * cb + m, 8 * cg));
@@ -410,7 +412,7 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
     dgam += __shfl_xor(dgam, 2);
     dgam += __shfl_xor(dgam, 4);
     __syncthreads();  // every staged operand has been read
-    if (hasS && (tid & 7) == 0) sGam[srow] = dgam;
+    if (hasS && (tid & 7) == 0) sGam[srow] = gam_row * dgam;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * rb + 4 * cg + jj;
@@ -429,8 +431,6 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
     }
     __syncthreads();
 }
-
-// ============================================================================ to dq, dk, dg, db
 
 // Per (chunk, head), 1024 threads: first the sums over the value columns (colsum_to_lds), then through
 // N = Minv Diag(b) and Minv = (I + Diag(b) Abar)^{-1} to db and dAbar, then through the decayed Gram
@@ -454,9 +454,19 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     constexpr int NT = 1024;
     constexpr int LD = DK + 4;
     constexpr int CPT = DK / 16;
-    __shared__ __align__(16) float sq[64 * LD], sk[64 * LD], sG[64 * LD], sM1[64 * 65], sM2[64 * 65],
-        sM3[64 * 65], sB[64], sDB[64], sGb[5 * DK], sFf[6 * DK], sDf[4 * DK];
-    __shared__ uint32_t sMk[64 * DK / 32];  // bit set: g outside [-5, 0] (its gradient is zero)
+    // one block, in this order, so that the column sums can stage their operands across the first
+    // areas (colsum_to_lds)
+    constexpr int O_Q = 0, O_K = O_Q + 64 * LD, O_G = O_K + 64 * LD, O_M1 = O_G + 64 * LD, O_M2 = O_M1 + 64 * 65,
+                  O_M3 = O_M2 + 64 * 65, O_B = O_M3 + 64 * 65, O_DB = O_B + 64, O_GB = O_DB + 64, O_FF = O_GB + 5 * DK,
+                  O_DF = O_FF + 6 * DK, O_MK = O_DF + 4 * DK, O_GD = O_MK + 64 * DK / 32, FLOATS = O_GD + DK;
+    __shared__ __align__(16) float smem[FLOATS];
+    float *sq = smem + O_Q, *sk = smem + O_K, *sG = smem + O_G, *sM1 = smem + O_M1, *sM2 = smem + O_M2,
+          *sM3 = smem + O_M3, *sB = smem + O_B, *sDB = smem + O_DB, *sGb = smem + O_GB, *sFf = smem + O_FF,
+          *sDf = smem + O_DF;
+    uint32_t* sMk = reinterpret_cast<uint32_t*>(smem + O_MK);  // bit set: g outside [-5, 0] (its gradient is zero)
+    float* sGd = smem + O_GD;                                  // gamma o dgamma per channel
+    static_assert(O_M3 * 4 >= 2 * LMat<false, DK, 32>::BYTES + 5 * LMat<false, 64, 32>::BYTES,
+                  "the column sums' staging ends before sM3");
     const int tid = threadIdx.x;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x % H);
@@ -476,21 +486,19 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     for (int a = 0; a < EPT; ++a) vM[a] = rec[R::MIT + tid + a * NT];
 #pragma unroll
     for (int a = 0; a < EPT; ++a) vA[a] = rec[R::AB + tid + a * NT];
-    const float vgm = rec[R::GM + tid % DK];
 
     // ---- the sums over the value columns, into LDS
     colsum_to_lds<DK>(d_o, t0, nt, H, h, Dv, states + ch * DK * (int64_t)Dv, dstates + ch * DK * (int64_t)Dv,
-                      xu + ch * 128 * (int64_t)Dv, dudx + ch * 128 * (int64_t)Dv, sq, sk, sG, sM1, sM2, sM3, sFf,
-                      tid);
-    // this thread's pieces of them: dN and dP elements as in the loads above, dgamma of channel tid % DK,
-    // and its own elements of dQt, dKt, dKb (row tid / 16, channels (tid % 16) DK / 16 ..)
+                      xu + ch * 128 * (int64_t)Dv, dudx + ch * 128 * (int64_t)Dv, rec + R::GM, sq, sk, sG, sM1, sM3,
+                      sGd, tid);
+    // this thread's pieces of them: dN and dP elements as in the loads above, and its own elements of
+    // dQt, dKt, dKb (row tid / 16, channels (tid % 16) DK / 16 ..)
 #pragma unroll
     for (int a = 0; a < EPT; ++a) {
         const int e = tid + a * NT;
         vN[a] = sM1[(e >> 6) * 65 + (e & 63)];
         vP[a] = sM3[(e >> 6) * 65 + (e & 63)];
     }
-    const float vgd = vgm * sFf[tid % DK];  // gamma dgamma of channel tid % DK
     float pQt[CPT], pKt[CPT], pKb[CPT];
     {
         const int e0 = (tid >> 4) * LD + CPT * (tid & 15);
@@ -830,7 +838,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     __syncthreads();
     {
         const int c = sc_;
-        float off = vgd;  // gamma dgamma (c = tid % DK)
+        float off = sGd[c];  // gamma dgamma
         for (int wv = 0; wv < 16; ++wv) off += sM3[wv * DK + c];
         for (int s2 = sg_ + 1; s2 < NSEG; ++s2) off += sq[(SEG * s2) * LD + c];
 #pragma unroll
