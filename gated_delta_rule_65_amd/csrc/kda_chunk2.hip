@@ -939,49 +939,84 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 // Initial states of the segments of a split sequence, one workgroup per (sequence, head,
 // 32-column slice): S_in(0) = s0 (or 0), S_in(p+1) = Phi_p S_in(p) + S0_p for p < P - 1, written
 // to sfold [n][h][p][Dk][Dv] (p = 0 included).  fp32 throughout; the running state stays in LDS.
+// Each step is a [Dk x Dk] x [Dk x 32] product on fp32 MFMA (16x16x4): wave w owns result rows
+// 16 RT w .. as 16x16 tiles (row tile rt, column tile ct); MFMA number t of a tile contracts channel
+// (Dk/4) g + t in lane group g, so each lane reads one run of Dk/4 channels of its Phi row.  The next
+// step's Phi rows are requested while the current step's products run.
 template <int DK>
 __global__ __launch_bounds__(256) void fold_kernel(const float* s0, const float* __restrict__ sx,
                                                    float* __restrict__ sfold, int H, int Dv, int P) {
-    __shared__ float sS[DK][kS + 1];
-    const int tid = threadIdx.x, j = tid % kS, r0 = tid / kS;  // column j, rows r0 + 8i
-    constexpr int RPT = DK / 8;
+    constexpr int RT = DK / 64;   // row tiles per wave (4 waves x RT x 16 rows = DK)
+    constexpr int KPL = DK / 4;   // channels contracted by one lane group
+    constexpr int NQ = KPL / 4;   // float4 runs of a lane's Phi row
+    constexpr int SST = kS + 1;
+    __shared__ float sS[DK * SST];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
     const int NV = Dv / kS;
     const int64_t item = blockIdx.x / NV;  // n * H + h
-    const int col = (int)(blockIdx.x % NV) * kS + j;
-    float* const dst0 = sfold + (item * P * DK) * (int64_t)Dv;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int c = r0 + 8 * i;
-        const float x = s0 ? s0[(item * DK + c) * (int64_t)Dv + col] : 0.f;
-        sS[c][j] = x;
-        dst0[c * (int64_t)Dv + col] = x;
+    const int col0 = (int)(blockIdx.x % NV) * kS;
+    const int64_t ldx = Dv + DK;
+    // S_in(0): to LDS and to sfold[p = 0]
+    float* const dst0 = sfold + (item * P * DK) * (int64_t)Dv + col0;
+    for (int e = tid; e < DK * kS; e += 256) {
+        const int c = e / kS, j = e % kS;
+        const float x = s0 ? s0[(item * DK + c) * (int64_t)Dv + col0 + j] : 0.f;
+        sS[c * SST + j] = x;
+        dst0[c * Dv + j] = x;
     }
+    // Phi rows of this lane: row 16 (RT w + rt) + m, channels KPL g + 0..KPL-1 (NQ float4 per row tile)
+    float4 ph[RT][NQ];
+    auto load_phi = [&](int p) {
+        const float* X = sx + ((item * (P - 1) + p) * DK) * ldx + Dv;  // Phi_p [Dk][Dk] at column Dv
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                ph[rt][q] = *reinterpret_cast<const float4*>(X + (16 * (RT * w + rt) + m) * ldx + KPL * g + 4 * q);
+    };
+    if (P > 1) load_phi(0);
     __syncthreads();
     for (int p = 0; p + 1 < P; ++p) {
-        const float* X = sx + ((item * (P - 1) + p) * DK) * (int64_t)(Dv + DK);  // [Dk][Dv + Dk]
-        float acc[RPT];
+        const float* S0p = sx + ((item * (P - 1) + p) * DK) * ldx + col0;  // S0_p [Dk][Dv] at column 0
+        f32x4_t acc[RT][2];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = r0 + 8 * i;
-            const float* phi = X + c * (int64_t)(Dv + DK) + Dv;  // row c of Phi_p
-            float a = X[c * (int64_t)(Dv + DK) + col];           // S0_p
-            for (int cc = 0; cc < DK; cc += 4) {
-                const float4 f = *reinterpret_cast<const float4*>(phi + cc);
-                a = fmaf(f.x, sS[cc][j], a);
-                a = fmaf(f.y, sS[cc + 1][j], a);
-                a = fmaf(f.z, sS[cc + 2][j], a);
-                a = fmaf(f.w, sS[cc + 3][j], a);
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rt][ct][i] = S0p[(16 * (RT * w + rt) + 4 * g + i) * ldx + 16 * ct + m];
+        float4 cur[RT][NQ];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) cur[rt][q] = ph[rt][q];
+        if (p + 2 < P) load_phi(p + 1);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = 4 * q + u;
+                const float b0 = sS[(KPL * g + t) * SST + m], b1 = sS[(KPL * g + t) * SST + 16 + m];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const float av = u == 0 ? cur[rt][q].x : (u == 1 ? cur[rt][q].y : (u == 2 ? cur[rt][q].z : cur[rt][q].w));
+                    acc[rt][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b0, acc[rt][0], 0, 0, 0);
+                    acc[rt][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, acc[rt][1], 0, 0, 0);
+                }
             }
-            acc[i] = a;
-        }
-        __syncthreads();
-        float* dst = sfold + (((item * P + p + 1) * DK) * (int64_t)Dv);
+        __syncthreads();  // every lane has read S_in(p)
+        float* dst = sfold + ((item * P + p + 1) * DK) * (int64_t)Dv + col0;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int c = r0 + 8 * i;
-            sS[c][j] = acc[i];
-            dst[c * (int64_t)Dv + col] = acc[i];
-        }
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * (RT * w + rt) + 4 * g + i;
+                    sS[r * SST + 16 * ct + m] = acc[rt][ct][i];
+                    dst[r * Dv + 16 * ct + m] = acc[rt][ct][i];
+                }
         __syncthreads();
     }
 }

@@ -24,8 +24,12 @@
 // stores them without a pass through LDS.  The chain keeps the state in LDS in the same order.
 //
 // Precision.  Every product accumulates in fp32; the state is carried in fp32.  -W, Qh, Kbar, S and
-// U enter the products as fp16 (11 significant bits); N, P, V and U0 as fp16 hi + lo pairs
-// (about 21 bits).  v is converted exactly (bf16 values are fp16 values when they are in range).
+// U enter the products as fp16 (11 significant bits); N, P and U0 as fp16 hi + lo pairs (about 21
+// bits); V as fp16, exactly (a bf16 value times a power of two is an fp16 value while in range).
+// Range: the operands built from q, k and g scale with |q| |k| and |k|^2 (every decay factor is at
+// most 1), which unit-norm keys and queries keep far inside fp16; V and S carry the caller's scale,
+// so the chain runs on V 2^-e and S 2^-e with a per-chunk power-of-two e chosen from their maxima
+// (range_exp below) and scales o and the final state back.
 #include <algorithm>
 #include <type_traits>
 
@@ -39,6 +43,7 @@ namespace {
 constexpr int kC = 64;            // tokens per chunk
 constexpr int kS = 32;            // state columns per chain workgroup
 constexpr int kThreads = 576;     // chain workgroup: eight computing waves and one prefetching wave
+constexpr int kThreadsSO = 512;   // state-only chain: the eight computing waves, two workgroups per CU
 constexpr int kPl = 1024;         // one fragment plane: 64 lanes x 16 bytes
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -707,7 +712,7 @@ struct OutOps16 {
 // from a zero state, identity columns with V = 0; SO compiles the outputs out); 2 segment outputs from
 // the folded initial states.
 template <int DK, bool SO>
-__global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __restrict__ vv, const float* s0,
+__global__ __launch_bounds__(SO ? kThreadsSO : kThreads, SO ? 4 : 1) void chain16_kernel(const void* __restrict__ vv, const float* s0,
                                                               float* __restrict__ o, float* s_final,
                                                               const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                               int64_t T_stride, int64_t total, int64_t N, int H,
@@ -784,7 +789,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                accS[i][jj] = s_src[(16 * cbw + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nbt(i) + m];
+                accS[i][jj] = s_src[(16 * cbw + 4 * cg + jj) * Dv + col0 + 16 * nbt(i) + m];
     } else {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) accS[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1193,7 +1198,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain16_kernel(const void* __rest
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                sdst[(16 * cbw + 4 * cg + jj) * (int64_t)ld_dst + col_dst + 16 * nbt(i) + m] = sc * accS[i][jj];
+                sdst[(16 * cbw + 4 * cg + jj) * ld_dst + col_dst + 16 * nbt(i) + m] = sc * accS[i][jj];  // 32-bit
+                // offsets from the uniform base: a 64-bit address kept across the chunk loop spilled
     }
 }
 
@@ -1252,7 +1258,7 @@ static hipError_t launch16(const ChunkArgs& a, void* ws, hipStream_t st, bool al
     float* sfold = sx + a.N * a.H * (int64_t)(P - 1) * a.Dk * (a.Dv + a.Dk);
     const ChainMode c1{1, P, Lc, sx, nullptr};
     hipLaunchKernelGGL((chain16_kernel<DK, true>), dim3((unsigned)grid16(a.N * a.H * (P - 1), NV + DK / kS)),
-                       dim3(kThreads), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, T_stride, a.total,
+                       dim3(kThreadsSO), 0, st, a.v, a.s0, a.o, a.s_final, a.cu_seqlens, a.T_fixed, T_stride, a.total,
                        a.N, a.H, a.Dv, c1, static_cast<const char*>(ws));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_fold(DK, a.s0, sx, sfold, a.N * a.H, a.H, a.Dv, P, st)) != hipSuccess) return e;
