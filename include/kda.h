@@ -117,6 +117,13 @@ typedef enum {
  *   s_final : [B, H, Dk, Dv] float32 final state (written), or NULL
  * T = 0 is allowed: o is untouched and s_final receives s0 (or zeros).
  * s_final may alias s0 (each state is read before it is written).
+ * Arithmetic: float32 accumulation and a float32 state throughout.  With a
+ * workspace and bf16 inputs the per-chunk operands are fp16 (some as fp16
+ * pairs) on the matrix cores; v and the state are scaled by a power of two per
+ * chunk so that any magnitude stays in fp16's range, and queries and keys of
+ * the method's scale (unit norm, or qk_l2norm) keep the other operands far
+ * inside it.  fp32 inputs and the fused kernel (workspace NULL) use split-bf16
+ * or fp32 operands.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
@@ -133,8 +140,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
  * runs the call in windows of W * 64 tokens whose per-chunk records fit there:
  * W = floor((128 MiB - state) / (B * H * record)), with the record size given
  * for kda_chunk_workspace_bytes and state = B*H*Dk*Dv*4 bytes (rounded up to
- * 256) when s_final is NULL, else 0.  Calls with W < 1 (B*H above 1254 at
- * Dk = 128 with bf16 inputs and s_final given, above 777 without) are rejected with
+ * 256) when s_final is NULL, else 0.  Calls with W < 1 (B*H above 1807 at
+ * Dk = 128 with bf16 inputs and s_final given, above 960 without) are rejected with
  * KDA_ERR_BAD_SHAPE.  The scratch of the current device is used: `stream`
  * must belong to it.  Every call on a GPU shares that GPU's scratch, so calls
  * that may overlap on one GPU (different streams, or concurrent host threads)
@@ -148,8 +155,8 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
 /*
  * Workspace bytes kda_chunk_fwd needs for these sizes (0 if none are needed or
  * the arguments are unsupported): B * ceil(T/64) * H records of
- * 64*Dk*10 (bf16) or 64*Dk*12 (fp32) + 24576 + 4*Dk bytes
- * (104.5 KiB per chunk and head at Dk = 128 with bf16 inputs).  Calls with few
+ * 64*Dk*6 (bf16) or 64*Dk*12 (fp32) + 24576 + 4*Dk bytes
+ * (72.5 KiB per chunk and head at Dk = 128 with bf16 inputs).  Calls with few
  * state columns in all (2 * B*H*Dv/32 <= 256) and long sequences are cut into
  * P = min(256 / (B*H*Dv/32), ceil(T/64) / 64) >= 2 segments along T; they need
  * B*H*Dk*4*((P-1)*(Dv+Dk) + P*Dv) more bytes for the segment states.
