@@ -31,6 +31,7 @@
 // so the chain runs on V 2^-e and S 2^-e with a per-chunk power-of-two e chosen from their maxima
 // (range_exp below) and scales o and the final state back.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1218,7 +1219,54 @@ static int64_t segment16_bytes(const ChunkArgs& a, int P) {
 }
 static int64_t order16_bytes(const ChunkArgs& a) { return a.cu_seqlens ? ((a.N * 4 + 255) / 256) * 256 : 0; }
 
+// T-windows of long split calls.  A split-T call whose records would exceed the budget runs as
+// windows of equal length (at most the budget of records each), each a complete split-T call over its
+// tokens with the state carried from window to window in fp32 (s0 of the call, then a carry area or
+// s_final, read by the window's fold and written by its last segment), so that the workspace holds the
+// records of one window (the million-token call: 9.7 GB of records in one piece, 2.4 GB per window).
+// KDA_SPLIT_WINDOW_BYTES (bytes) overrides the budget, for tests of the windowed path at small sizes.
+static int64_t split_window_budget() {
+    const char* e = getenv("KDA_SPLIT_WINDOW_BYTES");
+    if (e && *e) {
+        const long long v = atoll(e);
+        if (v > 0) return (int64_t)v;
+    }
+    return int64_t(3) << 30;
+}
+static int64_t round256_16(int64_t x) { return (x + 255) / 256 * 256; }
+// chunks per window, or 0 when the call runs in one piece
+static int64_t split_window_chunks16(const ChunkArgs& a) {
+    if (a.cu_seqlens || a.T_fixed <= 0 || chunk_segments(a) < 2) return 0;
+    const int64_t nch = (a.T_fixed + kC - 1) / kC;
+    const int64_t per_chunk = a.N * a.H * chunk16_record_bytes(a.Dk);
+    const int64_t wmax = split_window_budget() / per_chunk;
+    if (nch <= wmax) return 0;
+    const int64_t nwin = (nch + std::max<int64_t>(wmax, 1) - 1) / std::max<int64_t>(wmax, 1);
+    return (nch + nwin - 1) / nwin;  // <= wmax (at least one chunk)
+}
+// the window of W chunks starting at token t0 of every sequence
+static ChunkArgs window16(const ChunkArgs& a, int64_t t0, int64_t W) {
+    ChunkArgs w = a;
+    w.T_fixed = std::min<int64_t>(W * kC, a.T_fixed - t0);
+    w.T_stride = a.T_stride > 0 ? a.T_stride : a.T_fixed;
+    const int64_t tk = t0 * a.H;  // token offset times heads
+    const int64_t g_es = a.pro.g_bf16 ? 2 : 4, b_es = a.pro.b_bf16 ? 2 : 4;
+    w.q = static_cast<const char*>(a.q) + tk * a.Dk * 2;
+    w.k = static_cast<const char*>(a.k) + tk * a.Dk * 2;
+    w.v = static_cast<const char*>(a.v) + tk * a.Dv * 2;
+    w.g = static_cast<const char*>(a.g) + tk * a.Dk * g_es;
+    w.beta = static_cast<const char*>(a.beta) + tk * b_es;
+    w.o = a.o + tk * a.Dv;
+    return w;
+}
+static int64_t window_state_bytes16(const ChunkArgs& a) { return round256_16(a.N * a.H * (int64_t)a.Dk * a.Dv * 4); }
+
 int64_t chunk16_workspace_bytes(const ChunkArgs& a) {
+    const int64_t W = split_window_chunks16(a);
+    if (W > 0) {
+        const ChunkArgs w = window16(a, 0, W);
+        return window_state_bytes16(a) + records16_bytes(w) + segment16_bytes(w, chunk_segments(w));
+    }
     return records16_bytes(a) + segment16_bytes(a, chunk_segments(a)) + order16_bytes(a);
 }
 
@@ -1226,6 +1274,21 @@ static int64_t grid16(int64_t items, int slices) { return ((items + 7) / 8) * 8 
 
 template <int DK>
 static hipError_t launch16(const ChunkArgs& a, void* ws, hipStream_t st, bool allow_split) {
+    if (allow_split) {
+        const int64_t W = split_window_chunks16(a);
+        if (W > 0) {  // windows, each a split call of its own
+            float* carry = a.s_final ? a.s_final : static_cast<float*>(ws);
+            char* wws = static_cast<char*>(ws) + window_state_bytes16(a);
+            for (int64_t t0 = 0; t0 < a.T_fixed; t0 += W * kC) {
+                ChunkArgs w = window16(a, t0, W);
+                w.s0 = t0 == 0 ? a.s0 : carry;
+                w.s_final = carry;
+                const hipError_t e = launch16<DK>(w, wws, st, true);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
+    }
     const int64_t T_stride = a.T_stride > 0 ? a.T_stride : a.T_fixed;
     const int64_t prep_grid = slots16(a) * a.H;
     char* w = static_cast<char*>(ws);

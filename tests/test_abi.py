@@ -163,14 +163,49 @@ def segment_bytes(B, H, Dk, Dv, P):
     return 0 if P < 2 else B * H * Dk * 4 * ((P - 1) * (Dv + Dk) + P * Dv)
 
 
+SPLIT_WINDOW_BUDGET = 3 << 30  # records of one T-window of a long split call (bf16 inputs)
+
+
+def window_chunks(B, T, H, Dk, Dv, dtype, budget=SPLIT_WINDOW_BUDGET):
+    """Chunks per T-window, or 0 for one piece: bf16 split calls whose records exceed the budget run
+    as equal windows of at most the budget each."""
+    nch = -(-T // 64)
+    per_chunk = B * H * record_bytes(Dk, dtype)
+    if dtype != 1 or segments(B, T, H, Dv) < 2 or nch * per_chunk <= budget:
+        return 0
+    wmax = max(budget // per_chunk, 1)
+    nwin = -(-nch // wmax)
+    return -(-nch // nwin)
+
+
+def workspace_bytes(B, T, H, Dk, Dv, dtype, budget=SPLIT_WINDOW_BUDGET):
+    W = window_chunks(B, T, H, Dk, Dv, dtype, budget)
+    if W == 0:
+        return B * (-(-T // 64)) * H * record_bytes(Dk, dtype) + segment_bytes(B, H, Dk, Dv, segments(B, T, H, Dv))
+    state = -(-(B * H * Dk * Dv * 4) // 256) * 256  # carried between windows
+    return state + B * W * H * record_bytes(Dk, dtype) + segment_bytes(B, H, Dk, Dv, segments(B, W * 64, H, Dv))
+
+
 @pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("B,T,H,Dk,Dv", [(1, 64, 1, 128, 128), (4, 8192, 16, 128, 128), (2, 65, 3, 64, 128),
                                          (3, 1, 2, 64, 64), (1, 1 << 20, 8, 128, 128), (1, 16421, 2, 128, 128),
-                                         (1, 8192, 1, 64, 64)])
+                                         (1, 8192, 1, 64, 64), (1, 1 << 19, 8, 128, 128)])
 def test_chunk_workspace_size(B, T, H, Dk, Dv, dtype):
-    P = segments(B, T, H, Dv)
-    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv, dtype) == (B * (-(-T // 64)) * H * record_bytes(Dk, dtype)
-                                                                 + segment_bytes(B, H, Dk, Dv, P))
+    assert kda.chunk_workspace_bytes(B, T, H, Dk, Dv, dtype) == workspace_bytes(B, T, H, Dk, Dv, dtype)
+
+
+def test_long_split_calls_run_in_windows():
+    # the million-token call: four windows of 4,096 chunks, 2.4 GB of records instead of 9.7 GB
+    assert window_chunks(1, 1 << 20, 8, 128, 128, 1) == 4096
+    assert kda.chunk_workspace_bytes(1, 1 << 20, 8, 128, 128) < 2.5e9
+    assert window_chunks(4, 8192, 16, 128, 128, 1) == 0 and window_chunks(1, 1 << 20, 8, 128, 128, 0) == 0
+
+
+def test_window_budget_override(monkeypatch):
+    monkeypatch.setenv("KDA_SPLIT_WINDOW_BYTES", str(8 << 20))
+    for B, T, H in [(1, 16421, 2), (1, 8192, 1), (1, 1 << 16, 2)]:
+        assert kda.chunk_workspace_bytes(B, T, H, 128, 128) == workspace_bytes(B, T, H, 128, 128, 1, 8 << 20)
+    assert window_chunks(1, 1 << 16, 2, 128, 128, 1, 8 << 20) > 0
 
 
 def test_segment_counts():

@@ -325,6 +325,18 @@ def test_split_t_segments(T, H, Dk, Dv, dtype, with_s0):
     check(inp, *run_chunk(inp))
 
 
+def test_long_split_call_in_windows(monkeypatch):
+    """A split call whose records exceed the window budget runs as T-windows, each a split call of
+    its own, with the state carried between them: four windows of 256 chunks, four segments each."""
+    monkeypatch.setenv("KDA_SPLIT_WINDOW_BYTES", str(40 << 20))
+    spec = kda_inputs.Spec([65536], 2, 128, 128, "bf16", "softplus_bounds", 0.05, s0_std=0.02, seed=45,
+                           name="split-windows")
+    inp = kda_inputs.generate(spec)
+    B, T, H = 1, 65536, 2
+    assert kda.chunk_workspace_bytes(B, T, H, 128, 128) < B * (T // 64) * H * 74240  # windowed
+    check(inp, *run_chunk(inp))
+
+
 def test_two_pass_with_caller_workspace_reused_and_dirty():
     """The workspace needs no initial contents and one buffer serves calls of different sizes."""
     big = kda_inputs.generate(kda_inputs.Spec([300] * 2, 3, 128, 128, "bf16", "softplus_bounds", 0.05,
