@@ -20,9 +20,10 @@
 //   then through Abar, P, Qt, Kt, Kb and gamma to q, k and G, and from G to g by a reverse
 //   running sum inside the chunk (the clamp passes the gradient where -5 <= g <= 0).
 //
-// Qt, Kt, Kb, P, Minv, Abar, gamma, b per (chunk, head) (fp32) and the state at every chunk start come
-// from the forward pass's prep kernel in its backward form and its chain kernel in mode 3, on split-bf16
-// records with every product in three passes (launch_chunk_states).  Then two kernels, fp32
+// Per (chunk, head), the reverse chain's operands Qt^T, -Kt^T, Kb, P^T, (Minv Diag(b))^T as split-bf16
+// MFMA fragments, the gradient kernel's Minv, Abar, gamma, b in fp32, and the state at every chunk
+// start come from the forward pass's prep kernel in its backward form and its chain kernel in mode 3,
+// on split-bf16 records with every product in three passes (launch_chunk_states).  Then two kernels, fp32
 // accumulation (the reverse chain and the column sums as three-pass split-bf16 products, the rest of the
 // gradient kernel on fp32 MFMA):
 //   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS', dU, dX of every
@@ -117,47 +118,55 @@ __device__ __forceinline__ bool chain_item(int64_t items, int NS, int64_t& pr, i
 
 // ============================================================================ state gradients, in reverse
 
-// One workgroup of 1024 threads (16 waves) per (sequence, head, 32 state columns) walks the chunks
-// backwards on MFMA (F32: fp32 products, else split bf16):
-//   dU = P^T dO + Kb dS',  dX = Diag(b) Minv^T dU,  dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX.
-// Waves 0-7 own one 16x16 tile of dU and dX each; every wave (Dk = 128) or waves 0-7 (Dk = 64) own
-// one 16x16 tile of dS, which stays in their registers from chunk to chunk.  dS' (the gradient at
-// the chunk end) goes to dstates, dU and dX to dudx, dX to dv.  The operands are read with 16-byte
-// loads into registers one phase ahead of their use and staged in LDS in operand order (rows, then
-// the contracted index), so that each MFMA fragment is one row read.
-template <int DK, bool F32>
-__global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __restrict__ d_o,
-                                                              const float* __restrict__ d_sfinal, float* ds0,
-                                                              const int32_t* __restrict__ cu, int64_t T_fixed,
-                                                              int64_t total, int64_t N, int H, int Dv,
-                                                              const float* __restrict__ recs,
-                                                              float* __restrict__ dstates, float* __restrict__ dudx,
-                                                              float* __restrict__ dv) {
+// Two consecutive elements (columns col, col + 1; col even) of one row of a split-bf16 LDS matrix.
+template <int ROWS, int COLS>
+__device__ __forceinline__ void lds_store2(char* base, int row, int col, float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    using M = LMat<false, ROWS, COLS>;
+    const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+    const bf16x2_t hi = {ha, hb}, lo = {(__bf16)(a - (float)ha), (__bf16)(b - (float)hb)};
+    __bf16* p = reinterpret_cast<__bf16*>(base) + row * M::STRIDE + col;
+    *reinterpret_cast<bf16x2_t*>(p) = hi;
+    *reinterpret_cast<bf16x2_t*>(p + M::PLANE) = lo;
+}
+
+// A split-bf16 MFMA fragment of a record: a plane of 64 lanes x 16 B of bf16 hi, then one of bf16 lo.
+__device__ __forceinline__ Frag<false> rec_frag(const float* p, int lane) {
+    Frag<false> f;
+    f.hi = reinterpret_cast<const bf16x8_t*>(p)[lane];
+    f.lo = reinterpret_cast<const bf16x8_t*>(p + 256)[lane];
+    return f;
+}
+
+// One workgroup per (sequence, head, 32 state columns) walks the chunks backwards on split-bf16 MFMA:
+//   dU = P^T dO + Kb dS',  dX = N^T dU,  dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX   (N = Minv Diag(b)).
+// Waves 0-3 (U waves) own rows 16w.. of dU and dX; waves 4.. (S waves) own rows 16(w-4).. of dS,
+// which stays in their registers from chunk to chunk; each wave covers both 16-column tiles of its
+// rows.  A wave loads the fragments of P^T, Kb, N^T (U) or Qt^T, -Kt^T (S) that it multiplies
+// straight from the record into registers, one chunk ahead (each a contiguous 1 KiB request per
+// plane), so each record is read once per workgroup and the products take only the operands shared
+// between waves from LDS: dO^T, dS'^T, dU^T, dX^T.  Three barriers per chunk:
+//   (1) U: dU -> LDS                        S: dS = Diag(gamma) dS' + Qt^T dO
+//   (2) U: dX -> LDS; dU, dX and dv to memory
+//   (3) U: dO^T of the next chunk -> LDS    S: dS -= Kt^T dX; dS' of the next chunk -> LDS
+// Every chunk issues the same memory instructions in the same order (the loads past either end
+// are clamped to an existing chunk, never skipped, and the first chunk is peeled off the loop), so
+// the compiler's wait counts are exact and no wait for a load also waits for a store.
+template <int DK>
+__global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
+    const float* __restrict__ d_o, const float* __restrict__ d_sfinal, float* ds0, const int32_t* __restrict__ cu,
+    int64_t T_fixed, int64_t total, int64_t N, int H, int Dv, const float* __restrict__ recs,
+    float* __restrict__ dstates, float* __restrict__ dudx, float* __restrict__ dv) {
     using R = BRec<DK>;
-    using Fr = Frag<F32>;
-    using MTT = LMat<F32, 64, 64>;   // P^T, Minv^T  [i][r]
-    using MKB = LMat<F32, 64, DK>;   // Kb           [i][c]
-    using MQT = LMat<F32, DK, 64>;   // Qt^T, -Kt^T  [c][r]
-    using MOT = LMat<F32, kBS, 64>;  // dO^T, dU^T, dX^T [j][r]
-    using MDS = LMat<F32, kBS, DK>;  // dS'^T [j][c]
-    constexpr int NT = 1024;
-    constexpr int AB1 = MTT::BYTES + MKB::BYTES, AB2 = 2 * MQT::BYTES;
-    constexpr int A_BYTES = AB1 > AB2 ? AB1 : AB2;  // P^T + Kb (for dU), then Qt^T + -Kt^T (for dS)
-    constexpr int O_MT = A_BYTES, O_OT = O_MT + MTT::BYTES, O_DS = O_OT + MOT::BYTES, O_DU = O_DS + MDS::BYTES,
-                  O_DX = O_DU + MOT::BYTES, O_B = O_DX + MOT::BYTES, O_G = O_B + 256, TOTAL = O_G + DK * 4;
-    constexpr int KQ = 64 * DK / 4 / NT;  // 16-byte pieces per thread of a [64][DK] operand
-    __shared__ __align__(16) char smem[TOTAL];
-    char* pPT = smem;
-    char* pKB = smem + MTT::BYTES;
-    char* pQT = smem;
-    char* pKT = smem + MQT::BYTES;
-    char* pMT = smem + O_MT;
-    char* pOT = smem + O_OT;
-    char* pDS = smem + O_DS;
-    char* pDU = smem + O_DU;
-    char* pDX = smem + O_DX;
-    float* sB = reinterpret_cast<float*>(smem + O_B);
-    float* sG = reinterpret_cast<float*>(smem + O_G);
+    using Fr = Frag<false>;
+    using MOT = LMat<false, kBS, 64>;  // dO^T, dU^T, dX^T [j][r]
+    using MDS = LMat<false, kBS, DK>;  // dS'^T [j][c]
+    constexpr int KS = DK / 32;
+    __shared__ __align__(16) char smem[3 * MOT::BYTES + MDS::BYTES];
+    char* pOT = smem;
+    char* pDU = smem + MOT::BYTES;
+    char* pDX = smem + 2 * MOT::BYTES;
+    char* pDS = smem + 3 * MOT::BYTES;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     int64_t pr;
@@ -168,133 +177,181 @@ __global__ __launch_bounds__(1024, 1) void bwd_dstates_kernel(const float* __res
     const BSeq sr = bseq(cu, n, T_fixed, total);
     const int64_t nch = (sr.end - sr.start + kBC - 1) / kBC;
     const int col0 = sl * kBS;
-
-    const bool uwave = w < 8;                         // owns a tile of dU and dX
-    const int rb = (w >> 1) & 3, nb = w & 1;          // that tile: rows 16rb.., columns 16nb..
-    const int s0u = rb >= 2 ? 1 : 0;                  // P^T, Minv^T rows 16rb.. vanish below column 32 s0u
-    const bool swave = w < DK / 8;                    // owns a tile of dS
-    const int cb = w >> 1;                            // that tile: rows 16cb.., columns 16nb..
-
-    // dS' in the owners' registers (D layout: rows 16cb + 4cg + jj, column 16nb + m) and in LDS
-    f32x4_t dS = {0.f, 0.f, 0.f, 0.f};
-    if (swave) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            dS[jj] = d_sfinal ? d_sfinal[((n * H + h) * DK + 16 * cb + 4 * cg + jj) * (int64_t)Dv + col0 + 16 * nb + m]
-                              : 0.f;
-        lds_store4<F32, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, dS);
-    }
-
-    float4 rPT, rMT, rKB[KQ], rQT[KQ], rKT[KQ];
-    float2 rO;
-    float rB = 0.f, rG = 0.f;
-    const int orow = tid >> 4, ocol = 2 * (tid & 15);  // this thread's two dO values
     auto rec_of = [&](int64_t jc) {
         return recs + (bslot(cu, n, jc, T_fixed, sr.start) * H + h) * (int64_t)R::FLOATS;
     };
-    auto load_a = [&](int64_t jc) {  // P^T, Minv^T, Kb, dO, b, gamma of chunk jc
-        const float* rec = rec_of(jc);
-        rPT = reinterpret_cast<const float4*>(rec + R::PMT)[tid];
-        rMT = reinterpret_cast<const float4*>(rec + R::MIT)[tid];
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) rKB[q] = reinterpret_cast<const float4*>(rec + R::KB)[tid + q * NT];
-        const int64_t t0 = sr.start + jc * kBC;
-        const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        rO = orow < nt ? *reinterpret_cast<const float2*>(d_o + ((t0 + orow) * H + h) * (int64_t)Dv + col0 + ocol)
-                       : make_float2(0.f, 0.f);
-        if (tid < 64) rB = rec[R::BT + tid];
-        if (tid < DK) rG = rec[R::GM + tid];
-    };
-    auto load_c = [&](int64_t jc) {  // Qt^T, Kt^T of chunk jc
-        const float* rec = rec_of(jc);
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            rQT[q] = reinterpret_cast<const float4*>(rec + R::QTT)[tid + q * NT];
-            rKT[q] = reinterpret_cast<const float4*>(rec + R::KTT)[tid + q * NT];
-        }
-    };
-    auto f4 = [](float4 x, float sgn) { return f32x4_t{sgn * x.x, sgn * x.y, sgn * x.z, sgn * x.w}; };
 
-    if (nch > 0) load_a(nch - 1);
-    for (int64_t jc = nch - 1; jc >= 0; --jc) {
-        const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
-        const int64_t t0 = sr.start + jc * kBC;
-        const int nt = (int)min<int64_t>(kBC, sr.end - t0);
-        if (swave) {  // dS' of this chunk
-            float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv + col0 + 16 * nb + m;
+    if (w < 4) {  // ------------------------------------------------------------------ U waves
+        const int rb = w;
+        Fr fP[2], fK[KS], fN[2];
+        float4 o0, o1;
+        const int p = tid >> 3, q = tid & 7;  // dO staging: rows 2p, 2p + 1, columns 4q .. 4q + 3
+        int ont = 0;                          // valid rows of the chunk whose dO is in o0, o1
+        auto load_o = [&](int64_t jc) {
+            const int64_t t0 = sr.start + jc * kBC;
+            ont = (int)min<int64_t>(kBC, sr.end - t0);
+            const float* base = d_o + (int64_t)h * Dv + col0 + 4 * q;
+            o0 = *reinterpret_cast<const float4*>(base + (t0 + min(2 * p, ont - 1)) * H * (int64_t)Dv);
+            o1 = *reinterpret_cast<const float4*>(base + (t0 + min(2 * p + 1, ont - 1)) * H * (int64_t)Dv);
+        };
+        auto stage_o = [&]() {  // dO^T (rows past the end as zeros)
+            const float4 a = 2 * p < ont ? o0 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 b = 2 * p + 1 < ont ? o1 : make_float4(0.f, 0.f, 0.f, 0.f);
+            lds_store2<kBS, 64>(pOT, 4 * q + 0, 2 * p, a.x, b.x);
+            lds_store2<kBS, 64>(pOT, 4 * q + 1, 2 * p, a.y, b.y);
+            lds_store2<kBS, 64>(pOT, 4 * q + 2, 2 * p, a.z, b.z);
+            lds_store2<kBS, 64>(pOT, 4 * q + 3, 2 * p, a.w, b.w);
+        };
+        if (nch > 0) {
+            const float* rec = rec_of(nch - 1);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) st_nt(&dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv], dS[jj]);
-        }
-        // stage P^T, Minv^T, Kb, dO^T, b, gamma (the previous chunk's dS phase has finished: barrier)
-        lds_store4<F32, 64, 64>(pPT, (4 * tid) >> 6, (4 * tid) & 63, f4(rPT, 1.f));
-        lds_store4<F32, 64, 64>(pMT, (4 * tid) >> 6, (4 * tid) & 63, f4(rMT, 1.f));
+            for (int s = 0; s < 2; ++s) fP[s] = rec_frag(rec + R::PTF + (rb * 2 + s) * R::FRAG, lane);
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            const int e = 4 * (tid + q * NT);
-            lds_store4<F32, 64, DK>(pKB, e / DK, e % DK, f4(rKB[q], 1.f));
+            for (int s = 0; s < KS; ++s) fK[s] = rec_frag(rec + R::KBF + (rb * KS + s) * R::FRAG, lane);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) fN[s] = rec_frag(rec + R::NTF + (rb * 2 + s) * R::FRAG, lane);
+            load_o(nch - 1);
+            stage_o();
+            load_o(nch > 1 ? nch - 2 : 0);
         }
-        lds_store1<F32, kBS, 64>(pOT, ocol, orow, rO.x);
-        lds_store1<F32, kBS, 64>(pOT, ocol + 1, orow, rO.y);
-        if (tid < 64) sB[tid] = rB;
-        if (tid < DK) sG[tid] = rG;
-        load_c(jc);
-        __syncthreads();
-        if (jc > 0) load_a(jc - 1);
-
-        f32x4_t accU = {0.f, 0.f, 0.f, 0.f};
-        if (uwave) {  // dU = P^T dO + Kb dS'
-            for (int s = s0u; s < 2; ++s)
-                accU = mma_full(accU, lds_frag<F32, 64, 64>(pPT, 16 * rb + m, 32 * s + 8 * cg),
-                                lds_frag<F32, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
-#pragma unroll 1  // (unrolled, the fragments of several steps are read ahead and registers spill)
-            for (int s = 0; s < DK / 32; ++s)
-                accU = mma_full(accU, lds_frag<F32, 64, DK>(pKB, 16 * rb + m, 32 * s + 8 * cg),
-                                lds_frag<F32, kBS, DK>(pDS, 16 * nb + m, 32 * s + 8 * cg));
-            lds_store4<F32, kBS, 64>(pDU, 16 * nb + m, 16 * rb + 4 * cg, accU);
-        }
-        __syncthreads();
-        if (uwave) {  // dX = Diag(b) Minv^T dU; dU, dX of the chunk and dv = dX
-            f32x4_t accX = {0.f, 0.f, 0.f, 0.f};
-            for (int s = s0u; s < 2; ++s)
-                accX = mma_full(accX, lds_frag<F32, 64, 64>(pMT, 16 * rb + m, 32 * s + 8 * cg),
-                                lds_frag<F32, kBS, 64>(pDU, 16 * nb + m, 32 * s + 8 * cg));
-            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + 16 * nb + m;
+        lds_barrier();
+        auto chunk = [&](int64_t jc) {
+            const float* recn = rec_of(jc > 0 ? jc - 1 : 0);  // operands of the next chunk
+            const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
+            const int64_t t0 = sr.start + jc * kBC;
+            const int nt = (int)min<int64_t>(kBC, sr.end - t0);
+            // (1) dU = P^T dO + Kb dS'
+            f32x4_t aU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const Fr a = fP[s];
+                fP[s] = rec_frag(recn + R::PTF + (rb * 2 + s) * R::FRAG, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    aU[nb] = mma_full(aU[nb], a, lds_frag<false, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
+            }
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const Fr a = fK[s];
+                fK[s] = rec_frag(recn + R::KBF + (rb * KS + s) * R::FRAG, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    aU[nb] = mma_full(aU[nb], a, lds_frag<false, kBS, DK>(pDS, 16 * nb + m, 32 * s + 8 * cg));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, 64>(pDU, 16 * nb + m, 16 * rb + 4 * cg, aU[nb]);
+            lds_barrier();  // (1)
+            // (2) dX = N^T dU; dU, dX of the chunk and dv = dX to memory
+            f32x4_t aX[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const Fr a = fN[s];
+                fN[s] = rec_frag(recn + R::NTF + (rb * 2 + s) * R::FRAG, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    aX[nb] = mma_full(aX[nb], a, lds_frag<false, kBS, 64>(pDU, 16 * nb + m, 32 * s + 8 * cg));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, aX[nb]);
+            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + m;
+            float* dv_o = dv + (t0 * H + h) * (int64_t)Dv + col0 + m;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * rb + 4 * cg + jj;
-                accX[jj] *= sB[i];
-                st_nt(&du_o[i * (int64_t)Dv], accU[jj]);
-                st_nt(&du_o[(64 + i) * (int64_t)Dv], accX[jj]);
-                if (i < nt) st_nt(&dv[((t0 + i) * H + h) * (int64_t)Dv + col0 + 16 * nb + m], accX[jj]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    st_nt(&du_o[i * (int64_t)Dv + 16 * nb], aU[nb][jj]);
+                    st_nt(&du_o[(64 + i) * (int64_t)Dv + 16 * nb], aX[nb][jj]);
+                    // rows past the end store dX a second time over its own dudx entry
+                    st_nt(i < nt ? &dv_o[i * (int64_t)H * Dv + 16 * nb] : &du_o[(64 + i) * (int64_t)Dv + 16 * nb],
+                          aX[nb][jj]);
+                }
             }
-            lds_store4<F32, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, accX);
+            lds_barrier();  // (2)
+            // (3) dO^T of the next chunk (every read of this chunk's dO^T is behind barrier 1)
+            stage_o();
+            load_o(jc > 1 ? jc - 2 : 0);
+            lds_barrier();  // (3)
+        };
+        if (nch > 0) {  // the first chunk peeled: the loop is entered only after one whole chunk
+            chunk(nch - 1);
+            for (int64_t jc = nch - 2; jc >= 0; --jc) chunk(jc);
         }
-        __syncthreads();  // P^T and Kb are no longer read: Qt^T and -Kt^T go over them
+    } else {  // ------------------------------------------------------------------------ S waves
+        const int cb = w - 4;
+        Fr fQ[2], fK[2];
+        float4 g4;
+        // dS' in registers (D layout: rows 16cb + 4cg + jj, columns 16nb + m) and in LDS
+        f32x4_t acc[2];
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-            const int e = 4 * (tid + q * NT);
-            lds_store4<F32, DK, 64>(pQT, e / 64, e % 64, f4(rQT[q], 1.f));
-            lds_store4<F32, DK, 64>(pKT, e / 64, e % 64, f4(rKT[q], -1.f));
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                acc[nb][jj] = d_sfinal ? d_sfinal[((n * H + h) * DK + 16 * cb + 4 * cg + jj) * (int64_t)Dv + col0 +
+                                                  16 * nb + m]
+                                       : 0.f;
+            lds_store4<false, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, acc[nb]);
         }
-        __syncthreads();
-        if (swave) {  // dS = Diag(gamma) dS' + Qt^T dO - Kt^T dX
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dS[jj] *= sG[16 * cb + 4 * cg + jj];
+        if (nch > 0) {
+            const float* rec = rec_of(nch - 1);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                dS = mma_full(dS, lds_frag<F32, DK, 64>(pQT, 16 * cb + m, 32 * s + 8 * cg),
-                              lds_frag<F32, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
-                dS = mma_full(dS, lds_frag<F32, DK, 64>(pKT, 16 * cb + m, 32 * s + 8 * cg),
-                              lds_frag<F32, kBS, 64>(pDX, 16 * nb + m, 32 * s + 8 * cg));
+                fQ[s] = rec_frag(rec + R::QTF + (cb * 2 + s) * R::FRAG, lane);
+                fK[s] = rec_frag(rec + R::KTF + (cb * 2 + s) * R::FRAG, lane);
             }
-            lds_store4<F32, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, dS);
+            g4 = *reinterpret_cast<const float4*>(rec + R::GM + 16 * cb + 4 * cg);
         }
-        __syncthreads();
-    }
-    if (ds0 && swave) {
-        float* d0 = ds0 + (n * H + h) * (int64_t)DK * Dv + col0;  // uniform base, small per-lane offsets
+        lds_barrier();
+        auto chunk = [&](int64_t jc) {
+            const float* recn = rec_of(jc > 0 ? jc - 1 : 0);
+            const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
+            // dS' of this chunk (the gradient at its end) to memory
+            float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv + col0 + m;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) d0[(16 * cb + 4 * cg + jj) * Dv + 16 * nb + m] = dS[jj];
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) st_nt(&dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv + 16 * nb], acc[nb][jj]);
+            // (1) dS = Diag(gamma) dS' + Qt^T dO
+            const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[nb][jj] *= gg[jj];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const Fr a = fQ[s];
+                fQ[s] = rec_frag(recn + R::QTF + (cb * 2 + s) * R::FRAG, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[nb] = mma_full(acc[nb], a, lds_frag<false, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
+            }
+            g4 = *reinterpret_cast<const float4*>(recn + R::GM + 16 * cb + 4 * cg);
+            lds_barrier();  // (1)
+            lds_barrier();  // (2)
+            // (3) dS -= Kt^T dX; dS' of the next chunk to LDS (every read of dS'^T is behind barrier 1)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const Fr a = fK[s];
+                fK[s] = rec_frag(recn + R::KTF + (cb * 2 + s) * R::FRAG, lane);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[nb] = mma_full(acc[nb], a, lds_frag<false, kBS, 64>(pDX, 16 * nb + m, 32 * s + 8 * cg));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, acc[nb]);
+            lds_barrier();  // (3)
+        };
+        if (nch > 0) {  // the first chunk peeled: the loop is entered only after one whole chunk
+            chunk(nch - 1);
+            for (int64_t jc = nch - 2; jc >= 0; --jc) chunk(jc);
+        }
+        if (ds0) {
+            float* d0 = ds0 + (n * H + h) * (int64_t)DK * Dv + col0;  // uniform base, small per-lane offsets
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) d0[(16 * cb + 4 * cg + jj) * Dv + 16 * nb + m] = acc[nb][jj];
+        }
     }
 }
 
@@ -891,7 +948,7 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
-    hipLaunchKernelGGL((bwd_dstates_kernel<DK, false>), dim3(chain), dim3(1024), 0, st, a.d_o, a.d_sfinal, a.ds0,
+    hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(64 * (4 + DK / 16)), 0, st, a.d_o, a.d_sfinal, a.ds0,
                        a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, dudx, a.dv);
     if (ch > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<DK, F32>), dim3((unsigned)ch), dim3(1024), 0, st, a.q, a.k, a.g, a.d_o,

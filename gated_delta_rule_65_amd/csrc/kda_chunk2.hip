@@ -227,8 +227,9 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
 }
 
 // F32: precision policy of the records (fp32 MFMA operands, else split bf16); IN_F32: q/k input type.
-// BWD: also write the backward pass's plain operands (BwdRec) to brecs, and leave out the Qt and P fragments of
-// the record (only the state-only chain reads these records).
+// BWD: also write the backward pass's operands (BwdRec: the reverse chain's fragments, the gradient kernel's
+// fp32 operands) to brecs, and leave out the Qt and P fragments of the record (only the state-only chain
+// reads these records).
 template <int DK, bool F32, bool PRO, bool IN_F32 = F32, bool BWD = false>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                       const void* __restrict__ gv, const void* __restrict__ bv,
@@ -364,42 +365,63 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
     lds_barrier();  // (2)
 
     // ---- Qt, Kt to the record; Gram factors E = e^{Gloc}, Ei = e^{-Gloc}; column operands to LDS
-    // (two exponentials per element: the sub-block offsets come from the per-channel tables)
+    // (two exponentials per element: the sub-block offsets come from the per-channel tables).
+    // Backward form: Qt^T and -Kt^T fragments too, 64 channels at a time, transposed through the P
+    // and A areas ([64][68] fp32 each, not written before the Gram products)
     float E[KS][8], Ei[KS][8];
+    constexpr int HALVES = BWD ? DK / 64 : 1;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const int c0 = 32 * s + 8 * cg;
-        float pw[8], bt[8], xq[8], xk[8], xc[8];
-        lds_read8(&tPw[w * DK + c0], pw);
-        lds_read8(&tBt[w * DK + c0], bt);
+    for (int hf = 0; hf < HALVES; ++hf) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            E[s][jj] = __builtin_amdgcn_exp2f(gl[s][jj]);
-            Ei[s][jj] = __builtin_amdgcn_exp2f(-gl[s][jj]);
-            const float gam = pw[jj] * E[s][jj];  // e^{G_r}
-            xq[jj] = qf[s][jj] * gam;
-            xk[jj] = kf[s][jj] * gam;
-            xc[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);  // k e^{G_end(w) - G_r}
-        }
-        Fr fq, fk;
-        fq.set(xq);
-        if constexpr (BWD) fk.set(xk);
-        else fk.set_hi_only(xk);
-        if constexpr (!BWD) gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);  // the state-only chain reads no Qt
-        if constexpr (R::KT_PLANES == 2) gfrag_store<F32>(rec + R::KT + (w * KS + s) * 2 * kPlane, lane, fk);
-        else gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * kPlane, lane, fk);
-        if constexpr (BWD) {  // Qt^T, Kt^T [c][r]; rows past the end as zeros
-            const float z = rv ? 1.f : 0.f;
+        for (int s = hf * (KS / HALVES); s < (hf + 1) * (KS / HALVES); ++s) {
+            const int c0 = 32 * s + 8 * cg;
+            float pw[8], bt[8], xq[8], xk[8], xc[8];
+            lds_read8(&tPw[w * DK + c0], pw);
+            lds_read8(&tBt[w * DK + c0], bt);
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
-                brec[BR::QTT + (c0 + jj) * 64 + r] = z * xq[jj];
-                brec[BR::KTT + (c0 + jj) * 64 + r] = z * xk[jj];
+                E[s][jj] = __builtin_amdgcn_exp2f(gl[s][jj]);
+                Ei[s][jj] = __builtin_amdgcn_exp2f(-gl[s][jj]);
+                const float gam = pw[jj] * E[s][jj];  // e^{G_r}
+                xq[jj] = qf[s][jj] * gam;
+                xk[jj] = kf[s][jj] * gam;
+                xc[jj] = kf[s][jj] * (bt[jj] * Ei[s][jj]);  // k e^{G_end(w) - G_r}
+            }
+            Fr fq, fk;
+            fq.set(xq);
+            if constexpr (BWD) fk.set(xk);
+            else fk.set_hi_only(xk);
+            if constexpr (!BWD) gfrag_store<F32>(rec + R::QT + (w * KS + s) * 2 * kPlane, lane, fq);  // the state-only chain reads no Qt
+            if constexpr (R::KT_PLANES == 2) gfrag_store<F32>(rec + R::KT + (w * KS + s) * 2 * kPlane, lane, fk);
+            else gfrag_store_hi<F32>(rec + R::KT + (w * KS + s) * kPlane, lane, fk);
+            if constexpr (BWD) {  // Qt^T, -Kt^T [c - 64 hf][r] (rows past the end as zeros)
+                const float z = rv ? 1.f : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    sP[(c0 + jj - 64 * hf) * 68 + r] = z * xq[jj];
+                    sA[(c0 + jj - 64 * hf) * 68 + r] = -z * xk[jj];
+                }
+            }
+            if (w < 3) {
+                float* dst = sCol + r * (DK + 4) + c0;
+                *reinterpret_cast<float4*>(dst) = make_float4(xc[0], xc[1], xc[2], xc[3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(xc[4], xc[5], xc[6], xc[7]);
             }
         }
-        if (w < 3) {
-            float* dst = sCol + r * (DK + 4) + c0;
-            *reinterpret_cast<float4*>(dst) = make_float4(xc[0], xc[1], xc[2], xc[3]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(xc[4], xc[5], xc[6], xc[7]);
+        if constexpr (BWD) {  // wave w: matrix w / 2, channel blocks 2 (w % 2) and 2 (w % 2) + 1 of the half
+            lds_barrier();  // (3a)
+            const float* stg = (w < 2) ? sP : sA;
+            char* dstb = reinterpret_cast<char*>(brec + ((w < 2) ? BR::QTF : BR::KTF));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int cbl = 2 * (w & 1) + (i >> 1), s2 = i & 1;
+                float x[8];
+                lds_read8(&stg[(16 * cbl + m) * 68 + 32 * s2 + 8 * cg], x);
+                Fr f;
+                f.set(x);
+                gfrag_store<F32>(dstb + ((4 * hf + cbl) * 2 + s2) * 2 * kPlane, lane, f);
+            }
+            if (hf + 1 < HALVES) lds_barrier();  // (3b) the next half goes over the same areas
         }
     }
     lds_barrier();  // (3)
@@ -438,8 +460,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         f.set(x);
         gfrag_store<F32>(rec + R::PM + pair_of(w, kb) * 2 * kPlane, lane, f);
     }
-    if constexpr (BWD) {
-        for (int e = tid; e < 4096; e += 256) brec[BR::PMT + e] = sP[(e & 63) * 68 + (e >> 6)];  // P^T
+    if constexpr (BWD) {  // P^T fragments of row block w: columns of P
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = sP[(32 * s2 + 8 * cg + e) * 68 + 16 * w + m];
+            Fr f;
+            f.set(x);
+            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::PTF) + (w * 2 + s2) * 2 * kPlane, lane, f);
+        }
         if (tid < kC) brec[BR::BT + tid] = sBeta[tid];
     }
     lds_barrier();  // (5)
@@ -488,11 +518,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         float bt[8], af[8];
         lds_read8(&tBt[w * DK + c0], bt);
         lds_read8(&tAf[w * DK + c0], af);
+        float kb8[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const float kbar = (kf[s][jj] * (bt[jj] * Ei[s][jj])) * af[jj];  // k e^{G_C - G_r}
             lds_store1<F32, DK, kC>(pKB, c0 + jj, r, kbar);
-            if constexpr (BWD) brec[BR::KB + r * DK + c0 + jj] = rv ? kbar : 0.f;
+            kb8[jj] = rv ? kbar : 0.f;
+        }
+        if constexpr (BWD) {  // this lane's piece of the Kb fragment (row block w, step s)
+            Fr f;
+            f.set(kb8);
+            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::KBF) + (w * KS + s) * 2 * kPlane, lane, f);
         }
     }
     lds_barrier();  // (6)
@@ -522,6 +558,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         Fr f;
         f.set(x);
         gfrag_store<F32>(rec + R::NM + pair_of(w, kb) * 2 * kPlane, lane, f);
+    }
+    if constexpr (BWD) {  // (M^{-1} Diag(b))^T fragments of row block w: columns of M^{-1} Diag(b)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = sA[(32 * s2 + 8 * cg + e) * 68 + 16 * w + m];
+            Fr f;
+            f.set(x);
+            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::NTF) + (w * 2 + s2) * 2 * kPlane, lane, f);
+        }
     }
 }
 

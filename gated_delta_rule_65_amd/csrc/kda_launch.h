@@ -91,13 +91,22 @@ int64_t chunk16_record_bytes(int Dk);
 int64_t chunk16_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_fwd16(const ChunkArgs& a, void* ws, hipStream_t st, bool allow_split);
 
-// Per (chunk, head) operands of the backward pass in plain row-major fp32 (float offsets):
-// Qt^T, Kt^T [DK][64]; Kb [64][DK]; P^T, Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1};
-// Abar [64][64]; gamma [DK]; b [64].  Transposed where the backward products contract over tokens.
-// Written by the forward preparation kernel in its backward form, read by the backward kernels.
+// Per (chunk, head) operands of the backward pass (float offsets).  The reverse state chain's operands
+// are MFMA A fragments (split bf16, FRAG floats each: a plane of 64 lanes x 16 B of bf16 hi, then
+// one of bf16 lo; lane l holds row 16*block + l%16, contracted indices 32*s + 8*(l/16) .. +7), in
+// the order [block][s]:
+//   QTF  Qt^T              rows: channels, contracted: tokens   [DK/16][2]
+//   KTF  -Kt^T             rows: channels, contracted: tokens   [DK/16][2]
+//   KBF  Kb                rows: tokens,   contracted: channels [4][DK/32]
+//   PTF  P^T               rows: tokens,   contracted: tokens   [4][2]
+//   NTF  Diag(b) Minv^T    rows: tokens,   contracted: tokens   [4][2]
+// and the gradient kernel's plain fp32 operands: Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1},
+// Abar [64][64], gamma [DK], b [64].  Written by the forward preparation kernel in its backward form.
 template <int DK>
 struct BwdRec {
-    static constexpr int QTT = 0, KTT = 64 * DK, KB = 128 * DK, PMT = 192 * DK, MIT = PMT + 4096,
+    static constexpr int FRAG = 512;
+    static constexpr int QTF = 0, KTF = QTF + (DK / 16) * 2 * FRAG, KBF = KTF + (DK / 16) * 2 * FRAG,
+                         PTF = KBF + 4 * (DK / 32) * FRAG, NTF = PTF + 8 * FRAG, MIT = NTF + 8 * FRAG,
                          AB = MIT + 4096, GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
     static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
 };
