@@ -489,6 +489,54 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
     __syncthreads();
 }
 
+// A [64][DK] fp32 token-by-channel table staged channel-major as split bf16 over its own area: a
+// plane of bf16 hi, then one of bf16 lo, each [DK][64]; the 8-byte groups of four tokens of row c
+// are swizzled by c % 16, so that sixteen consecutive rows read at one token offset hit distinct banks.
+__device__ __forceinline__ int tst_index(int c, int t) { return c * 64 + 4 * ((t >> 2) ^ (c & 15)) + (t & 3); }
+
+// Four consecutive reduction-index values of a v_mfma_f32_16x16x16_bf16 operand, split.
+struct Frag4 {
+    bf16x4_t hi, lo;
+};
+__device__ __forceinline__ Frag4 split4(float a, float b, float c, float d) {
+    const float x[4] = {a, b, c, d};
+    Frag4 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const __bf16 h = (__bf16)x[j];
+        f.hi[j] = h;
+        f.lo[j] = (__bf16)(x[j] - (float)h);
+    }
+    return f;
+}
+// acc += A * B with the split (three-pass) policy: lane l holds A[l % 16][4 (l / 16) ..] and
+// B[4 (l / 16) ..][l % 16] of the 16x16x16 product.
+__device__ __forceinline__ f32x4_t mma16(f32x4_t acc, const Frag4& a, const Frag4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+    return acc;
+}
+// Stage the EPS tokens r0 .. r0 + EPS - 1 (a multiple of four) of channel c.
+template <int DK, int EPS>
+__device__ __forceinline__ void tstage(float* base, int c, int r0, const float* x) {
+    __bf16* p = reinterpret_cast<__bf16*>(base);
+#pragma unroll
+    for (int g = 0; g < EPS / 4; ++g) {
+        const Frag4 f = split4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+        const int idx = tst_index(c, r0 + 4 * g);
+        *reinterpret_cast<bf16x4_t*>(p + idx) = f.hi;
+        *reinterpret_cast<bf16x4_t*>(p + DK * 64 + idx) = f.lo;
+    }
+}
+// Tokens t0 .. t0 + 3 (t0 a multiple of four) of channel c of a staged table.
+template <int DK>
+__device__ __forceinline__ Frag4 tfrag(const float* base, int c, int t0) {
+    const __bf16* p = reinterpret_cast<const __bf16*>(base);
+    const int idx = tst_index(c, t0);
+    return Frag4{*reinterpret_cast<const bf16x4_t*>(p + idx), *reinterpret_cast<const bf16x4_t*>(p + DK * 64 + idx)};
+}
+
 // Per (chunk, head), 1024 threads: first the sums over the value columns (colsum_to_lds), then through
 // N = Minv Diag(b) and Minv = (I + Diag(b) Abar)^{-1} to db and dAbar, then through the decayed Gram
 // blocks Abar and P, Qt, Kt, Kb and gamma to dq, dk and dG, and from G to dg.  Thread t owns row t/16
@@ -747,68 +795,77 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     __syncthreads();
 
 
-    // ---- the decayed Gram contractions on fp32 MFMA (16x16x4).  Wave wv owns the (row block R,
-    // 16-channel block cb) pairs below and, for each, three 16x16 results at rows 16R.. and
-    // channels 16cb.. (F_RR = D_R):
-    //   aq  = sum_{I <= R} F_RI o (dP[R, I] (k B1)[I])          (for dq)
-    //   ak1 = sum_{I <= R} F_RI o (dAbar[R, I] (k B1)[I])       (for dk)
-    //   ak2 = sum_{R2 >= R} F_{R2, R} o (dAbar[R2, R]^T (k A1)[R2] + dP[R2, R]^T (q A1)[R2])
-    // The decay factor depends only on the channel (the result's column), so it scales each block
-    // pair's product as a whole.  MFMA number kk takes reduction index 4 kk + lane / 16 in both
-    // operands; every pair costs 8 (R + 1) + 8 (4 - R) = 40 products.
+    // ---- the decayed Gram contractions on split-bf16 MFMA (16x16x16, three passes), as transposed
+    // results.  Wave wv owns the (row block R, 16-channel block cb) pairs below and, for each, three
+    // 16x16 results with channels 16cb.. as rows and tokens 16R.. as columns (F_RR = D_R):
+    //   aq^T  = sum_{I <= R} F_RI o ((k B1)^T[cb, I] dP[R, I]^T)                  (for dq)
+    //   ak1^T = sum_{I <= R} F_RI o ((k B1)^T[cb, I] dAbar[R, I]^T)               (for dk)
+    //   ak2^T = sum_{R2 >= R} F_{R2, R} o ((k A1)^T[cb, R2] dAbar[R2, R] + (q A1)^T[cb, R2] dP[R2, R])
+    // The decay factor depends only on the channel (the result's row), so it scales each block
+    // pair's product as a whole.  The channel-major operands (k B1, k A1, q A1 transposed) are split
+    // once and staged over sG, sk and sq; the blocks of dP and dAbar are split as they are read.
     constexpr int NCB = DK / 16, PPW = 4 * NCB / 16;  // pairs per wave
+    constexpr int EPS = 64 * DK / NT;                  // staged elements per thread
+    {
+        const int c = tid % DK, r0 = EPS * (tid / DK);
+        float xg[EPS], xk[EPS], xq[EPS];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+            xg[e] = sG[(r0 + e) * LD + c];
+            xk[e] = sk[(r0 + e) * LD + c];
+            xq[e] = sq[(r0 + e) * LD + c];
+        }
+        __syncthreads();  // every fp32 element read before the split copies go over them
+        tstage<DK, EPS>(sG, c, r0, xg);
+        tstage<DK, EPS>(sk, c, r0, xk);
+        tstage<DK, EPS>(sq, c, r0, xq);
+    }
+    __syncthreads();
     const int wv = tid >> 6, mm = tid & 15, cq = (tid >> 4) & 3;
     f32x4_t oq[PPW], ok1[PPW], ok2[PPW];
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
         const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
-        const int c = 16 * cb + mm;
-        f32x4_t aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f}, aK2 = {0.f, 0.f, 0.f, 0.f};
+        const int crow = 16 * cb + mm;    // this lane's A-operand channel
+        const int c4 = 16 * cb + 4 * cq;  // this lane's four result channels c4 .. c4 + 3
+        const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t aQ = z4, aK = z4, aK2 = z4;
 #pragma unroll 1
         for (int I = 0; I <= R; ++I) {
-            f32x4_t tq = {0.f, 0.f, 0.f, 0.f}, tk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int i = 16 * I + 4 * kk + cq;
-                const float bv = sG[i * LD + c];
-                tq = __builtin_amdgcn_mfma_f32_16x16x4f32(sM2[(16 * R + mm) * 65 + i], bv, tq, 0, 0, 0);
-                tk = __builtin_amdgcn_mfma_f32_16x16x4f32(sM1[(16 * R + mm) * 65 + i], bv, tk, 0, 0, 0);
-            }
-            const float f = I < R ? sFf[(R * (R - 1) / 2 + I) * DK + c] : sDf[R * DK + c];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                aQ[jj] = fmaf(f, tq[jj], aQ[jj]);
-                aK[jj] = fmaf(f, tk[jj], aK[jj]);
-            }
+            const Frag4 a = tfrag<DK>(sG, crow, 16 * I + 4 * cq);
+            const float* pp = sM2 + (16 * R + mm) * 65 + 16 * I + 4 * cq;
+            const float* pa = sM1 + (16 * R + mm) * 65 + 16 * I + 4 * cq;
+            const f32x4_t tq = mma16(z4, a, split4(pp[0], pp[1], pp[2], pp[3]));
+            const f32x4_t tk = mma16(z4, a, split4(pa[0], pa[1], pa[2], pa[3]));
+            const float4 f = *reinterpret_cast<const float4*>(I < R ? &sFf[(R * (R - 1) / 2 + I) * DK + c4]
+                                                                     : &sDf[R * DK + c4]);
+            aQ = f32x4_t{fmaf(f.x, tq[0], aQ[0]), fmaf(f.y, tq[1], aQ[1]), fmaf(f.z, tq[2], aQ[2]), fmaf(f.w, tq[3], aQ[3])};
+            aK = f32x4_t{fmaf(f.x, tk[0], aK[0]), fmaf(f.y, tk[1], aK[1]), fmaf(f.z, tk[2], aK[2]), fmaf(f.w, tk[3], aK[3])};
         }
 #pragma unroll 1
         for (int R2 = R; R2 < 4; ++R2) {
-            f32x4_t t2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int r = 16 * R2 + 4 * kk + cq;
-                t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sM1[r * 65 + 16 * R + mm], sk[r * LD + c], t2, 0, 0, 0);
-                t2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sM2[r * 65 + 16 * R + mm], sq[r * LD + c], t2, 0, 0, 0);
-            }
-            const float f = R2 > R ? sFf[(R2 * (R2 - 1) / 2 + R) * DK + c] : sDf[R * DK + c];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) aK2[jj] = fmaf(f, t2[jj], aK2[jj]);
+            const Frag4 ak = tfrag<DK>(sk, crow, 16 * R2 + 4 * cq), aq = tfrag<DK>(sq, crow, 16 * R2 + 4 * cq);
+            const float* pa = sM1 + (16 * R2 + 4 * cq) * 65 + 16 * R + mm;
+            const float* pp = sM2 + (16 * R2 + 4 * cq) * 65 + 16 * R + mm;
+            const f32x4_t t2 = mma16(mma16(z4, ak, split4(pa[0], pa[65], pa[130], pa[195])), aq,
+                                     split4(pp[0], pp[65], pp[130], pp[195]));
+            const float4 f = *reinterpret_cast<const float4*>(R2 > R ? &sFf[(R2 * (R2 - 1) / 2 + R) * DK + c4]
+                                                                      : &sDf[R * DK + c4]);
+            aK2 = f32x4_t{fmaf(f.x, t2[0], aK2[0]), fmaf(f.y, t2[1], aK2[1]), fmaf(f.z, t2[2], aK2[2]),
+                          fmaf(f.w, t2[3], aK2[3])};
         }
         oq[p] = aQ;
         ok1[p] = aK;
         ok2[p] = aK2;
     }
-    __syncthreads();  // every operand has been read: sq, sk, sG take the three results
+    __syncthreads();  // every operand has been read: sq, sk, sG take the three results ([token][channel])
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
         const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int e = (16 * R + 4 * cq + jj) * LD + 16 * cb + mm;
-            sq[e] = oq[p][jj];
-            sk[e] = ok1[p][jj];
-            sG[e] = ok2[p][jj];
-        }
+        const int e = (16 * R + mm) * LD + 16 * cb + 4 * cq;
+        *reinterpret_cast<float4*>(&sq[e]) = make_float4(oq[p][0], oq[p][1], oq[p][2], oq[p][3]);
+        *reinterpret_cast<float4*>(&sk[e]) = make_float4(ok1[p][0], ok1[p][1], ok1[p][2], ok1[p][3]);
+        *reinterpret_cast<float4*>(&sG[e]) = make_float4(ok2[p][0], ok2[p][1], ok2[p][2], ok2[p][3]);
     }
     __syncthreads();
     float aq[CPT], ak1[CPT], ak2[CPT];
