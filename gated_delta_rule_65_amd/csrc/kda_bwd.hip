@@ -529,6 +529,13 @@ __device__ __forceinline__ void tstage(float* base, int c, int r0, const float* 
         *reinterpret_cast<bf16x4_t*>(p + DK * 64 + idx) = f.lo;
     }
 }
+// The lower 16x16 blocks (R, I <= R; block R (R + 1) / 2 + I) of dP and dAbar staged as split bf16:
+// arrays 0, 1 hold the blocks of dP, dAbar as [row][column], arrays 2, 3 as [column][row]; each block
+// a plane of 256 bf16 hi, then 256 lo.  Row `row`, columns 4 cq .. 4 cq + 3 of block bb of array arr.
+__device__ __forceinline__ Frag4 gblk(const float* base, int arr, int bb, int row, int cq) {
+    const __bf16* p = reinterpret_cast<const __bf16*>(base) + (arr * 10 + bb) * 512 + row * 16 + 4 * cq;
+    return Frag4{*reinterpret_cast<const bf16x4_t*>(p), *reinterpret_cast<const bf16x4_t*>(p + 256)};
+}
 // Tokens t0 .. t0 + 3 (t0 a multiple of four) of channel c of a staged table.
 template <int DK>
 __device__ __forceinline__ Frag4 tfrag(const float* base, int c, int t0) {
@@ -795,18 +802,46 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     __syncthreads();
 
 
-    // ---- the decayed Gram contractions on split-bf16 MFMA (16x16x16, three passes), as transposed
-    // results.  Wave wv owns the (row block R, 16-channel block cb) pairs below and, for each, three
-    // 16x16 results with channels 16cb.. as rows and tokens 16R.. as columns (F_RR = D_R):
-    //   aq^T  = sum_{I <= R} F_RI o ((k B1)^T[cb, I] dP[R, I]^T)                  (for dq)
-    //   ak1^T = sum_{I <= R} F_RI o ((k B1)^T[cb, I] dAbar[R, I]^T)               (for dk)
-    //   ak2^T = sum_{R2 >= R} F_{R2, R} o ((k A1)^T[cb, R2] dAbar[R2, R] + (q A1)^T[cb, R2] dP[R2, R])
-    // The decay factor depends only on the channel (the result's row), so it scales each block
-    // pair's product as a whole.  The channel-major operands (k B1, k A1, q A1 transposed) are split
-    // once and staged over sG, sk and sq; the blocks of dP and dAbar are split as they are read.
+    // ---- the decayed Gram contractions on split-bf16 MFMA (16x16x16, three passes).  Wave wv owns
+    // the (row block R, 16-channel block cb) pairs below and, for each, three 16x16 results at rows
+    // 16R.. and channels 16cb.. (F_RR = D_R):
+    //   aq  = sum_{I <= R} F_RI o (dP[R, I] (k B1)[I])                             (for dq)
+    //   ak1 = sum_{I <= R} F_RI o (dAbar[R, I] (k B1)[I])                          (for dk)
+    //   ak2 = sum_{R2 >= R} F_{R2, R} o (dAbar[R2, R]^T (k A1)[R2] + dP[R2, R]^T (q A1)[R2])
+    // The decay factor depends only on the channel (the result's column), so it scales each block
+    // pair's product as a whole.  Every operand is split once and staged with the reduction index
+    // innermost: k B1, k A1, q A1 as [channel][token] over sG, sk, sq; the ten lower 16x16 blocks of
+    // dP and dAbar, as they are and transposed, over sM1 .. sM3 (gblk).
     constexpr int NCB = DK / 16, PPW = 4 * NCB / 16;  // pairs per wave
-    constexpr int EPS = 64 * DK / NT;                  // staged elements per thread
+    constexpr int EPS = 64 * DK / NT;                  // staged table elements per thread
+    constexpr int NBI = 4 * 10 * 64;                   // block pieces: (array, block, row, four columns)
+    static_assert(4 * 10 * 1024 <= 3 * 65 * 64 * 4, "the staged blocks fit sM1 .. sM3");
     {
+        float xb[3][4];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int it = tid + u * NT;
+            if (it < NBI) {
+                const int arr = it / 640, bb = (it >> 6) % 10, rr = (it >> 2) & 15, g = it & 3;
+                const int R = bb >= 6 ? 3 : (bb >= 3 ? 2 : (bb >= 1 ? 1 : 0)), I = bb - R * (R + 1) / 2;
+                const float* src = (arr & 1) ? sM1 : sM2;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xb[u][j] = arr < 2 ? src[(16 * R + rr) * 65 + 16 * I + 4 * g + j]
+                                       : src[(16 * R + 4 * g + j) * 65 + 16 * I + rr];
+            }
+        }
+        __syncthreads();  // dP and dAbar read before their blocks go over them
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int it = tid + u * NT;
+            if (it < NBI) {
+                const Frag4 f = split4(xb[u][0], xb[u][1], xb[u][2], xb[u][3]);
+                __bf16* d = reinterpret_cast<__bf16*>(sM1) + (it >> 6) * 512 + ((it >> 2) & 15) * 16 + 4 * (it & 3);
+                *reinterpret_cast<bf16x4_t*>(d) = f.hi;
+                *reinterpret_cast<bf16x4_t*>(d + 256) = f.lo;
+            }
+        }
         const int c = tid % DK, r0 = EPS * (tid / DK);
         float xg[EPS], xk[EPS], xq[EPS];
 #pragma unroll
@@ -815,7 +850,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
             xk[e] = sk[(r0 + e) * LD + c];
             xq[e] = sq[(r0 + e) * LD + c];
         }
-        __syncthreads();  // every fp32 element read before the split copies go over them
+        __syncthreads();  // every fp32 table element read before the split copies go over them
         tstage<DK, EPS>(sG, c, r0, xg);
         tstage<DK, EPS>(sk, c, r0, xk);
         tstage<DK, EPS>(sq, c, r0, xq);
@@ -826,33 +861,30 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
         const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
-        const int crow = 16 * cb + mm;    // this lane's A-operand channel
-        const int c4 = 16 * cb + 4 * cq;  // this lane's four result channels c4 .. c4 + 3
+        const int c = 16 * cb + mm;  // this lane's result channel and B-operand channel
         const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
         f32x4_t aQ = z4, aK = z4, aK2 = z4;
 #pragma unroll 1
         for (int I = 0; I <= R; ++I) {
-            const Frag4 a = tfrag<DK>(sG, crow, 16 * I + 4 * cq);
-            const float* pp = sM2 + (16 * R + mm) * 65 + 16 * I + 4 * cq;
-            const float* pa = sM1 + (16 * R + mm) * 65 + 16 * I + 4 * cq;
-            const f32x4_t tq = mma16(z4, a, split4(pp[0], pp[1], pp[2], pp[3]));
-            const f32x4_t tk = mma16(z4, a, split4(pa[0], pa[1], pa[2], pa[3]));
-            const float4 f = *reinterpret_cast<const float4*>(I < R ? &sFf[(R * (R - 1) / 2 + I) * DK + c4]
-                                                                     : &sDf[R * DK + c4]);
-            aQ = f32x4_t{fmaf(f.x, tq[0], aQ[0]), fmaf(f.y, tq[1], aQ[1]), fmaf(f.z, tq[2], aQ[2]), fmaf(f.w, tq[3], aQ[3])};
-            aK = f32x4_t{fmaf(f.x, tk[0], aK[0]), fmaf(f.y, tk[1], aK[1]), fmaf(f.z, tk[2], aK[2]), fmaf(f.w, tk[3], aK[3])};
+            const int bb = R * (R + 1) / 2 + I;
+            const Frag4 b = tfrag<DK>(sG, c, 16 * I + 4 * cq);
+            const f32x4_t tq = mma16(z4, gblk(sM1, 0, bb, mm, cq), b);
+            const f32x4_t tk = mma16(z4, gblk(sM1, 1, bb, mm, cq), b);
+            const float f = I < R ? sFf[(R * (R - 1) / 2 + I) * DK + c] : sDf[R * DK + c];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                aQ[jj] = fmaf(f, tq[jj], aQ[jj]);
+                aK[jj] = fmaf(f, tk[jj], aK[jj]);
+            }
         }
 #pragma unroll 1
         for (int R2 = R; R2 < 4; ++R2) {
-            const Frag4 ak = tfrag<DK>(sk, crow, 16 * R2 + 4 * cq), aq = tfrag<DK>(sq, crow, 16 * R2 + 4 * cq);
-            const float* pa = sM1 + (16 * R2 + 4 * cq) * 65 + 16 * R + mm;
-            const float* pp = sM2 + (16 * R2 + 4 * cq) * 65 + 16 * R + mm;
-            const f32x4_t t2 = mma16(mma16(z4, ak, split4(pa[0], pa[65], pa[130], pa[195])), aq,
-                                     split4(pp[0], pp[65], pp[130], pp[195]));
-            const float4 f = *reinterpret_cast<const float4*>(R2 > R ? &sFf[(R2 * (R2 - 1) / 2 + R) * DK + c4]
-                                                                      : &sDf[R * DK + c4]);
-            aK2 = f32x4_t{fmaf(f.x, t2[0], aK2[0]), fmaf(f.y, t2[1], aK2[1]), fmaf(f.z, t2[2], aK2[2]),
-                          fmaf(f.w, t2[3], aK2[3])};
+            const int bb = R2 * (R2 + 1) / 2 + R;
+            const f32x4_t t2 = mma16(mma16(z4, gblk(sM1, 3, bb, mm, cq), tfrag<DK>(sk, c, 16 * R2 + 4 * cq)),
+                                     gblk(sM1, 2, bb, mm, cq), tfrag<DK>(sq, c, 16 * R2 + 4 * cq));
+            const float f = R2 > R ? sFf[(R2 * (R2 - 1) / 2 + R) * DK + c] : sDf[R * DK + c];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) aK2[jj] = fmaf(f, t2[jj], aK2[jj]);
         }
         oq[p] = aQ;
         ok1[p] = aK;
@@ -862,10 +894,13 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
 #pragma unroll
     for (int p = 0; p < PPW; ++p) {
         const int cb = wv % NCB, R = wv / NCB + p * (16 / NCB);
-        const int e = (16 * R + mm) * LD + 16 * cb + 4 * cq;
-        *reinterpret_cast<float4*>(&sq[e]) = make_float4(oq[p][0], oq[p][1], oq[p][2], oq[p][3]);
-        *reinterpret_cast<float4*>(&sk[e]) = make_float4(ok1[p][0], ok1[p][1], ok1[p][2], ok1[p][3]);
-        *reinterpret_cast<float4*>(&sG[e]) = make_float4(ok2[p][0], ok2[p][1], ok2[p][2], ok2[p][3]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int e = (16 * R + 4 * cq + jj) * LD + 16 * cb + mm;
+            sq[e] = oq[p][jj];
+            sk[e] = ok1[p][jj];
+            sG[e] = ok2[p][jj];
+        }
     }
     __syncthreads();
     float aq[CPT], ak1[CPT], ak2[CPT];
