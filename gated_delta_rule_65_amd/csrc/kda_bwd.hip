@@ -24,10 +24,10 @@
 // MFMA fragments, the gradient kernel's Minv, Abar, gamma, b in fp32, and the state at every chunk
 // start come from the forward pass's prep kernel in its backward form and its chain kernel in mode 3,
 // on split-bf16 records with every product in three passes (launch_chunk_states).  Then two kernels, fp32
-// accumulation (the reverse chain and the column sums as three-pass split-bf16 products, the rest of the
-// gradient kernel on fp32 MFMA):
-//   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS', dU, dX of every
-//                      chunk, dv = dX, ds0
+// accumulation (the reverse chain, the column sums and the decayed Gram contractions as three-pass
+// split-bf16 products, the products through the inverse on fp32 MFMA):
+//   bwd_dstates_kernel per (sequence, head, 32 state columns), chunks in reverse: dS' and dU of every
+//                      chunk, dv = dX (which the gradient kernel reads back), ds0
 //   bwd_grad_kernel    per (chunk, head): the sums over value columns (dQt, dKt, dKb, dP, dN, dgamma),
 //                      kept in LDS, then through the inverse, the decayed Gram blocks and the gates
 #include <type_traits>
@@ -156,7 +156,7 @@ template <int DK>
 __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
     const float* __restrict__ d_o, const float* __restrict__ d_sfinal, float* ds0, const int32_t* __restrict__ cu,
     int64_t T_fixed, int64_t total, int64_t N, int H, int Dv, const float* __restrict__ recs,
-    float* __restrict__ dstates, float* __restrict__ dudx, float* __restrict__ dv) {
+    float* __restrict__ dstates, float* __restrict__ du, float* __restrict__ dv, float* __restrict__ trash) {
     using R = BRec<DK>;
     using Fr = Frag<false>;
     using MOT = LMat<false, kBS, 64>;  // dO^T, dU^T, dX^T [j][r]
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, aX[nb]);
-            float* du_o = dudx + (slot * H + h) * 128 * (int64_t)Dv + col0 + m;
+            float* du_o = du + (slot * H + h) * 64 * (int64_t)Dv + col0 + m;
             float* dv_o = dv + (t0 * H + h) * (int64_t)Dv + col0 + m;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -261,10 +261,8 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
                     st_nt(&du_o[i * (int64_t)Dv + 16 * nb], aU[nb][jj]);
-                    st_nt(&du_o[(64 + i) * (int64_t)Dv + 16 * nb], aX[nb][jj]);
-                    // rows past the end store dX a second time over its own dudx entry
-                    st_nt(i < nt ? &dv_o[i * (int64_t)H * Dv + 16 * nb] : &du_o[(64 + i) * (int64_t)Dv + 16 * nb],
-                          aX[nb][jj]);
+                    // rows past the end (zero: b vanishes there) go to the trash row, never read
+                    st_nt(i < nt ? &dv_o[i * (int64_t)H * Dv + 16 * nb] : &trash[col0 + 16 * nb + m], aX[nb][jj]);
                 }
             }
             lds_barrier();  // (2)
@@ -383,14 +381,13 @@ template <int DK>
 __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int64_t t0, int nt, int H, int h,
                                               int Dv, const float* __restrict__ S, const float* __restrict__ dS,
                                               const float* __restrict__ X, const float* __restrict__ dU,
-                                              const float* __restrict__ gam, float* sq, float* sk, float* sG,
+                                              const float* __restrict__ dv, const float* __restrict__ gam, float* sq, float* sk, float* sG,
                                               float* sM1, float* sM3, float* sGam, int tid) {
     using MS = LMat<false, DK, 32>;  // S, dS' column step [c][n]
     using MR = LMat<false, 64, 32>;  // U, X, dO, dX, dU column step [t][n]
     constexpr int LD = DK + 4;
     constexpr int CB = DK / 16;
     const float* U = X + 64 * (int64_t)Dv;
-    const float* dX = dU + 64 * (int64_t)Dv;
     char* pS = reinterpret_cast<char*>(sq);
     char* pD = pS + MS::BYTES;
     char* pU = pD + MS::BYTES;
@@ -402,13 +399,14 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
     const int rb = w & 3, role = w >> 2;
     // staging pieces of four values, columns 4 (tid % 8) of the step: S and dS' row tid / 8 (threads
     // below 8 DK); row (tid % 512) / 8 of U or X (threads below / from 512) and of dO or dX (likewise);
-    // dU row tid / 8 (threads below 512).  dO rows past the end read the last token and count as zero.
+    // dU row tid / 8 (threads below 512).  dO and dX (= dv, written by the reverse chain) rows past the
+    // end read the last token and count as zero.
     const bool hasS = tid < 8 * DK, lo = tid < 512;
     const int srow = tid >> 3, scol = 4 * (tid & 7), urow = (tid & 511) >> 3;
     const float gam_row = hasS && (tid & 7) == 0 ? gam[srow] : 0.f;  // gamma of row srow, for its writer
     const float* UX = lo ? U : X;
-    const float* OD = lo ? d_o + ((t0 + min(urow, nt - 1)) * H + h) * (int64_t)Dv - urow * (int64_t)Dv : dX;
-    const float omask = lo && urow >= nt ? 0.f : 1.f;
+    const float* OD = (lo ? d_o : dv) + ((t0 + min(urow, nt - 1)) * H + h) * (int64_t)Dv - urow * (int64_t)Dv;
+    const float omask = urow >= nt ? 0.f : 1.f;
     char* pUX = lo ? pU : pX;
     char* pOD = lo ? pO : pDX;
     float4 vS = make_float4(0.f, 0.f, 0.f, 0.f), vD = vS, vR = vS, vO = vS, vW = vS;
@@ -559,7 +557,8 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
                                                            const float* __restrict__ states,
                                                            const float* __restrict__ dstates,
                                                            const float* __restrict__ xu,
-                                                           const float* __restrict__ dudx,
+                                                           const float* __restrict__ du,
+                                                           const float* __restrict__ dv,
                                                            float* __restrict__ dq, float* __restrict__ dk,
                                                            float* __restrict__ dg, float* __restrict__ dbeta) {
     using R = BRec<DK>;
@@ -601,7 +600,7 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
 
     // ---- the sums over the value columns, into LDS
     colsum_to_lds<DK>(d_o, t0, nt, H, h, Dv, states + ch * DK * (int64_t)Dv, dstates + ch * DK * (int64_t)Dv,
-                      xu + ch * 128 * (int64_t)Dv, dudx + ch * 128 * (int64_t)Dv, rec + R::GM, sq, sk, sG, sM1, sM3,
+                      xu + ch * 128 * (int64_t)Dv, du + ch * 64 * (int64_t)Dv, dv, rec + R::GM, sq, sk, sG, sM1, sM3,
                       sGd, tid);
     // this thread's pieces of them: dN and dP elements as in the loads above, and its own elements of
     // dQt, dKt, dKb (row tid / 16, channels (tid % 16) DK / 16 ..)
@@ -1012,10 +1011,11 @@ static int64_t bwd_rec_floats(int Dk) { return Dk == 128 ? BRec<128>::FLOATS : B
 // the state recompute's fragment records, in floats (their bytes are a multiple of 256)
 static int64_t bwd_frag_floats(int Dk) { return chunk_states_record_bytes(Dk) / 4; }
 
-// [records][states][state gradients][fragment records][X, U][dU, dX], each per (slot, head)
+// [records][states][state gradients][fragment records][X, U][dU], each per (slot, head), then one trash
+// row of Dv floats (256-byte granules) for the reverse chain's stores past the end of a sequence
 int64_t bwd_workspace_bytes(const BwdArgs& a) {
-    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_frag_floats(a.Dk) + 4 * 64 * (int64_t)a.Dv;
-    return bwd_slots(a) * a.H * per * 4;
+    const int64_t per = bwd_rec_floats(a.Dk) + 2 * (int64_t)a.Dk * a.Dv + bwd_frag_floats(a.Dk) + 3 * 64 * (int64_t)a.Dv;
+    return bwd_slots(a) * a.H * per * 4 + (4 * (int64_t)a.Dv + 255) / 256 * 256;
 }
 
 
@@ -1027,7 +1027,8 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     float* dstates = states + ch * (int64_t)DK * a.Dv;
     float* frecs = dstates + ch * (int64_t)DK * a.Dv;
     float* xu = frecs + ch * bwd_frag_floats(DK);
-    float* dudx = xu + ch * 128 * (int64_t)a.Dv;
+    float* du = xu + ch * 128 * (int64_t)a.Dv;
+    float* trash = du + ch * 64 * (int64_t)a.Dv;
     const int64_t items = a.N * (int64_t)a.H;
     const int NS = a.Dv / kBS;
     const unsigned chain = (unsigned)(((items + 7) / 8) * 8 * NS);
@@ -1041,10 +1042,10 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, void* ws, hipStream_t st) {
     }
     // with no chunks at all this only passes d_sfinal (or zeros) through to ds0
     hipLaunchKernelGGL((bwd_dstates_kernel<DK>), dim3(chain), dim3(64 * (4 + DK / 16)), 0, st, a.d_o, a.d_sfinal, a.ds0,
-                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, dudx, a.dv);
+                       a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, dstates, du, a.dv, trash);
     if (ch > 0) {
         hipLaunchKernelGGL((bwd_grad_kernel<DK, F32>), dim3((unsigned)ch), dim3(1024), 0, st, a.q, a.k, a.g, a.d_o,
-                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, states, dstates, xu, dudx, a.dq,
+                           a.cu_seqlens, a.T_fixed, a.total, a.N, a.H, a.Dv, recs, states, dstates, xu, du, a.dv, a.dq,
                            a.dk, a.dg, a.dbeta);
     }
     return hipGetLastError();

@@ -221,6 +221,23 @@ def test_varlen_workspace_size(N, total, H, Dk, dtype):
                                                                         + order)
 
 
+def bwd_workspace_bytes(records, Dk, Dv):
+    # the backward's workspace formula as the header states it: per record 4 (386 Dk + 22592 + 2 Dk Dv
+    # + 192 Dv) bytes, plus one trash row of Dv floats in 256-byte granules
+    return records * 4 * (386 * Dk + 22592 + 2 * Dk * Dv + 192 * Dv) + -(-(4 * Dv) // 256) * 256
+
+
+@pytest.mark.parametrize("B,T,H,Dk,Dv", [(4, 8192, 16, 128, 128), (2, 200, 3, 64, 64), (1, 65, 2, 128, 64),
+                                         (3, 100, 2, 64, 128), (1, 1, 1, 128, 64)])
+def test_backward_workspace_size(B, T, H, Dk, Dv):
+    assert kda.chunk_bwd_workspace_bytes(B, T, H, Dk, Dv) == bwd_workspace_bytes(B * -(-T // 64) * H, Dk, Dv)
+
+
+@pytest.mark.parametrize("N,total,H,Dk", [(2, 100, 2, 128), (32, 65536, 16, 128), (3, 7, 1, 64)])
+def test_varlen_backward_workspace_size(N, total, H, Dk):
+    assert kda.varlen_bwd_workspace_bytes(N, total, H, Dk, 128) == bwd_workspace_bytes((total // 64 + N) * H, Dk, 128)
+
+
 def test_workspace_size_of_unsupported_or_empty_is_zero():
     assert kda.chunk_workspace_bytes(0, 64, 1, 128, 128) == 0
     assert kda.chunk_workspace_bytes(1, 0, 1, 128, 128) == 0
