@@ -146,9 +146,11 @@ __device__ __forceinline__ Frag<false> rec_frag(const float* p, int lane) {
 // straight from the record into registers, one chunk ahead (each a contiguous 1 KiB request per
 // plane), so each record is read once per workgroup and the products take only the operands shared
 // between waves from LDS: dO^T, dS'^T, dU^T, dX^T.  Three barriers per chunk:
-//   (1) U: dU -> LDS                        S: dS = Diag(gamma) dS' + Qt^T dO
-//   (2) U: dX -> LDS; dU, dX and dv to memory
-//   (3) U: dO^T of the next chunk -> LDS    S: dS -= Kt^T dX; dS' of the next chunk -> LDS
+//   (1) U: dU -> LDS                        S: dS' to memory; dS = Diag(gamma) dS' + Qt^T dO
+//   (2) U: dX -> LDS
+//   (3) U: dU, dv = dX to memory;           S: dS -= Kt^T dX; dS' of the next chunk -> LDS
+//          dO^T of the next chunk -> LDS
+// The results also pass through fp32 tiles in LDS, so that each goes to memory as whole 128-byte rows.
 // Every chunk issues the same memory instructions in the same order (the loads past either end
 // are clamped to an existing chunk, never skipped, and the first chunk is peeled off the loop), so
 // the compiler's wait counts are exact and no wait for a load also waits for a store.
@@ -162,11 +164,15 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
     using MOT = LMat<false, kBS, 64>;  // dO^T, dU^T, dX^T [j][r]
     using MDS = LMat<false, kBS, DK>;  // dS'^T [j][c]
     constexpr int KS = DK / 32;
-    __shared__ __align__(16) char smem[3 * MOT::BYTES + MDS::BYTES];
+    constexpr int FS = kBS + 4;  // fp32 row stride of the tiles on their way to memory
+    __shared__ __align__(16) char smem[3 * MOT::BYTES + MDS::BYTES + (DK + 128) * FS * 4];
     char* pOT = smem;
     char* pDU = smem + MOT::BYTES;
     char* pDX = smem + 2 * MOT::BYTES;
     char* pDS = smem + 3 * MOT::BYTES;
+    float* fDS = reinterpret_cast<float*>(smem + 3 * MOT::BYTES + MDS::BYTES);  // dS' [DK][FS] fp32
+    float* fDU = fDS + DK * FS;                                                 // dU [64][FS]
+    float* fDX = fDU + 64 * FS;                                                 // dX [64][FS]
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     int64_t pr;
@@ -239,9 +245,13 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
                     aU[nb] = mma_full(aU[nb], a, lds_frag<false, kBS, DK>(pDS, 16 * nb + m, 32 * s + 8 * cg));
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, 64>(pDU, 16 * nb + m, 16 * rb + 4 * cg, aU[nb]);
+            for (int nb = 0; nb < 2; ++nb) {
+                lds_store4<false, kBS, 64>(pDU, 16 * nb + m, 16 * rb + 4 * cg, aU[nb]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) fDU[(16 * rb + 4 * cg + jj) * FS + 16 * nb + m] = aU[nb][jj];
+            }
             lds_barrier();  // (1)
-            // (2) dX = N^T dU; dU, dX of the chunk and dv = dX to memory
+            // (2) dX = N^T dU
             f32x4_t aX[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -252,21 +262,23 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
                     aX[nb] = mma_full(aX[nb], a, lds_frag<false, kBS, 64>(pDU, 16 * nb + m, 32 * s + 8 * cg));
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, aX[nb]);
-            float* du_o = du + (slot * H + h) * 64 * (int64_t)Dv + col0 + m;
-            float* dv_o = dv + (t0 * H + h) * (int64_t)Dv + col0 + m;
+            for (int nb = 0; nb < 2; ++nb) {
+                lds_store4<false, kBS, 64>(pDX, 16 * nb + m, 16 * rb + 4 * cg, aX[nb]);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * rb + 4 * cg + jj;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    st_nt(&du_o[i * (int64_t)Dv + 16 * nb], aU[nb][jj]);
-                    // rows past the end (zero: b vanishes there) go to the trash row, never read
-                    st_nt(i < nt ? &dv_o[i * (int64_t)H * Dv + 16 * nb] : &trash[col0 + 16 * nb + m], aX[nb][jj]);
-                }
+                for (int jj = 0; jj < 4; ++jj) fDX[(16 * rb + 4 * cg + jj) * FS + 16 * nb + m] = aX[nb][jj];
             }
             lds_barrier();  // (2)
-            // (3) dO^T of the next chunk (every read of this chunk's dO^T is behind barrier 1)
+            // (3) dU and dX = dv of the chunk to memory, whole 128-byte rows (eight lanes a row); dO^T of
+            // the next chunk (every read of this chunk's dO^T is behind barrier 1)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int i = (tid >> 3) + 32 * hh, c4 = 4 * (tid & 7);
+                const float4 u = *reinterpret_cast<const float4*>(&fDU[i * FS + c4]);
+                const float4 x = *reinterpret_cast<const float4*>(&fDX[i * FS + c4]);
+                st_nt4(du + ((slot * H + h) * 64 + i) * (int64_t)Dv + col0 + c4, u.x, u.y, u.z, u.w);
+                // rows past the end (zero: b vanishes there) go to the trash row, never read
+                st_nt4(i < nt ? dv + ((t0 + i) * H + h) * (int64_t)Dv + col0 + c4 : trash + col0 + c4, x.x, x.y, x.z, x.w);
+            }
             stage_o();
             load_o(jc > 1 ? jc - 2 : 0);
             lds_barrier();  // (3)
@@ -289,6 +301,8 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
                                                   16 * nb + m]
                                        : 0.f;
             lds_store4<false, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, acc[nb]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) fDS[(16 * cb + 4 * cg + jj) * FS + 16 * nb + m] = acc[nb][jj];
         }
         if (nch > 0) {
             const float* rec = rec_of(nch - 1);
@@ -303,12 +317,13 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
         auto chunk = [&](int64_t jc) {
             const float* recn = rec_of(jc > 0 ? jc - 1 : 0);
             const int64_t slot = bslot(cu, n, jc, T_fixed, sr.start);
-            // dS' of this chunk (the gradient at its end) to memory
-            float* dst = dstates + (slot * H + h) * (int64_t)DK * Dv + col0 + m;
+            // dS' of this chunk (the gradient at its end) to memory, whole 128-byte rows from its fp32 tile
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) st_nt(&dst[(16 * cb + 4 * cg + jj) * (int64_t)Dv + 16 * nb], acc[nb][jj]);
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c = ((tid - 256) >> 3) + (DK / 2) * hh, c4 = 4 * (tid & 7);
+                const float4 d = *reinterpret_cast<const float4*>(&fDS[c * FS + c4]);
+                st_nt4(dstates + ((slot * H + h) * DK + c) * (int64_t)Dv + col0 + c4, d.x, d.y, d.z, d.w);
+            }
             // (1) dS = Diag(gamma) dS' + Qt^T dO
             const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
@@ -336,7 +351,11 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
                     acc[nb] = mma_full(acc[nb], a, lds_frag<false, kBS, 64>(pDX, 16 * nb + m, 32 * s + 8 * cg));
             }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) lds_store4<false, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, acc[nb]);
+            for (int nb = 0; nb < 2; ++nb) {
+                lds_store4<false, kBS, DK>(pDS, 16 * nb + m, 16 * cb + 4 * cg, acc[nb]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) fDS[(16 * cb + 4 * cg + jj) * FS + 16 * nb + m] = acc[nb][jj];
+            }
             lds_barrier();  // (3)
         };
         if (nch > 0) {  // the first chunk peeled: the loop is entered only after one whole chunk
