@@ -584,6 +584,11 @@ struct ChainLds {
     static constexpr int O = U + MX::BYTES;     // fp32 output rows [64][kS + 4] on their way to HBM
     static constexpr int V = O + 64 * (kS + 4) * 4;  // v rows [64][kS] (input type) on their way from HBM
     static constexpr int TOTAL = V + 64 * kS * 4;
+    // mode 3 (state only): X rows over O, then U rows [64][kS + 4] and the chunk-start state rows
+    // [DK][kS + 4], fp32, on their way to HBM as whole 128-byte rows
+    static constexpr int FU = TOTAL;
+    static constexpr int FS = FU + 64 * (kS + 4) * 4;
+    static constexpr int TOTAL_ST = FS + DK * (kS + 4) * 4;
 };
 
 // Operands of one chunk for one wave of the chain kernel.  A state wave (row block rb) holds the rows
@@ -628,12 +633,16 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     constexpr int VPL = 16 / (int)sizeof(In);       // v values per 16-byte lane load
     const In* __restrict__ v = static_cast<const In*>(vv);
 
-    __shared__ __align__(16) char smem[L::TOTAL];
+    __shared__ __align__(16) char smem[ST ? L::TOTAL_ST : L::TOTAL];
     char* pS = smem + L::S;
     char* pX = smem + L::X;
     char* pU = smem + L::U;
     float* sO = reinterpret_cast<float*>(smem + L::O);
     In* sV = reinterpret_cast<In*>(smem + L::V);
+    constexpr int FLD = kS + 4;  // row stride of the mode-3 fp32 tiles
+    float* fX = reinterpret_cast<float*>(smem + L::O);  // mode 3 only (SO: no output rows)
+    float* fU = reinterpret_cast<float*>(smem + (ST ? L::FU : 0));
+    float* fS = reinterpret_cast<float*>(smem + (ST ? L::FS : 0));
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, cg = lane >> 4;
     const int rb = w & 3;
@@ -699,6 +708,15 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
+    auto tile_state = [&]() {  // mode 3: this wave's S tiles to the fp32 state rows
+        if constexpr (ST) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) fS[(16 * cbw + 4 * cg + jj) * FLD + 16 * nbt(i) + m] = accS[i][jj];
+        }
+    };
+    tile_state();
 
     auto record = [&](int64_t jc) -> const char* {
         return ws + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * R::BYTES;
@@ -729,6 +747,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     auto store_state = [&]() {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
+        tile_state();
     };
     auto read_u = [&](Fr (&uf)[2][2]) {
 #pragma unroll
@@ -741,15 +760,30 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
         for (int kb = 0; kb < 2; ++kb) fKB[kb] = gfrag_load<F32>(rec + R::KB + (cbw * 2 + kb) * 2 * kPlane, lane);
         gC = *reinterpret_cast<const float4*>(rec + R::GC + (16 * cbw + 4 * cg) * 4);
     };
-    auto store_start_state = [&](int64_t jc) {  // mode 3: the state at the start of chunk jc
-        if constexpr (ST) {
-            float* sj = cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0;
+    // mode 3, every thread: rows of a staged fp32 tile to memory, eight lanes per 128-byte row
+    // (ROWS a multiple of 64: unrolled, so that the compiler counts every store)
+    auto store_rows = [&](float* dst, const float* tile, auto rows) {
+        constexpr int ROWS = decltype(rows)::value;
+        static_assert(ROWS % (kChainThreads / 8) == 0, "whole passes");
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    sj[(16 * cbw + 4 * cg + jj) * (int64_t)Dv + 16 * nbt(i) + m] = accS[i][jj];
+        for (int k = 0; k < ROWS / (kChainThreads / 8); ++k) {
+            const int r = (tid >> 3) + k * (kChainThreads / 8);
+            const float4 x = *reinterpret_cast<const float4*>(&tile[r * FLD + 4 * (tid & 7)]);
+            st_nt4(dst + r * (int64_t)Dv + 4 * (tid & 7), x.x, x.y, x.z, x.w);
         }
+    };
+    auto store_start_state = [&](int64_t jc) {  // mode 3: the state at the start of chunk jc
+        if constexpr (ST)
+            store_rows(cm.sx + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * (int64_t)DK * Dv + col0, fS, std::integral_constant<int, DK>{});
+    };
+    auto store_x = [&](int64_t jc) {  // mode 3: X rows of chunk jc (staged in phase 1)
+        if constexpr (ST)
+            store_rows(cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0, fX, std::integral_constant<int, 64>{});
+    };
+    auto store_u = [&](int64_t jc) {  // mode 3: U rows of chunk jc (staged in phase 2)
+        if constexpr (ST)
+            store_rows(cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) * (int64_t)Dv + col0,
+                       fU, std::integral_constant<int, 64>{});
     };
 
     if (w < 4) {
@@ -808,12 +842,11 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                     xv[jj] = vscale * vj - accX[nb][jj];
                 }
                 lds_store4<F32, kS, kC>(pX, 16 * nb + m, 16 * rb + 4 * cg, xv);
-                if constexpr (ST) {
-                    float* xo = cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0;
+                if constexpr (ST) {  // rows past the end stored as zeros
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int row = 16 * rb + 4 * cg + jj;
-                        xo[row * (int64_t)Dv + 16 * nb + m] = row < nt ? xv[jj] : 0.f;
+                        fX[row * FLD + 16 * nb + m] = row < nt ? xv[jj] : 0.f;
                     }
                 }
             }
@@ -822,6 +855,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
 #pragma unroll
             for (int s = 0; s < KS; ++s) load_k(nxt, recn, s);
             lds_barrier();  // (1)
+            store_x(jc);
 
             // ---- phase 2:  U = M^{-1} Diag(b) X
             f32x4_t accU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -836,14 +870,13 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
             for (int nb = 0; nb < 2; ++nb) {
                 lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * rb + 4 * cg, accU[nb]);
                 if constexpr (ST) {
-                    float* uo = cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) *
-                                            (int64_t)Dv + col0;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) uo[(16 * rb + 4 * cg + jj) * (int64_t)Dv + 16 * nb + m] = accU[nb][jj];
+                    for (int jj = 0; jj < 4; ++jj) fU[(16 * rb + 4 * cg + jj) * FLD + 16 * nb + m] = accU[nb][jj];
                 }
             }
             load_nv(nxt, recn, jn);  // after the products that read this chunk's M^{-1} rows
             lds_barrier();  // (2)
+            store_u(jc);
 
             // ---- phase 3:  S tiles
             Fr uf[2][2];
@@ -920,6 +953,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                 if (jc > jbeg) store_o(chunk_start(jc) - kC, kC);
             }
             lds_barrier();  // (1)
+            store_x(jc);
 
             // ---- phase 2:  second half of the channels (S is rewritten only in phase 3)
             if constexpr (!SO) {
@@ -932,6 +966,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                 }
             }
             lds_barrier();  // (2)
+            store_u(jc);
 
             // ---- phase 3:  O += P U, S tiles
             Fr uf[2][2];
