@@ -435,7 +435,7 @@ def measure_backward(args, torch, kda, kda_inputs, device_inputs):
             "kernel_ms_min": k_min,
             "tokens_per_s": B * T / (k_ms * 1e-3), "achieved": alg / (k_ms * 1e-3) / 1e9, "unit": "GB/s",
             "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes_per_launch": alg,
-            "workspace_bytes": ws.numel(), "traffic": measured_traffic(name + "_backward"), "arith": "fp32 accumulation; split-bf16 three-pass products in the state recompute, the reverse chain and the column sums, fp32 MFMA elsewhere"}
+            "workspace_bytes": ws.numel(), "traffic": measured_traffic(name + "_backward"), "arith": "fp32 accumulation; split-bf16 three-pass products in the state recompute, the reverse chain, the column sums and the decayed Gram contractions, fp32 MFMA through the inverse"}
 
 
 if __name__ == "__main__":
