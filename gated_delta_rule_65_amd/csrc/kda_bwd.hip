@@ -22,7 +22,8 @@
 //
 // Per (chunk, head), the reverse chain's operands Qt^T, -Kt^T, Kb, P^T, (Minv Diag(b))^T as split-bf16
 // MFMA fragments, the gradient kernel's Minv, Abar, gamma, b in fp32, and the state at every chunk
-// start come from the forward pass's prep kernel in its backward form and its chain kernel in mode 3,
+// start and X, U of every chunk come from the forward pass's prep kernel in its backward form and its
+// chain kernel in mode 3,
 // on split-bf16 records with every product in three passes (launch_chunk_states).  Then two kernels, fp32
 // accumulation (the reverse chain, the column sums and the decayed Gram contractions as three-pass
 // split-bf16 products, the products through the inverse on fp32 MFMA):
