@@ -212,11 +212,11 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
         if (nch > 0) {
             const float* rec = rec_of(nch - 1);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) fP[s] = rec_frag(rec + R::PTF + (rb * 2 + s) * R::FRAG, lane);
+            for (int s = 0; s < 2; ++s) fP[s] = rec_frag(rec + R::PTF + R::tri(rb, s) * R::FRAG, lane);
 #pragma unroll
             for (int s = 0; s < KS; ++s) fK[s] = rec_frag(rec + R::KBF + (rb * KS + s) * R::FRAG, lane);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) fN[s] = rec_frag(rec + R::NTF + (rb * 2 + s) * R::FRAG, lane);
+            for (int s = 0; s < 2; ++s) fN[s] = rec_frag(rec + R::NTF + R::tri(rb, s) * R::FRAG, lane);
             load_o(nch - 1);
             stage_o();
             load_o(nch > 1 ? nch - 2 : 0);
@@ -230,9 +230,9 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
             // (1) dU = P^T dO + Kb dS'
             f32x4_t aU[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const Fr a = fP[s];
-                fP[s] = rec_frag(recn + R::PTF + (rb * 2 + s) * R::FRAG, lane);
+            for (int s = 0; s < 2; ++s) {  // (row blocks 2, 3: step 0 is zero, its registers hold step 1)
+                const Fr a = s < (rb >> 1) ? Fr{} : fP[s];
+                fP[s] = rec_frag(recn + R::PTF + R::tri(rb, s) * R::FRAG, lane);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     aU[nb] = mma_full(aU[nb], a, lds_frag<false, kBS, 64>(pOT, 16 * nb + m, 32 * s + 8 * cg));
@@ -256,8 +256,8 @@ __global__ __launch_bounds__(64 * (4 + DK / 16), 1) void bwd_dstates_kernel(
             f32x4_t aX[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const Fr a = fN[s];
-                fN[s] = rec_frag(recn + R::NTF + (rb * 2 + s) * R::FRAG, lane);
+                const Fr a = s < (rb >> 1) ? Fr{} : fN[s];
+                fN[s] = rec_frag(recn + R::NTF + R::tri(rb, s) * R::FRAG, lane);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     aX[nb] = mma_full(aX[nb], a, lds_frag<false, kBS, 64>(pDU, 16 * nb + m, 32 * s + 8 * cg));

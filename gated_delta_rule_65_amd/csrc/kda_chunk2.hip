@@ -460,15 +460,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         f.set(x);
         gfrag_store<F32>(rec + R::PM + pair_of(w, kb) * 2 * kPlane, lane, f);
     }
-    if constexpr (BWD) {  // P^T fragments of row block w: columns of P
+    if constexpr (BWD) {  // P^T fragments of row block w: columns of P (the zero block of w >= 2 left out)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 < (w >> 1)) continue;
             float x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = sP[(32 * s2 + 8 * cg + e) * 68 + 16 * w + m];
             Fr f;
             f.set(x);
-            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::PTF) + (w * 2 + s2) * 2 * kPlane, lane, f);
+            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::PTF) + BR::tri(w, s2) * 2 * kPlane, lane, f);
         }
         if (tid < kC) brec[BR::BT + tid] = sBeta[tid];
     }
@@ -559,15 +560,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
         f.set(x);
         gfrag_store<F32>(rec + R::NM + pair_of(w, kb) * 2 * kPlane, lane, f);
     }
-    if constexpr (BWD) {  // (M^{-1} Diag(b))^T fragments of row block w: columns of M^{-1} Diag(b)
+    if constexpr (BWD) {  // (M^{-1} Diag(b))^T fragments of row block w: columns of M^{-1} Diag(b) (zero block left out)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 < (w >> 1)) continue;
             float x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = sA[(32 * s2 + 8 * cg + e) * 68 + 16 * w + m];
             Fr f;
             f.set(x);
-            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::NTF) + (w * 2 + s2) * 2 * kPlane, lane, f);
+            gfrag_store<F32>(reinterpret_cast<char*>(brec + BR::NTF) + BR::tri(w, s2) * 2 * kPlane, lane, f);
         }
     }
 }

@@ -98,17 +98,21 @@ hipError_t launch_chunk_fwd16(const ChunkArgs& a, void* ws, hipStream_t st, bool
 //   QTF  Qt^T              rows: channels, contracted: tokens   [DK/16][2]
 //   KTF  -Kt^T             rows: channels, contracted: tokens   [DK/16][2]
 //   KBF  Kb                rows: tokens,   contracted: channels [4][DK/32]
-//   PTF  P^T               rows: tokens,   contracted: tokens   [4][2]
-//   NTF  Diag(b) Minv^T    rows: tokens,   contracted: tokens   [4][2]
+//   PTF  P^T               rows: tokens,   contracted: tokens   [6 pairs]
+//   NTF  Diag(b) Minv^T    rows: tokens,   contracted: tokens   [6 pairs]
+// (P^T and Minv^T are upper triangular: row blocks 2 and 3 meet only the second step, so the six
+// (row block, step) pairs (0,0) (0,1) (1,0) (1,1) (2,1) (3,1) are stored, in that order: tri())
 // and the gradient kernel's plain fp32 operands: Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1},
 // Abar [64][64], gamma [DK], b [64].  Written by the forward preparation kernel in its backward form.
 template <int DK>
 struct BwdRec {
     static constexpr int FRAG = 512;
     static constexpr int QTF = 0, KTF = QTF + (DK / 16) * 2 * FRAG, KBF = KTF + (DK / 16) * 2 * FRAG,
-                         PTF = KBF + 4 * (DK / 32) * FRAG, NTF = PTF + 8 * FRAG, MIT = NTF + 8 * FRAG,
+                         PTF = KBF + 4 * (DK / 32) * FRAG, NTF = PTF + 6 * FRAG, MIT = NTF + 6 * FRAG,
                          AB = MIT + 4096, GM = AB + 4096, BT = GM + DK, FLOATS = BT + 64;
     static_assert(FLOATS % 64 == 0, "records stay 256-byte aligned");
+    // stored pair of (row block rb, step s) of P^T and N^T; for rb >= 2 step 0 (all zero) maps to step 1
+    static constexpr int tri(int rb, int s) { return rb < 2 ? 2 * rb + s : 2 + rb; }
 };
 
 // Backward pass (kda_bwd.hip): gradients of o and the final state.

@@ -222,9 +222,9 @@ def test_varlen_workspace_size(N, total, H, Dk, dtype):
 
 
 def bwd_workspace_bytes(records, Dk, Dv):
-    # the backward's workspace formula as the header states it: per record 4 (386 Dk + 22592 + 2 Dk Dv
+    # the backward's workspace formula as the header states it: per record 4 (386 Dk + 20544 + 2 Dk Dv
     # + 192 Dv) bytes, plus one trash row of Dv floats in 256-byte granules
-    return records * 4 * (386 * Dk + 22592 + 2 * Dk * Dv + 192 * Dv) + -(-(4 * Dv) // 256) * 256
+    return records * 4 * (386 * Dk + 20544 + 2 * Dk * Dv + 192 * Dv) + -(-(4 * Dv) // 256) * 256
 
 
 @pytest.mark.parametrize("B,T,H,Dk,Dv", [(4, 8192, 16, 128, 128), (2, 200, 3, 64, 64), (1, 65, 2, 128, 64),
