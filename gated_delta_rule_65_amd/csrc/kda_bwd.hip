@@ -459,27 +459,32 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
         __syncthreads();
         if (k0 + 32 < Dv) fetch(k0 + 32);
 
-        // (loops unrolled by two: fully unrolled, every fragment is read ahead and registers spill)
+        // Loops fully unrolled, so that the accumulator tiles are named registers (a loop index into
+        // acc[] makes the compiler move each tile through indexed register moves around its products);
+        // the scheduling barrier after each tile keeps its fragment read in place, so that the reads are
+        // not all hoisted ahead (which runs out of registers).
         const int ar = 16 * rb + m;
-        if (role == 0) {
+        if (role == 3) {
             const Frag<false> fO = lds_frag<false, 64, 32>(pO, ar, 8 * cg);
-#pragma unroll 2
-            for (int cb = 0; cb < CB; ++cb)
-                acc[cb] = mma_full(acc[cb], fO, lds_frag<false, DK, 32>(pS, 16 * cb + m, 8 * cg));
-        } else if (role == 3) {
-            const Frag<false> fO = lds_frag<false, 64, 32>(pO, ar, 8 * cg);
-#pragma unroll 2
-            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
                 acc[4 + ib] = mma_full(acc[4 + ib], fO, lds_frag<false, 64, 32>(pU, 16 * ib + m, 8 * cg));
+                __builtin_amdgcn_sched_barrier(0);
+            }
             const Frag<false> fdU = lds_frag<false, 64, 32>(pDU, ar, 8 * cg);
-#pragma unroll 2
-            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
                 acc[ib] = mma_full(acc[ib], fdU, lds_frag<false, 64, 32>(pX, 16 * ib + m, 8 * cg));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
-            const Frag<false> fr = lds_frag<false, 64, 32>(role == 1 ? pDX : pU, ar, 8 * cg);
-            const char* pB = role == 1 ? pS : pD;
-#pragma unroll 2
-            for (int cb = 0; cb < CB; ++cb) acc[cb] = mma_full(acc[cb], fr, lds_frag<false, DK, 32>(pB, 16 * cb + m, 8 * cg));
+            const Frag<false> fr = lds_frag<false, 64, 32>(role == 0 ? pO : (role == 1 ? pDX : pU), ar, 8 * cg);
+            const char* pB = role == 2 ? pD : pS;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                acc[cb] = mma_full(acc[cb], fr, lds_frag<false, DK, 32>(pB, 16 * cb + m, 8 * cg));
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     // dgamma: the eight threads of a row are adjacent lanes
