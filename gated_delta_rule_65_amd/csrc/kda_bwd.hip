@@ -613,15 +613,23 @@ __global__ __launch_bounds__(1024, 1) void bwd_grad_kernel(const void* __restric
     const float* rec = recs + ch * (int64_t)R::FLOATS;
 
     // ---- the records' operands of the later phases are requested up front, to arrive while the
-    // column sums run: four elements of each 64x64 block per thread
+    // column sums run: four elements of each 64x64 block per thread, only those inside the triangle that
+    // can be nonzero (i >= r of Minv^T, i < r of Abar; the preparation leaves the blocks outside it
+    // unwritten)
     static_assert(4096 % NT == 0 && 8 * DK <= NT, "one piece per thread");
     constexpr int EPT = 4096 / NT;
     const float vb = tid < 64 ? rec[R::BT + tid] : 0.f;
     float vN[EPT], vM[EPT], vA[EPT], vP[EPT];
 #pragma unroll
-    for (int a = 0; a < EPT; ++a) vM[a] = rec[R::MIT + tid + a * NT];
+    for (int a = 0; a < EPT; ++a) {
+        const int e = tid + a * NT, r = e >> 6, i = e & 63;
+        vM[a] = i >= r ? rec[R::MIT + e] : 0.f;
+    }
 #pragma unroll
-    for (int a = 0; a < EPT; ++a) vA[a] = rec[R::AB + tid + a * NT];
+    for (int a = 0; a < EPT; ++a) {
+        const int e = tid + a * NT, r = e >> 6, i = e & 63;
+        vA[a] = i < r ? rec[R::AB + e] : 0.f;
+    }
 
     // ---- the sums over the value columns, into LDS
     colsum_to_lds<DK>(d_o, t0, nt, H, h, Dv, states + ch * DK * (int64_t)Dv, dstates + ch * DK * (int64_t)Dv,

@@ -158,7 +158,8 @@ struct PrepLds {
 // Gram row block W (rows 16W..16W+15), all column blocks I <= W: A (one pass) into sA,
 // scaled by b_r and strictly lower on the diagonal block; P (full precision) into sP,
 // lower with diagonal; blocks I > W of both are zero.
-// gAbar (backward form only): the unscaled strictly lower A, row-major [64][64].
+// gAbar (backward form only): the unscaled strictly lower A, row-major [64][64]; the blocks right of
+// the diagonal block are not written (their readers take them as zero).
 template <int W, int DK, bool F32, bool BWD>
 __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf)[8], const float (*E)[8],
                                           const float (*Ei)[8], const float* sCol, const float* tD,
@@ -221,7 +222,9 @@ __device__ __forceinline__ void prep_gram(const float (*qf)[8], const float (*kf
             }
             sA[gr * 68 + gi] = a * sBeta[gr];
             sP[gr * 68 + gi] = pv;
-            if constexpr (BWD) gAbar[gr * 64 + gi] = a;
+            if constexpr (BWD) {
+                if (I <= W) gAbar[gr * 64 + gi] = a;
+            }
         }
     }
 }
@@ -506,11 +509,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
             Nr[R_] = nv;
         }
     }
-    if constexpr (BWD) {  // column block w of M^{-1}, as rows of (M^{-1})^T
+    if constexpr (BWD) {  // column block w of M^{-1}, as rows of (M^{-1})^T (its zero blocks above the
+                          // diagonal block are not written; their readers take them as zero)
 #pragma unroll
         for (int R_ = 0; R_ < 4; ++R_)
-            *reinterpret_cast<float4*>(brec + BR::MIT + (16 * w + m) * 64 + 16 * R_ + 4 * cg) =
-                make_float4(Nr[R_][0], Nr[R_][1], Nr[R_][2], Nr[R_][3]);
+            if (R_ >= w)
+                *reinterpret_cast<float4*>(brec + BR::MIT + (16 * w + m) * 64 + 16 * R_ + 4 * cg) =
+                    make_float4(Nr[R_][0], Nr[R_][1], Nr[R_][2], Nr[R_][3]);
     }
     // ---- Kbar = e^{G_C - G} k staged transposed ([c][t]) over the Gram operands and P
 #pragma unroll

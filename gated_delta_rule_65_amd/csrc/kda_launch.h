@@ -103,7 +103,9 @@ hipError_t launch_chunk_fwd16(const ChunkArgs& a, void* ws, hipStream_t st, bool
 // (P^T and Minv^T are upper triangular: row blocks 2 and 3 meet only the second step, so the six
 // (row block, step) pairs (0,0) (0,1) (1,0) (1,1) (2,1) (3,1) are stored, in that order: tri())
 // and the gradient kernel's plain fp32 operands: Minv^T [64][64] with Minv = (I + Diag(b) Abar)^{-1},
-// Abar [64][64], gamma [DK], b [64].  Written by the forward preparation kernel in its backward form.
+// Abar [64][64], gamma [DK], b [64].  Written by the forward preparation kernel in its backward form;
+// the six 16x16 blocks of Minv^T below its diagonal blocks and of Abar above them are all zero and are
+// not written (the gradient kernel reads only the triangle that can be nonzero).
 template <int DK>
 struct BwdRec {
     static constexpr int FRAG = 512;
