@@ -456,8 +456,8 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
         lds_store4<false, 64, 32>(pUX, urow, scol, f32x4_t{vR.x, vR.y, vR.z, vR.w});
         lds_store4<false, 64, 32>(pOD, urow, scol, f32x4_t{omask * vO.x, omask * vO.y, omask * vO.z, omask * vO.w});
         if (lo) lds_store4<false, 64, 32>(pDU, urow, scol, f32x4_t{vW.x, vW.y, vW.z, vW.w});
+        if (k0 + 32 < Dv) fetch(k0 + 32);  // as soon as this step's pieces are staged
         __syncthreads();
-        if (k0 + 32 < Dv) fetch(k0 + 32);
 
         // Loops fully unrolled, so that the accumulator tiles are named registers (a loop index into
         // acc[] makes the compiler move each tile through indexed register moves around its products);
