@@ -430,11 +430,13 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
     char* pUX = lo ? pU : pX;
     char* pOD = lo ? pO : pDX;
     float4 vS = make_float4(0.f, 0.f, 0.f, 0.f), vD = vS, vR = vS, vO = vS, vW = vS;
-    auto fetch = [&](int k0) {
+    auto fetch_sd = [&](int k0) {
         if (hasS) {
             vS = *reinterpret_cast<const float4*>(S + srow * (int64_t)Dv + k0 + scol);
             vD = *reinterpret_cast<const float4*>(dS + srow * (int64_t)Dv + k0 + scol);
         }
+    };
+    auto fetch_rows = [&](int k0) {
         vR = *reinterpret_cast<const float4*>(UX + urow * (int64_t)Dv + k0 + scol);
         vO = *reinterpret_cast<const float4*>(OD + urow * (int64_t)Dv + k0 + scol);
         if (lo) vW = *reinterpret_cast<const float4*>(dU + urow * (int64_t)Dv + k0 + scol);
@@ -445,7 +447,8 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float dgam = 0.f;
-    fetch(0);
+    fetch_sd(0);
+    fetch_rows(0);
     for (int k0 = 0; k0 < Dv; k0 += 32) {
         __syncthreads();  // the previous step's fragments have been read
         if (hasS) {
@@ -453,10 +456,11 @@ __device__ __forceinline__ void colsum_to_lds(const float* __restrict__ d_o, int
             lds_store4<false, DK, 32>(pD, srow, scol, f32x4_t{vD.x, vD.y, vD.z, vD.w});
             dgam = fmaf(vS.x, vD.x, fmaf(vS.y, vD.y, fmaf(vS.z, vD.z, fmaf(vS.w, vD.w, dgam))));
         }
+        if (k0 + 32 < Dv) fetch_sd(k0 + 32);  // the next step's pieces as soon as these are staged
         lds_store4<false, 64, 32>(pUX, urow, scol, f32x4_t{vR.x, vR.y, vR.z, vR.w});
         lds_store4<false, 64, 32>(pOD, urow, scol, f32x4_t{omask * vO.x, omask * vO.y, omask * vO.z, omask * vO.w});
         if (lo) lds_store4<false, 64, 32>(pDU, urow, scol, f32x4_t{vW.x, vW.y, vW.z, vW.w});
-        if (k0 + 32 < Dv) fetch(k0 + 32);  // as soon as this step's pieces are staged
+        if (k0 + 32 < Dv) fetch_rows(k0 + 32);
         __syncthreads();
 
         // Loops fully unrolled, so that the accumulator tiles are named registers (a loop index into
