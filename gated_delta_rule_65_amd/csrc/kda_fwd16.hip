@@ -178,23 +178,41 @@ __device__ __forceinline__ void load_pi8_gate(const void* g, int64_t idx, bool b
 
 // ============================================================================ prep kernel
 
+// Lower block-triangular fp32 [64][64] matrix (A, then N; P, then -P N): row block R keeps its 16 (R + 1)
+// columns plus 4 of padding, so rows stay 16-byte aligned and 16 rows of one column fall in 16 banks.
+__host__ __device__ constexpr int tri_stride(int R) { return 16 * R + 20; }
+__host__ __device__ constexpr int tri_base(int R) { return 128 * R * R + 192 * R; }
+// element (row 16 R + rr, column c), c < 16 (R + 1)
+__host__ __device__ constexpr int tri(int R, int rr, int c) { return tri_base(R) + rr * tri_stride(R) + c; }
+constexpr int kTriFloats = tri_base(4);  // 2816
+
 template <int DK>
 struct Prep16Lds {
+    // The regions live in two phases.  Up to the Gram results: the fp32 Gram column operands of sub-blocks
+    // 0..2 [48][DK+4] (pi positions) and row block 3's Gram operands for waves 0 and 1.  From then on:
+    // A (later N) and P (later -P N) in block-triangular form, the fp16 staging of Kbar^T and then Kt^T
+    // [DK][72], and the diagonal inverses.  The gates' sub-block sums are only read before the column
+    // operands are written.  Tables and b live throughout.  At DK = 128 this is 53,248 bytes: three
+    // workgroups per CU.
     static constexpr int COL_BYTES = 48 * (DK + 4) * 4;
+    static constexpr int ROW3_BYTES = DK / 32 * 3 * 64 * 16;
     static constexpr int STG = 72;                         // halves per row of the fp16 staging [DK][72]
-    static_assert(DK * STG * 2 <= COL_BYTES, "the staging fits over the column operands");
-    static constexpr int COL = 0;                          // fp32 Gram column operands, sub-blocks 0..2 [48][DK+4]
-                                                           // (pi positions); later fp16 Kbar^T, then Kt^T [DK][72]
-    static constexpr int PM = COL + COL_BYTES;             // fp32 P [64][68], later -P N (rows of block w by wave w)
-    static constexpr int A = PM + 64 * 68 * 4;             // fp32 b_r A_ri [64][68], later N; before the
-                                                           // Gram results, row block 3's Gram operands
-    static_assert(DK / 32 * 3 * 64 * 16 <= 64 * 68 * 4, "row block 3's Gram operands fit over A");
-    static constexpr int D = A + 64 * 68 * 4;              // fp32 diagonal inverses [4][16][17]
-    static constexpr int TAB = D + 4 * 16 * 17 * 4;        // fp32 tables [15][DK] (pi positions)
-    static constexpr int GT = TAB + 15 * DK * 4;           // fp32 sub-block gate sums (log2) [4][DK]
-    static constexpr int BETA = GT + 4 * DK * 4;           // fp32 b [64]
+    static constexpr int TRI_BYTES = kTriFloats * 4;
+    static constexpr int COL = 0;                          // phase 1: column operands
+    static constexpr int ROW3 = COL + COL_BYTES;           // phase 1: row block 3's Gram operands
+    static constexpr int GT = 0;                           // before phase 1: sub-block gate sums (log2) [4][DK]
+    static constexpr int A = 0;                            // phase 2: b_r A_ri, later N
+    static constexpr int PM = A + TRI_BYTES;               // phase 2: P, later -P N (rows of block w by wave w)
+    static constexpr int STGO = PM + TRI_BYTES;            // phase 2: fp16 Kbar^T, later Kt^T [DK][72]
+    static constexpr int D = STGO + DK * STG * 2;          // phase 2: fp32 diagonal inverses [4][16][17]
+    static constexpr int END2 = D + 4 * 16 * 17 * 4;
+    static constexpr int END1 = ROW3 + ROW3_BYTES;
+    static_assert(ROW3 + ROW3_BYTES <= D, "row block 3's operands stay clear of the diagonal inverses");
+    static_assert(GT + 4 * DK * 4 <= COL_BYTES, "the gate sums lie inside the column operands");
+    static constexpr int TAB = END1 > END2 ? END1 : END2;  // fp32 tables [15][DK] (pi positions)
+    static constexpr int BETA = TAB + 15 * DK * 4;         // fp32 b [64]
     static constexpr int TOTAL = BETA + 64 * 4;
-    static_assert(TOTAL <= 80 * 1024, "two prep workgroups per CU");
+    static_assert(DK != 128 || TOTAL <= 160 * 1024 / 3, "three prep workgroups per CU");
 };
 
 // The decay-folded Gram blocks (R, I), I <= R, of A (one bf16 pass; scaled by b_r and strictly lower on
@@ -274,16 +292,12 @@ __device__ __forceinline__ void gram16_store(const GramOut<DK>& g, const float* 
                 if (m >= rr) av = 0.f;
                 if (m > rr) pp = 0.f;
             }
-            sA[gr * 68 + gi] = av * sBeta[gr];
-            sP[gr * 68 + gi] = pp;
+            sA[tri(R, rr, gi)] = av * sBeta[gr];
+            sP[tri(R, rr, gi)] = pp;
         }
     };
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int I = ILO; I < 4; ++I) {
-        if (I <= W) put(W, I, g.a[I - ILO], g.p[I - ILO], I == W);
-        else put(W, I, z, z, false);
-    }
+    for (int I = ILO; I <= W; ++I) put(W, I, g.a[I - ILO], g.p[I - ILO], I == W);
     if constexpr (W < 2) put(3, W, g.a[W + 1], g.p[W + 1], false);
 }
 
@@ -301,8 +315,8 @@ __device__ __forceinline__ void pn_tiles(const float* sP, const float* sA, int m
             if (J < ct || J > R) continue;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[(16 * R + m) * 68 + 16 * J + 4 * kk + cg],
-                                                           sA[(16 * J + 4 * kk + cg) * 68 + 16 * ct + m], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sP[tri(R, m, 16 * J + 4 * kk + cg)],
+                                                           sA[tri(J, 4 * kk + cg, 16 * ct + m)], acc, 0, 0, 0);
         }
         return acc;
     };
@@ -315,17 +329,16 @@ __device__ __forceinline__ void pn_store(float* sP, int m, int cg, const f32x4_t
     constexpr int CLO = W == 3 ? 2 : 0;
     auto put = [&](int R, int ct, const f32x4_t& x) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sP[(16 * R + 4 * cg + jj) * 68 + 16 * ct + m] = -x[jj];
+        for (int jj = 0; jj < 4; ++jj) sP[tri(R, 4 * cg + jj, 16 * ct + m)] = -x[jj];
     };
-    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ct = CLO; ct < 4; ++ct) put(W, ct, ct <= W ? pn[ct - CLO] : z);
+    for (int ct = CLO; ct <= W; ++ct) put(W, ct, pn[ct - CLO]);
     if constexpr (W < 2) put(3, W, pn[W + 1]);
 }
 
-// One workgroup (four waves, wave w = token rows 16w..16w+15) per (chunk, head); two per CU.
+// One workgroup (four waves, wave w = token rows 16w..16w+15) per (chunk, head); three per CU.
 template <int DK, bool PRO>
-__global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
+__global__ __launch_bounds__(256, 3) void prep16_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                         const void* __restrict__ gv, const void* __restrict__ bv,
                                                         const int32_t* __restrict__ cu_seqlens, int64_t T_fixed,
                                                         int64_t T_stride, int64_t total, int64_t N, int H,
@@ -341,10 +354,10 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
 
     __shared__ __align__(16) char smem[L::TOTAL];
     float* sCol = reinterpret_cast<float*>(smem + L::COL);
-    _Float16* sStg = reinterpret_cast<_Float16*>(smem + L::COL);
+    _Float16* sStg = reinterpret_cast<_Float16*>(smem + L::STGO);
     float* sP = reinterpret_cast<float*>(smem + L::PM);
     float* sA = reinterpret_cast<float*>(smem + L::A);
-    bf16x8_t* sRow3 = reinterpret_cast<bf16x8_t*>(smem + L::A);  // over sA until the Gram results
+    bf16x8_t* sRow3 = reinterpret_cast<bf16x8_t*>(smem + L::ROW3);
     float* sD = reinterpret_cast<float*>(smem + L::D);
     float* tPw = reinterpret_cast<float*>(smem + L::TAB);   // e^{sum_{J<w} Gt_J}     [4][DK]
     float* tBt = tPw + 4 * DK;                              // e^{Gt_w}               [4][DK]
@@ -383,6 +396,14 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
     // ---- rows of sub-block w (rows past the end re-read the last row); running gate sums (log2)
     const int r = 16 * w + m;
     const bool rv = r < nt;
+    // this lane's 8 columns 32 kb + 8 cg.. of row r of a block-triangular matrix (zeros right of block w)
+    auto tri_row8 = [&](const float* t, int kb, float x[8]) {
+        const int c0 = 32 * kb + 8 * cg;
+        const bool in = c0 < 16 * (w + 1);
+        lds_read8(t + tri(w, m, in ? c0 : 0), x);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) x[jj] = in ? x[jj] : 0.f;
+    };
     const int64_t base = ((t0 + min(r, nt - 1)) * H + h) * (int64_t)DK + 4 * cg;
     float braw = 0.f;
     if (tid < kC) braw = load1_gate(bv, (t0 + min(tid, nt - 1)) * H + h, pf.b_bf16);
@@ -506,13 +527,14 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
     // ---- diagonal blocks of M^{-1} = (I + A)^{-1}: forward substitution, one column per lane
     if (lane < 16) {
         const int cidx = lane;
-        const float* Ab = &sA[(16 * w) * 68 + 16 * w];
+        const int ast = tri_stride(w);
+        const float* Ab = &sA[tri(w, 0, 16 * w)];
         float x[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
+        for (int rr = 0; rr < 16; ++rr, Ab += ast) {
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jj = 0; jj < rr; ++jj) acc[jj & 3] = fmaf(Ab[rr * 68 + jj], x[jj], acc[jj & 3]);
+            for (int jj = 0; jj < rr; ++jj) acc[jj & 3] = fmaf(Ab[jj], x[jj], acc[jj & 3]);
             const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             x[rr] = (rr == cidx) ? 1.f : (rr < cidx ? 0.f : -sum);
         }
@@ -524,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
     for (int kb = 0; kb < 2; ++kb) {
         if (kb >= steps_of(w)) continue;
         float x[8];
-        lds_read8(&sP[r * 68 + 32 * kb + 8 * cg], x);
+        tri_row8(sP, kb, x);
         f16x8_t hi, lo;
         to_h8_split(x, hi, lo);
         char* dst = rec + R::PM + pair_of(w, kb) * 2 * kPl;
@@ -550,7 +572,7 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
                     if (J < I || J >= R_) continue;
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
-                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * R_ + m) * 68 + 16 * J + 4 * cg + jj],
+                        z = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[tri(R_, m, 16 * J + 4 * cg + jj)],
                                                                  Nr[J][jj], z, 0, 0, 0);
                 }
                 f32x4_t y = {0.f, 0.f, 0.f, 0.f};
@@ -582,7 +604,8 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
 #pragma unroll
         for (int R_ = 0; R_ < 4; ++R_)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) sA[(16 * R_ + 4 * cg + jj) * 68 + 16 * w + m] = Nr[R_][jj] * bcol;
+            for (int jj = 0; jj < 4; ++jj)
+                if (R_ >= w) sA[tri(R_, 4 * cg + jj, 16 * w + m)] = Nr[R_][jj] * bcol;
     }
 #pragma unroll
     for (int i = 0; i < DK / 32; ++i) {  // (c-block, kb) groups w, w+4, ...
@@ -598,7 +621,7 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
     for (int kb = 0; kb < 2; ++kb) {
         if (kb >= steps_of(w)) continue;
         float x[8];
-        lds_read8(&sA[r * 68 + 32 * kb + 8 * cg], x);
+        tri_row8(sA, kb, x);
         f16x8_t hi, lo;
         to_h8_split(x, hi, lo);
         char* dst = rec + R::NM + pair_of(w, kb) * 2 * kPl;
@@ -639,9 +662,9 @@ __global__ __launch_bounds__(256, 2) void prep16_kernel(const void* __restrict__
         for (int kb = 0; kb < 2; ++kb) {
             if (kb >= steps_of(w)) continue;
             float x[8];
-            lds_read8(&sA[r * 68 + 32 * kb + 8 * cg], x);
+            tri_row8(sA, kb, x);
             to_h8_split(x, bN[kb][0], bN[kb][1]);
-            lds_read8(&sP[r * 68 + 32 * kb + 8 * cg], x);
+            tri_row8(sP, kb, x);
             to_h8_split(x, bC[kb][0], bC[kb][1]);
         }
 #pragma unroll
