@@ -18,7 +18,10 @@
 // (sequence, head, 32-column slice) in order and only runs the products of the
 // second line, with three workgroup barriers per chunk; each chunk's operands are
 // loaded during the previous chunk, once the products that read the registers they
-// replace have completed (the Qt steps right after their last read).
+// replace have completed (the Qt steps right after their last read).  The backward
+// pass's state-only form (mode 3) stores B = Kbar^T M^{-1} Diag(b) in Kbar^T's place
+// and updates S' = Diag(gamma_C) S + B X, so U leaves the carried chain: two
+// barriers per chunk.
 #include <algorithm>
 #include <type_traits>
 
@@ -101,7 +104,8 @@ struct Rec {
     static constexpr int KT_PLANES = KT2 ? 2 : 1;
     static constexpr int64_t QT = 0;                        // Qt rows:    [w 4][s KS], 2 planes
     static constexpr int64_t KT = QT + 4 * KS * 2 * kPlane;  // Kt rows:    [w 4][s KS], KT_PLANES
-    static constexpr int64_t KB = KT + 4 * KS * KT_PLANES * kPlane;  // Kbar^T rows: [c-block DK/16][kb 2], 2 planes
+    static constexpr int64_t KB = KT + 4 * KS * KT_PLANES * kPlane;  // Kbar^T rows (B = Kbar^T M^{-1} Diag(b) in
+                                                                     // the backward's records): [c-block DK/16][kb 2], 2 planes
     static constexpr int64_t NM = KB + (DK / 16) * 2 * 2 * kPlane;   // M^{-1} Diag(b): [pair 6], 2 planes
     static constexpr int64_t PM = NM + 6 * 2 * kPlane;               // P:            [pair 6], 2 planes
     static constexpr int64_t GC = PM + 6 * 2 * kPlane;               // gamma_C fp32 [DK]
@@ -547,14 +551,55 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const void* __restrict__ q
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) sA[(16 * R_ + 4 * cg + jj) * 68 + 16 * w + m] = Nr[R_][jj] * bcol;
     }
+    if constexpr (!BWD) {
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i) {  // (c-block, kb) groups w, w+4, ...
-        const int gidx = w + 4 * i;
-        const int cb = gidx >> 1, kb = gidx & 1;
-        const Fr f = lds_frag<F32, DK, kC>(pKB, 16 * cb + m, 32 * kb + 8 * cg);
-        gfrag_store<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane, f);
+        for (int i = 0; i < DK / 32; ++i) {  // (c-block, kb) groups w, w+4, ...
+            const int gidx = w + 4 * i;
+            const int cb = gidx >> 1, kb = gidx & 1;
+            const Fr f = lds_frag<F32, DK, kC>(pKB, 16 * cb + m, 32 * kb + 8 * cg);
+            gfrag_store<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane, f);
+        }
     }
     lds_barrier();  // (7)
+
+    if constexpr (BWD) {
+        // The state-only chain updates S' = Diag(gamma_C) S + B X with B = Kbar^T M^{-1} Diag(b)
+        // (= Kbar^T U / X: U = M^{-1} Diag(b) X), so its carried step needs X only.  B [DK][64] as
+        // fragments in Kbar^T's place: wave w takes channel blocks (DK/64) w .. and both token steps.
+        // Two 16x16 results per fragment, their result rows permuted so that a lane ends up with the
+        // eight consecutive columns 32 kb + 8 cg .. of its fragment row: result row i of tile T is
+        // column 32 kb + 8 (i / 4) + 4 T + i % 4.  N is lower triangular (with zero rows and columns
+        // past the chunk's end), so the contraction starts at token 32 kb.
+#pragma unroll
+        for (int i = 0; i < DK / 32; ++i) {
+            const int cb = (DK / 64) * w + (i >> 1), kb = i & 1;
+            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (s2 < kb) continue;
+                const Fr kf8 = lds_frag<F32, DK, kC>(pKB, 16 * cb + m, 32 * s2 + 8 * cg);
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    const int j = 32 * kb + 8 * (m >> 2) + 4 * T + (m & 3);
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = sA[(32 * s2 + 8 * cg + e) * 68 + j];
+                    Fr nf;
+                    nf.set(x);
+                    acc[T] = mma_full(acc[T], nf, kf8);
+                }
+            }
+            float x[8];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                x[jj] = acc[0][jj];
+                x[4 + jj] = acc[1][jj];
+            }
+            Fr f;
+            f.set(x);
+            gfrag_store<F32>(rec + R::KB + (cb * 2 + kb) * 2 * kPlane, lane, f);
+        }
+    }
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -620,7 +665,8 @@ struct ChainOutOps {
 // State waves 0-3 (row block rb = w) compute X = V - Kt S and U = M^{-1} Diag(b) X for the 16 rows
 // of rb and all 32 columns; output waves 4-7 (rb = w - 4) compute O = Qt S + P U for the same rows,
 // Qt S spread over the first two phases.  Every wave also updates DK / 64 of the (16-channel block,
-// 16-column half) tiles of S in the third phase.  Both kinds of wave pass the same three barriers
+// 16-column half) tiles of S in the third phase (mode 3: in the second, from X and B, while the state
+// waves form U for the stores).  Both kinds of wave pass the same three (mode 3: two) barriers
 // per chunk.
 template <int DK, bool F32, bool SO, bool IN_F32 = F32, bool ST = false>
 __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chain_kernel(const void* __restrict__ vv, const float* s0,
@@ -733,8 +779,9 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
     // the chunk after jc, or jc again after the last one
     auto next_chunk = [&](int64_t jc) { return jc + 1 < jend ? jc + 1 : jc; };
 
-    // third phase, both kinds of wave: S = gamma_C S + Kbar^T U on this wave's tiles
-    auto update_state = [&](const Fr (&uf)[2][2], const Fr (&fKB)[2], float4 gC) {
+    // third phase, both kinds of wave: S = gamma_C S + Kbar^T U on this wave's tiles (mode 3, second
+    // phase: S = gamma_C S + B X, B = Kbar^T M^{-1} Diag(b) from the record, ub = X^T)
+    auto update_state = [&](const Fr (&uf)[2][2], const Fr (&fKB)[2], float4 gC, const char* ub) {
         const float gcv[4] = {gC.x, gC.y, gC.z, gC.w};
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -745,7 +792,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                 if constexpr (TPW == 2) {  // tile i is column half i
                     accS[i] = mma_full(accS[i], fKB[kb], uf[i][kb]);
                 } else {
-                    const Fr u = lds_frag<F32, kS, kC>(pU, 16 * nbt(i) + m, 32 * kb + 8 * cg);
+                    const Fr u = lds_frag<F32, kS, kC>(ub, 16 * nbt(i) + m, 32 * kb + 8 * cg);
                     accS[i] = mma_full(accS[i], fKB[kb], u);
                 }
             }
@@ -756,11 +803,11 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
         for (int i = 0; i < TPW; ++i) lds_store4<F32, kS, DK>(pS, 16 * nbt(i) + m, 16 * cbw + 4 * cg, accS[i]);
         tile_state();
     };
-    auto read_u = [&](Fr (&uf)[2][2]) {
+    auto read_u = [&](Fr (&uf)[2][2], const char* ub) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) uf[hb][kb] = lds_frag<F32, kS, kC>(pU, 16 * hb + m, 32 * kb + 8 * cg);
+            for (int kb = 0; kb < 2; ++kb) uf[hb][kb] = lds_frag<F32, kS, kC>(ub, 16 * hb + m, 32 * kb + 8 * cg);
     };
     auto load_kb = [&](Fr (&fKB)[2], float4& gC, const char* rec) {
 #pragma unroll
@@ -787,7 +834,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
         if constexpr (ST)
             store_rows(cm.xu + (slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 * (int64_t)Dv + col0, fX, std::integral_constant<int, 64>{});
     };
-    auto store_u = [&](int64_t jc) {  // mode 3: U rows of chunk jc (staged in phase 2)
+    auto store_u = [&](int64_t jc) {  // mode 3: U rows of chunk jc (staged in phase 2, stored in the next step)
         if constexpr (ST)
             store_rows(cm.xu + ((slot_of(cu_seqlens, n, jc, T_fixed, start) * H + h) * 128 + 64) * (int64_t)Dv + col0,
                        fU, std::integral_constant<int, 64>{});
@@ -824,6 +871,9 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
             const int64_t jn = next_chunk(jc);
             const char* recn = record(jn);
             store_start_state(jc);
+            if constexpr (ST) {
+                if (jc > jbeg) store_u(jc - 1);  // staged in the previous step's second phase
+            }
 #pragma unroll
             for (int i = 0; i < VLOADS; ++i)
                 *reinterpret_cast<uint4*>(&sV[(vrow + i * VROWS) * kS + vpiece * VPL]) = cur.vraw[i];
@@ -875,20 +925,23 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * rb + 4 * cg, accU[nb]);
-                if constexpr (ST) {
+                if constexpr (ST) {  // U is only stored: the state update below takes X
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) fU[(16 * rb + 4 * cg + jj) * FLD + 16 * nb + m] = accU[nb][jj];
+                } else {
+                    lds_store4<F32, kS, kC>(pU, 16 * nb + m, 16 * rb + 4 * cg, accU[nb]);
                 }
             }
             load_nv(nxt, recn, jn);  // after the products that read this chunk's M^{-1} rows
-            lds_barrier();  // (2)
-            store_u(jc);
+            if constexpr (!ST) {
+                lds_barrier();  // (2)
+                store_u(jc);
+            }
 
-            // ---- phase 3:  S tiles
+            // ---- phase 3 (mode 3: still the second phase):  S tiles
             Fr uf[2][2];
-            read_u(uf);
-            update_state(uf, cur.fKB, cur.gC);
+            read_u(uf, ST ? pX : pU);
+            update_state(uf, cur.fKB, cur.gC, ST ? pX : pU);
             store_state();
             load_kb(nxt.fKB, nxt.gC, recn);  // after the tile products that read this chunk's copy
             lds_barrier();  // (3)
@@ -946,6 +999,9 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
             const int64_t jn = next_chunk(jc);
             const char* recn = record(jn);
             store_start_state(jc);
+            if constexpr (ST) {
+                if (jc > jbeg) store_u(jc - 1);  // staged in the previous step's second phase
+            }
 
             // ---- phase 1:  O = Qt S, first half of the channels
             f32x4_t accO[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -972,12 +1028,14 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                     load_q(nxt, recn, s);
                 }
             }
-            lds_barrier();  // (2)
-            store_u(jc);
+            if constexpr (!ST) {
+                lds_barrier();  // (2)
+                store_u(jc);
+            }
 
-            // ---- phase 3:  O += P U, S tiles
+            // ---- phase 3 (mode 3: the second phase):  O += P U, S tiles
             Fr uf[2][2];
-            read_u(uf);
+            read_u(uf, ST ? pX : pU);
             if constexpr (!SO) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -986,7 +1044,7 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
                     for (int nb = 0; nb < 2; ++nb) accO[nb] = mma_full(accO[nb], cur.fP[kb], uf[nb][kb]);
                 }
             }
-            update_state(uf, cur.fKB, cur.gC);
+            update_state(uf, cur.fKB, cur.gC, ST ? pX : pU);
             store_state();
             load_kb(nxt.fKB, nxt.gC, recn);  // after the tile products that read this chunk's copy
             if constexpr (!SO) {
@@ -1012,6 +1070,9 @@ __global__ __launch_bounds__(kChainThreads, SO && !F32 && !ST ? 4 : 1) void chai
         }
         if (jc < jend) step(opsA, opsB, jc);
         if (!SO && jbeg < jend) store_o(chunk_start(jend - 1), chunk_len(jend - 1));
+    }
+    if constexpr (ST) {  // the last chunk's U rows, staged before the last barrier
+        if (jbeg < jend) store_u(jend - 1);
     }
 
     if (sdst) {
