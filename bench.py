@@ -97,16 +97,28 @@ def measured_traffic(key):
 
 
 def time_launches(fn, steps, warmup, torch, flush=None):
-    """Run fn `warmup` times, then `steps` times bracketed by synchronize; per-launch durations from
-    events on the current stream (the stream the library launches on).  With `flush`, it runs before
-    each launch, outside the events.  Returns wall seconds of the timed loop and the mean, median and
-    min launch time in ms."""
+    """Run fn `warmup` times, then `steps` times bracketed by synchronize, on the current stream (the
+    stream the library launches on).  Without `flush` the timed loop holds nothing but the calls: one
+    event pair around all of them gives the mean launch time (events between calls cost the GPU about
+    10 us each time), and a second, untimed pass with events around each call gives the median and
+    min.  With `flush`, it runs before each launch, outside the per-call events of the timed loop.
+    Returns wall seconds of the timed loop and the mean, median and min launch time in ms."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mean = e0.elapsed_time(e1) / steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for a, b in evs:
         if flush is not None:
             flush()
@@ -114,9 +126,10 @@ def time_launches(fn, steps, warmup, torch, flush=None):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = np.array([a.elapsed_time(b) for a, b in evs])
-    return wall, float(per.mean()), float(np.median(per)), float(per.min())
+    if flush is not None:
+        wall, mean = time.perf_counter() - t1, float(per.mean())
+    return wall, float(mean), float(np.median(per)), float(per.min())
 
 
 def cpu_threads():
