@@ -124,6 +124,11 @@ typedef enum {
  * the method's scale (unit norm, or qk_l2norm) keep the other operands far
  * inside it.  fp32 inputs and the fused kernel (workspace NULL) use split-bf16
  * or fp32 operands.
+ * Speed: with workspace NULL the call is one fused kernel that repeats the
+ * state-independent work in every 32-column slice, about three times slower
+ * than the two-kernel path a workspace enables; a caller that cannot provide a
+ * workspace but can serialise its calls on a GPU gets the two-kernel path from
+ * kda_chunk_fwd_noalloc.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* s0, float* o, float* s_final, int64_t B, int64_t T, int H, int Dk,
