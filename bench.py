@@ -96,13 +96,33 @@ def measured_traffic(key):
     return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
 
+# Untimed calls before each measurement's warm-up, until the GPU clock has settled: its governor
+# raises the clock over a few hundred milliseconds of sustained load (the B=4 H=16 call takes 0.55 ms
+# at the first calls after idle and 0.47 ms once settled).
+SETTLE_S = 0.3
+
+
+def settle_clock(fn, torch, seconds=SETTLE_S):
+    """Call fn, untimed, until `seconds` of wall time have passed; returns the number of calls."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def time_launches(fn, steps, warmup, torch, flush=None):
     """Run fn `warmup` times, then `steps` times bracketed by synchronize, on the current stream (the
     stream the library launches on).  Without `flush` the timed loop holds nothing but the calls: one
     event pair around all of them gives the mean launch time (events between calls cost the GPU about
     10 us each time), and a second, untimed pass with events around each call gives the median and
     min.  With `flush`, it runs before each launch, outside the per-call events of the timed loop.
-    Returns wall seconds of the timed loop and the mean, median and min launch time in ms."""
+    Returns wall seconds of the timed loop and the mean, median and min launch time in ms.  Before the
+    warm-up, fn runs untimed until the clock has settled (settle_clock)."""
+    settle_clock(fn, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -296,6 +316,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_s": SETTLE_S,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
